@@ -1,0 +1,196 @@
+"""Dense float64 reference for multi-head attention (forward only).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py; never by the product path.
+
+What it computes, and from which passage
+----------------------------------------
+* Page "Multi-head attention and self-attention", Definition: general dims
+  h, d_q, d_k, d_v, d_h, d_vh, d_o, n_q, n_k; head i is scaled dot-product
+  attention of (Q W_i^Q, K W_i^K, V W_i^V) under one chosen mask shared by
+  every head; the heads are concatenated along the feature axis and
+  multiplied by W^O.  Self-attention is Q = K = V = X.
+* Page "Multi-Head Attention" review (llmprimer), "The Complete Multi-Head
+  Operation": A = softmax over the last axis of (Q K^T / sqrt(d_k) + M),
+  Z^(r) = A^(r) V^(r), Z = Concat, Y = Z W_O; batch-major shapes.
+  "Separate and Combined Projections": combined weights hold the heads side
+  by side; (B,T,h d_k) -> (B,T,h,d_k) -> (B,h,T,d_k).
+* Page "From Attention to Self-Attention" review, "The Complete Layer" and
+  "Distinctions to Keep": the mask acts before the softmax; a causal mask
+  removes later positions, a padding mask removes artificial key positions,
+  and the two may be combined.
+* Page "Stable summary of an attention key block", Definition: allowed key
+  sets are nonempty; the row maximum is the stabilising shift.
+
+Readings of points the pages leave open (each is listed in the design doc):
+* masks are allowed sets (additive M in {0, -inf}); combined rules AND;
+* key padding masks keys only, never whole query rows;
+* causal requires n_q == n_k and allows j <= i (0-based);
+* a row whose allowed set is empty violates the definition: EmptyRowError;
+* the scale c is an explicit argument (1/sqrt(d_h) is the caller's default).
+
+Nothing here is blocked, fused or reordered: every (batch, head) score
+matrix is materialised whole, and the softmax uses the exact row maximum.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+class EmptyRowError(ValueError):
+    """A query row has no allowed key (the definition requires one)."""
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def allowed_set(B, n_q, n_k, causal=False, key_len=None, allowed=None):
+    """Boolean allowed[b, i, j]: may query i of item b use key j.
+
+    Page "From Attention to Self-Attention" review, "Distinctions to Keep"
+    (causal and padding masks, combinable); page "Multi-head attention and
+    self-attention", Definition (one mask applied to every head, so there is
+    no head axis).  ``allowed`` is an optional explicit boolean mask of shape
+    [B or 1, n_q, n_k] for the general "any chosen mask" case.
+    """
+    A = np.ones((B, n_q, n_k), dtype=bool)
+    if causal:
+        if n_q != n_k:
+            raise ValueError("a causal mask needs n_q == n_k")
+        i = np.arange(n_q)[:, None]
+        j = np.arange(n_k)[None, :]
+        A &= (j <= i)[None]
+    if key_len is not None:
+        key_len = np.asarray(key_len)
+        j = np.arange(n_k)[None, None, :]
+        A &= j < key_len[:, None, None]
+    if allowed is not None:
+        G = np.asarray(allowed, dtype=bool)
+        A &= np.broadcast_to(G, (B, n_q, n_k))
+    return A
+
+
+def project_separate(X, W, h, d):
+    """Per-head products X W^(r), r = 0..h-1, stacked as [B, h, n, d].
+
+    Page "Multi-head attention and self-attention", Definition: each head
+    has its own projection matrix.  The combined matrix W [d_in, h*d] holds
+    head r in columns r*d .. r*d+d-1 (review page, "Separate and Combined
+    Projections"); here each head's block is sliced out and multiplied
+    on its own.
+    """
+    X = _f64(X)
+    W = _f64(W)
+    B, n, _ = X.shape
+    out = np.empty((B, h, n, d))
+    for r in range(h):
+        Wr = W[:, r * d:(r + 1) * d]
+        for b in range(B):
+            out[b, r] = X[b] @ Wr
+    return out
+
+
+def project_combined(X, W, h, d):
+    """One wide product, then reshape and transpose to [B, h, n, d].
+
+    Review page "Multi-Head Attention", "Separate and Combined Projections":
+    (B, T, h d) -> (B, T, h, d) -> (B, h, T, d).
+    """
+    X = _f64(X)
+    W = _f64(W)
+    B, n, _ = X.shape
+    wide = X @ W                       # (B, n, h*d)
+    split = wide.reshape(B, n, h, d)   # reshape splits the feature axis
+    return split.transpose(0, 2, 1, 3).copy()  # transpose swaps head and position
+
+
+def masked_softmax_rows(S, allow):
+    """Stable softmax of each row of S over its allowed entries.
+
+    S: [n_q, n_k] float64 scores; allow: [n_q, n_k] bool.
+    Returns (A, m, l): weights, row maxima over allowed entries, and
+    l = sum over allowed j of exp(S_ij - m_i).  Forbidden weights are
+    assigned 0.0 directly (never computed from -inf), so they are exact
+    zeros.  This is the one-block summary of page "Stable summary of an
+    attention key block" followed by dividing by its second coordinate.
+    """
+    if not np.all(allow.any(axis=1)):
+        bad = int(np.flatnonzero(~allow.any(axis=1))[0])
+        raise EmptyRowError(f"query row {bad} has no allowed key")
+    Smask = np.where(allow, S, -np.inf)
+    m = Smask.max(axis=1)
+    E = np.zeros_like(S)
+    E[allow] = np.exp((S - m[:, None])[allow])
+    l = E.sum(axis=1)
+    A = E / l[:, None]
+    return A, m, l
+
+
+def attn_core_ref(Qh, Kh, Vh, scale, allow, keep_A=False):
+    """Attention on projected heads; output in concatenated layout.
+
+    Qh [B,h,n_q,d_h], Kh [B,h,n_k,d_h], Vh [B,h,n_k,d_vh];
+    allow [B,n_q,n_k] (one mask for every head).
+    Returns dict with Z [B, n_q, h*d_vh] (head r in columns r*d_vh..),
+    m, l [B, h, n_q] (natural-log units), and A [B,h,n_q,n_k] if keep_A.
+    """
+    Qh, Kh, Vh = _f64(Qh), _f64(Kh), _f64(Vh)
+    B, h, n_q, _ = Qh.shape
+    n_k = Kh.shape[2]
+    d_vh = Vh.shape[3]
+    Z = np.empty((B, n_q, h * d_vh))
+    m = np.empty((B, h, n_q))
+    l = np.empty((B, h, n_q))
+    A_all = np.empty((B, h, n_q, n_k)) if keep_A else None
+    for b in range(B):
+        for r in range(h):
+            S = scale * (Qh[b, r] @ Kh[b, r].T)          # scores, materialised
+            A, m[b, r], l[b, r] = masked_softmax_rows(S, allow[b])
+            Z[b, :, r * d_vh:(r + 1) * d_vh] = A @ Vh[b, r]   # concat in head order
+            if keep_A:
+                A_all[b, r] = A
+    out = {"Z": Z, "m": m, "l": l}
+    if keep_A:
+        out["A"] = A_all
+    return out
+
+
+def mha_ref(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, scale, allow,
+            projection="combined", keep_A=False):
+    """Full multi-head attention forward in float64.
+
+    Q [B,n_q,d_q], K [B,n_k,d_k], V [B,n_k,d_v]; W_Q [d_q,h*d_h],
+    W_K [d_k,h*d_h], W_V [d_v,h*d_vh], W_O [h*d_vh,d_o]; no biases.
+    ``projection`` picks one of two independent projection code paths.
+    Returns dict with Y [B,n_q,d_o], Z, m, l (and A if keep_A).
+    """
+    proj = {"combined": project_combined, "separate": project_separate}[projection]
+    Qh = proj(Q, W_Q, h, d_h)
+    Kh = proj(K, W_K, h, d_h)
+    Vh = proj(V, W_V, h, d_vh)
+    out = attn_core_ref(Qh, Kh, Vh, scale, allow, keep_A=keep_A)
+    out["Y"] = out["Z"] @ _f64(W_O)                 # output projection
+    return out
+
+
+def mha_ref_rows(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, scale, allow, b, rows):
+    """The same computation restricted to query rows ``rows`` of item ``b``.
+
+    Keys and values of item b are projected in full; only the selected
+    query rows are projected and attended.  Used to check large problems
+    at sampled positions.  Returns (Y_rows [len(rows), d_o],
+    Z_rows [len(rows), h*d_vh], m_rows [h, len(rows)], l_rows [h, len(rows)]).
+    """
+    rows = np.asarray(rows)
+    Qb = _f64(Q[b])[rows][None]                        # (1, R, d_q)
+    Kb = _f64(K[b])[None]
+    Vb = _f64(V[b])[None]
+    Qh = project_combined(Qb, W_Q, h, d_h)
+    Kh = project_combined(Kb, W_K, h, d_h)
+    Vh = project_combined(Vb, W_V, h, d_vh)
+    sub_allow = np.asarray(allow[b])[rows][None]
+    out = attn_core_ref(Qh, Kh, Vh, scale, sub_allow)
+    Y = out["Z"][0] @ _f64(W_O)
+    return Y, out["Z"][0], out["m"][0], out["l"][0]

@@ -1,0 +1,204 @@
+"""Benchmark: multi-head attention forward on one MI355X.
+
+One "step" is one full forward pass (Q/K/V projections, fused masked
+attention with running summaries, concatenation, W^O projection) over one
+batch of the headline workload: self-attention, bf16 inputs with fp32
+accumulation, B=4, T=4096, d_model=1024, h=16, d_h=d_vh=64, causal mask.
+Inputs are seeded synthetic draws already resident in HBM when timing starts.
+
+Printed JSON line (rank 0):
+* value: whole-forward TFLOP/s, counting 2*B*h*n_q*n_k*(d_h+d_vh) (halved
+  for causal) for the attention core plus 2*M*N*K for each projection GEMM;
+* roofline: the attention-core kernel (dominant kernel) timed with HIP
+  events around its own launches on the stream it runs on, against the
+  bf16 dense matrix-core peak;
+* cpu_baseline: the float64 CPU oracle on a bounded sample (one batch item)
+  of the same workload, in the same unit.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MHA fwd TFLOP/s and % bf16 MFMA peak (T=4096, h=16, d_k=64, causal)"
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense matrix-core peaks
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters (optional)")
+    return ap.parse_args()
+
+
+def workspace_views(ws, w, torch):
+    """Qh, Kh, Vh inside the forward's workspace (layout documented in mha.h)."""
+    es = 2 if w.dtype == "bf16" else 4
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def r256(x):
+        return (x + 255) // 256 * 256
+    sizes = [w.B * w.h * w.n_q * w.d_h, w.B * w.h * w.n_k * w.d_h, w.B * w.h * w.n_k * w.d_vh]
+    shapes = [(w.B, w.h, w.n_q, w.d_h), (w.B, w.h, w.n_k, w.d_h), (w.B, w.h, w.n_k, w.d_vh)]
+    out, off = [], 0
+    for n, shp in zip(sizes, shapes):
+        out.append(ws[off:off + n * es].view(dt).view(shp))
+        off += r256(n * es)
+    return out
+
+
+def cpu_baseline(w, x):
+    """Time the float64 oracle on one batch item of the workload."""
+    import numpy as np
+    from oracle import allowed_set, mha_ref
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    sub = {k: x[k][:1].astype(np.float64) for k in ("Q", "K", "V")}
+    kl = None if x["key_len"] is None else x["key_len"][:1]
+    Ws = {k: x[k].astype(np.float64) for k in ("W_Q", "W_K", "W_V", "W_O")}
+    allow = allowed_set(1, w.n_q, w.n_k, causal=w.causal, key_len=kl)
+    t0 = time.perf_counter()
+    mha_ref(sub["Q"], sub["K"], sub["V"], Ws["W_Q"], Ws["W_K"], Ws["W_V"], Ws["W_O"], w.h,
+            w.d_h, w.d_vh, w.scale, allow)
+    dt = time.perf_counter() - t0
+    flops = (w.core_flops_effective(kl) + w.proj_flops()) / w.B
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"1 of {w.B} batch items of {w.name}: dense float64 oracle (full score "
+                      f"matrix per head, no causal skipping), FLOPs counted as for the GPU"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding plan is design-only)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import transformer_head_self_amd as mha
+    from transformer_head_self_amd.inputs import HEADLINE, WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    x = make_inputs(w)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def put(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(tdt)
+
+    Q = put(x["Q"])
+    K, V = (Q, Q) if w.kind == "self" else (put(x["K"]), put(x["V"]))
+    W = {k: put(x[k]) for k in ("W_Q", "W_K", "W_V", "W_O")}
+    kl = None if x["key_len"] is None else torch.from_numpy(x["key_len"]).to(dev)
+    Y = torch.empty((w.B, w.n_q, w.d_o), dtype=torch.float32, device=dev)
+    dims = mha.MhaDims(B=w.B, h=w.h, n_q=w.n_q, n_k=w.n_k, d_q=w.d_q, d_k=w.d_k, d_v=w.d_v,
+                       d_h=w.d_h, d_vh=w.d_vh, d_o=w.d_o, scale=w.scale,
+                       in_dtype=1 if w.dtype == "bf16" else 0, out_dtype=0)
+    ws = torch.empty(mha.mha_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mha.mha_forward(Q, K, V, W["W_Q"], W["W_K"], W["W_V"], W["W_O"], w.h, w.d_h, w.d_vh,
+                        scale=w.scale, causal=w.causal, key_len=kl, Y=Y, workspace=ws,
+                        stream=stream)
+
+    # ---- whole forward --------------------------------------------------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # ---- the dominant kernel alone: attention core on the projected heads ----
+    Qh, Kh, Vh = workspace_views(ws, w, torch)
+    Z = torch.empty((w.B, w.n_q, w.h * w.d_vh), dtype=tdt, device=dev)
+
+    def core():
+        mha.attn_core(Qh, Kh, Vh, scale=w.scale, causal=w.causal, key_len=kl, out_dtype=tdt,
+                      Z=Z, stream=stream)
+
+    for _ in range(args.warmup):
+        core()
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(args.steps):
+        core()
+    c1.record(stream)
+    torch.cuda.synchronize()
+    ms_core = c0.elapsed_time(c1) / args.steps
+
+    core_flops = w.core_flops_effective(x["key_len"])
+    total_flops = core_flops + w.proj_flops()
+    value = total_flops / (ms_step * 1e-3) / 1e12
+    core_tflops = core_flops / (ms_core * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            entry = tj.get(w.name, {}).get("attn_core")
+            traffic = None if entry is None else entry.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "n_q": w.n_q, "n_k": w.n_k, "d_q": w.d_q,
+                   "h": w.h, "d_h": w.d_h, "d_vh": w.d_vh, "d_o": w.d_o,
+                   "mask": "causal" if w.causal else ("key_padding" if w.pad_range else "none"),
+                   "parallelism": "single-gpu"},
+        "e2e_frac_of_peak": round(value / peak, 4),
+        "attn_core": {"ms": round(ms_core, 5), "tflops": round(core_tflops, 3),
+                      "frac_of_peak": round(core_tflops / peak, 4),
+                      "gflop": round(core_flops / 1e9, 3)},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel (attention core)",
+                     "achieved": round(core_tflops, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(core_tflops / peak, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,147 @@
+/*
+ * mha.h - C ABI of the MI355X (gfx950) multi-head attention forward library.
+ *
+ * What is computed
+ * ----------------
+ * Page "Multi-head attention and self-attention", Definition: for query,
+ * key and value matrices Q [n_q x d_q], K [n_k x d_k], V [n_k x d_v], head i
+ * is scaled dot-product attention of (Q W_i^Q, K W_i^K, V W_i^V) under one
+ * mask shared by every head; the heads are concatenated along the feature
+ * axis in head order and multiplied by W^O [h*d_vh x d_o].  Self-attention
+ * is the case Q = K = V.
+ * Page "Stable summary of an attention key block", Definition: the row
+ * softmax is computed as running (m, l, z) summaries of key blocks merged
+ * with the page's rule, so no score matrix is ever written to memory.
+ * Review page "Multi-Head Attention", "Separate and Combined Projections":
+ * weights are passed combined, head r occupying a contiguous column block.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor is dense, row-major, with the shapes given below, and lives
+ *   in device memory (hipMalloc'd or equivalent) unless a comment says host.
+ * - Element type of Q, K, V, the weights and the projected heads is
+ *   mha_dims.in_dtype; accumulation is always fp32.  With in_dtype BF16 the
+ *   projected heads, the softmax weights fed to the value product and the
+ *   concatenated heads are rounded to bfloat16 (round to nearest even).
+ * - The library allocates nothing, keeps no state between calls, never
+ *   synchronises, and enqueues its kernels on `stream` (a hipStream_t; NULL
+ *   means the null stream).  The caller owns every buffer.
+ * - Every argument that the host can check is checked before anything is
+ *   launched; on error nothing is launched and nothing is written.
+ * - Pointers must be aligned to their element size; 16-byte alignment and
+ *   row widths that are multiples of 16 bytes select the vectorised paths.
+ *
+ * Device-side preconditions (not checked: they would need a device read)
+ * ----------------------------------------------------------------------
+ * - 0 <= key_len[b] <= n_k.
+ * - Every query row has at least one allowed key (the summary definition
+ *   requires nonempty allowed sets).  A row with none gets NaN outputs
+ *   (0/0), row_m = -inf and row_l = 0.
+ */
+#ifndef MHA_H
+#define MHA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MHA_OK = 0,
+  MHA_ERR_NULL = -1,        /* a required pointer is NULL                           */
+  MHA_ERR_DIM = -2,         /* a dimension is <= 0, or an index would overflow       */
+  MHA_ERR_DTYPE = -3,       /* unknown in_dtype / out_dtype                          */
+  MHA_ERR_MASK = -4,        /* bad mask flags, causal with n_q != n_k, missing data  */
+  MHA_ERR_ALIGN = -5,       /* a pointer is not aligned to its element size          */
+  MHA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than mha_workspace_bytes()  */
+  MHA_ERR_UNSUPPORTED = -7, /* d_h or d_vh above the largest instantiated head width */
+  MHA_ERR_LAUNCH = -8,      /* the HIP runtime reported an error at launch           */
+  MHA_ERR_SCALE = -9        /* scale is not a finite number                          */
+} mha_status;
+
+typedef enum { MHA_F32 = 0, MHA_BF16 = 1 } mha_dtype;
+
+/* Mask rules, OR-able; 0 means every key is allowed.  The allowed set of a
+ * query row is the AND of every selected rule.  Page "From Attention to
+ * Self-Attention" review, "Distinctions to Keep": a causal mask removes
+ * later positions, a padding mask removes artificial key positions, and the
+ * two may be combined.  Page "Multi-head attention and self-attention",
+ * Definition: any chosen mask, one for every head (there is no head axis). */
+#define MHA_MASK_CAUSAL 1u      /* key j allowed for query i only if j <= i (needs n_q == n_k) */
+#define MHA_MASK_KEY_PADDING 2u /* key j allowed only if j < key_len[b]                      */
+#define MHA_MASK_BOOL 4u        /* key j allowed only if allowed[b][i][j] != 0               */
+
+typedef struct mha_mask {
+  uint32_t flags;               /* OR of MHA_MASK_* (unknown bits: MHA_ERR_MASK)            */
+  const int32_t* key_len;       /* [B] valid keys per batch item (KEY_PADDING), device      */
+  const uint8_t* allowed;       /* [Bm][n_q][n_k], 1 = allowed (BOOL), device               */
+  int64_t allowed_batch_stride; /* elements between items; 0 = one mask for the batch       */
+} mha_mask;
+
+/* Dimensions use the general definition's names (page "Multi-head attention
+ * and self-attention", Definition). */
+typedef struct mha_dims {
+  int32_t B;     /* batch items (independent; never mixed)            */
+  int32_t h;     /* heads                                             */
+  int32_t n_q;   /* query rows per item                               */
+  int32_t n_k;   /* key / value rows per item                         */
+  int32_t d_q;   /* query input width                                 */
+  int32_t d_k;   /* key input width                                   */
+  int32_t d_v;   /* value input width                                 */
+  int32_t d_h;   /* per-head query/key width                          */
+  int32_t d_vh;  /* per-head value width                              */
+  int32_t d_o;   /* output width                                      */
+  float scale;   /* score scale c; the usual choice is 1/sqrt(d_h)    */
+  int32_t in_dtype;  /* mha_dtype of inputs, weights, projected heads */
+  int32_t out_dtype; /* mha_dtype of Y (mha_forward) or Z (attn_core)  */
+} mha_dims;
+
+/* Bytes of scratch mha_forward needs for these dims: the projected heads
+ * Qh [B,h,n_q,d_h], Kh [B,h,n_k,d_h], Vh [B,h,n_k,d_vh] and the
+ * concatenation Z [B,n_q,h*d_vh], all in in_dtype, each 256-byte aligned.
+ * Returns 0 if `d` is NULL or invalid. */
+size_t mha_workspace_bytes(const mha_dims* d);
+
+/* Full forward pass.  Page "Multi-head attention and self-attention",
+ * Definition; review page "Multi-Head Attention", "The Complete Multi-Head
+ * Operation" (no biases).
+ *   Q   [B, n_q, d_q]   K [B, n_k, d_k]   V [B, n_k, d_v]        (in_dtype)
+ *   W_Q [d_q, h*d_h]    W_K [d_k, h*d_h]  W_V [d_v, h*d_vh]      (in_dtype)
+ *   W_O [h*d_vh, d_o]                                            (in_dtype)
+ *   Y   [B, n_q, d_o]                                            (out_dtype, written)
+ *   row_m, row_l  optional [B, h, n_q] fp32 (may be NULL): the final row
+ *        maximum of the scaled scores (natural-log units) and the shifted
+ *        normaliser sum_j exp(s_ij - row_m).
+ *   workspace  device scratch of at least mha_workspace_bytes(d) bytes.
+ * Q, K and V may alias (self-attention).  m may be NULL (no mask). */
+mha_status mha_forward(const mha_dims* d, const mha_mask* m,
+                       const void* Q, const void* K, const void* V,
+                       const void* W_Q, const void* W_K, const void* W_V,
+                       const void* W_O, void* Y, float* row_m, float* row_l,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention on projected heads, written in the concatenated layout.
+ * Page "Stable summary of an attention key block", Definition (summaries,
+ * merge, final division); review page "Multi-Head Attention", shapes and
+ * "Audit Order" (concatenate along the head-feature axis in head order).
+ * Uses B, h, n_q, n_k, d_h, d_vh, scale, in_dtype, out_dtype of `d`.
+ *   Qh [B, h, n_q, d_h]  Kh [B, h, n_k, d_h]  Vh [B, h, n_k, d_vh]   (in_dtype)
+ *   Z  [B, n_q, h*d_vh]  head r in columns r*d_vh .. r*d_vh+d_vh-1   (out_dtype)
+ *   row_m, row_l  optional, as for mha_forward. */
+mha_status attn_core(const mha_dims* d, const mha_mask* m,
+                     const void* Qh, const void* Kh, const void* Vh, void* Z,
+                     float* row_m, float* row_l, void* stream);
+
+/* Static, human-readable name of a status code (host memory, never freed). */
+const char* mha_status_string(int status);
+
+/* Largest per-head widths the kernels are built for (d_h, d_vh). */
+int32_t mha_max_head_dim(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHA_H */

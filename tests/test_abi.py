@@ -1,0 +1,195 @@
+"""CPU tests of the C ABI: the library loads, exports what include/mha.h
+declares, lays out its structs as the binding does, and rejects every
+host-checkable violation before touching the GPU (no kernel is launched in
+these tests: each call fails validation first).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import transformer_head_self_amd as mha
+from transformer_head_self_amd import MhaDims, MhaMask
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mha.h")
+
+FAKE = 0x10000  # a non-null, 256-byte aligned address; never dereferenced here
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    names = re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\([^;{]*\)\s*;", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("mha_forward", "attn_core", "mha_workspace_bytes", "mha_status_string",
+              "mha_max_head_dim"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = mha.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), f"libmha.so does not export {name}"
+    out = subprocess.run(["nm", "-D", "--defined-only", mha.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in exported
+
+
+def test_struct_layout_matches_header():
+    """Compile a tiny C program against the header and compare with ctypes."""
+    prog = r"""
+    #include <stdio.h>
+    #include <stddef.h>
+    #include "mha.h"
+    int main(void) {
+      printf("%zu %zu %zu %zu %zu %zu\n", sizeof(mha_dims), offsetof(mha_dims, scale),
+             offsetof(mha_dims, out_dtype), sizeof(mha_mask), offsetof(mha_mask, key_len),
+             offsetof(mha_mask, allowed_batch_stride));
+      return 0;
+    }
+    """
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(c, "w").write(prog)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), c, "-o", exe],
+                       check=True)
+        vals = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
+                                               check=True).stdout.split()]
+    assert vals == [ctypes.sizeof(MhaDims), MhaDims.scale.offset, MhaDims.out_dtype.offset,
+                    ctypes.sizeof(MhaMask), MhaMask.key_len.offset,
+                    MhaMask.allowed_batch_stride.offset]
+
+
+def _dims(**kw):
+    base = dict(B=2, h=4, n_q=64, n_k=64, d_q=64, d_k=64, d_v=64, d_h=16, d_vh=16, d_o=64,
+                scale=0.25, in_dtype=mha.MHA_F32, out_dtype=mha.MHA_F32)
+    base.update(kw)
+    return MhaDims(**base)
+
+
+def _fwd(d, m=None, ptrs=None, ws_bytes=1 << 30, ws=FAKE):
+    L = mha.lib()
+    p = [FAKE] * 8 if ptrs is None else ptrs
+    mp = ctypes.byref(m) if m is not None else None
+    return L.mha_forward(ctypes.byref(d) if d is not None else None, mp, *p, None, None, ws,
+                         ws_bytes, None)
+
+
+def _core(d, m=None, ptrs=None):
+    L = mha.lib()
+    p = [FAKE] * 4 if ptrs is None else ptrs
+    mp = ctypes.byref(m) if m is not None else None
+    return L.attn_core(ctypes.byref(d) if d is not None else None, mp, *p, None, None, None)
+
+
+def test_status_strings():
+    for code in range(0, -10, -1):
+        s = mha.mha_status_string(code)
+        assert s.startswith("MHA_")
+    assert "unknown" in mha.mha_status_string(-99)
+
+
+@pytest.mark.parametrize("field", ["B", "h", "n_q", "n_k", "d_q", "d_k", "d_v", "d_h", "d_vh",
+                                   "d_o"])
+def test_nonpositive_dims_rejected(field):
+    d = _dims(**{field: 0})
+    assert _fwd(d) == -2
+    if field in ("B", "h", "n_q", "n_k", "d_h", "d_vh"):
+        assert _core(_dims(**{field: -3})) == -2
+
+
+def test_overflowing_dims_rejected():
+    assert _fwd(_dims(B=1 << 16, n_q=1 << 16, n_k=1 << 16)) == -2
+
+
+def test_null_dims_and_pointers():
+    assert _fwd(None) == -1
+    assert _core(None) == -1
+    for i in range(8):
+        p = [FAKE] * 8
+        p[i] = None
+        assert _fwd(_dims(), ptrs=p) == -1
+    for i in range(4):
+        p = [FAKE] * 4
+        p[i] = None
+        assert _core(_dims(), ptrs=p) == -1
+
+
+def test_bad_dtype_and_scale():
+    assert _fwd(_dims(in_dtype=7)) == -3
+    assert _core(_dims(out_dtype=-1)) == -3
+    assert _fwd(_dims(scale=float("inf"))) == -9
+    assert _core(_dims(scale=float("nan"))) == -9
+
+
+def test_head_width_above_instantiated_maximum():
+    top = mha.lib().mha_max_head_dim()
+    assert top >= 128
+    assert _fwd(_dims(d_h=top + 1)) == -7
+    assert _core(_dims(d_vh=top + 8)) == -7
+
+
+def test_mask_descriptor_errors():
+    m = MhaMask(flags=8)
+    assert _fwd(_dims(), m) == -4
+    m = MhaMask(flags=mha.MHA_MASK_CAUSAL)
+    assert _fwd(_dims(n_k=65), m) == -4         # causal needs n_q == n_k
+    assert _core(_dims(n_q=10, n_k=11), m) == -4
+    m = MhaMask(flags=mha.MHA_MASK_KEY_PADDING)  # no key_len
+    assert _fwd(_dims(), m) == -4
+    m = MhaMask(flags=mha.MHA_MASK_BOOL)         # no allowed
+    assert _core(_dims(), m) == -4
+    m = MhaMask(flags=mha.MHA_MASK_BOOL, allowed=FAKE, allowed_batch_stride=5)
+    assert _core(_dims(), m) == -4               # stride shorter than one mask plane
+    m = MhaMask(flags=mha.MHA_MASK_KEY_PADDING, key_len=FAKE + 2)
+    assert _core(_dims(), m) == -5               # int32 array misaligned
+
+
+def test_misaligned_pointers():
+    p = [FAKE] * 8
+    p[0] = FAKE + 2                              # fp32 needs 4-byte alignment
+    assert _fwd(_dims(), ptrs=p) == -5
+    p = [FAKE] * 8
+    p[0] = FAKE + 2                              # bf16 accepts 2-byte alignment ...
+    p[7] = FAKE + 2                              # ... but Y (fp32 out) does not
+    assert _fwd(_dims(in_dtype=mha.MHA_BF16), ptrs=p) == -5
+    q = [FAKE] * 4
+    q[3] = FAKE + 1
+    assert _core(_dims(), ptrs=q) == -5
+
+
+def test_workspace_checks():
+    d = _dims()
+    need = mha.mha_workspace_bytes(d)
+    assert need > 0
+    assert _fwd(d, ws_bytes=need - 1) == -6
+    assert _fwd(d, ws=None) == -6
+    assert _fwd(d, ws=FAKE + 16, ws_bytes=need) == -5   # workspace must be 256-byte aligned
+
+
+def test_workspace_bytes_formula_and_monotonicity():
+    def r256(x):
+        return (x + 255) // 256 * 256
+    for dt, es in ((mha.MHA_F32, 4), (mha.MHA_BF16, 2)):
+        d = _dims(B=3, h=5, n_q=37, n_k=101, d_h=24, d_vh=40, in_dtype=dt)
+        expect = (r256(3 * 5 * 37 * 24 * es) + r256(3 * 5 * 101 * 24 * es) +
+                  r256(3 * 5 * 101 * 40 * es) + r256(3 * 37 * 5 * 40 * es))
+        assert mha.mha_workspace_bytes(d) == expect
+    base = mha.mha_workspace_bytes(_dims())
+    for f in ("B", "h", "n_q", "n_k", "d_h", "d_vh"):
+        bigger = _dims(**{f: getattr(_dims(), f) * 2})
+        assert mha.mha_workspace_bytes(bigger) > base
+    assert mha.mha_workspace_bytes(_dims(B=0)) == 0

@@ -1,0 +1,347 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Metric: max |out - ref| / RMS(ref) over every element (padded query rows
+included).  Bars: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs with fp32
+accumulation.  Small problems are compared in full; the large workloads are
+compared on sampled query rows that the oracle computes one by one, in the
+same launch configuration the benchmark times.  Exact (==) checks cover the
+properties that must hold bit for bit: forbidden keys do not influence the
+result, batch items do not mix, W_O = 0 gives 0, W_V leaves (m, l) alone,
+a row with one allowed key returns that key's value, runs are deterministic.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import transformer_head_self_amd as mha  # noqa: E402
+from transformer_head_self_amd.inputs import (  # noqa: E402
+    WORKLOADS, custom_workload, make_heads, make_inputs)
+from oracle import allowed_set, attn_core_ref, mha_ref, mha_ref_rows  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _rel_err(out, ref):
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert out.shape == ref.shape
+    rms = math.sqrt(float(np.mean(ref * ref)))
+    return float(np.max(np.abs(out - ref))) / rms
+
+
+def _tdtype(dt):
+    return torch.float32 if dt == "f32" else torch.bfloat16
+
+
+def _to_dev(a, dt):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(_tdtype(dt))
+
+
+def _run_forward(w, x, out_dtype=torch.float32, row_stats=False, **overrides):
+    dt = w.dtype
+    Q = _to_dev(x["Q"], dt)
+    if w.kind == "self":
+        K = V = Q
+    else:
+        K, V = _to_dev(x["K"], dt), _to_dev(x["V"], dt)
+    W = {k: _to_dev(x[k], dt) for k in ("W_Q", "W_K", "W_V", "W_O")}
+    rm = rl = None
+    if row_stats:
+        rm = torch.empty((w.B, w.h, w.n_q), dtype=torch.float32, device=DEV)
+        rl = torch.empty_like(rm)
+    kl = None if x["key_len"] is None else torch.from_numpy(x["key_len"]).to(DEV)
+    Y = mha.mha_forward(Q, K, V, W["W_Q"], W["W_K"], W["W_V"], W["W_O"], w.h, w.d_h, w.d_vh,
+                        causal=w.causal, key_len=kl, out_dtype=out_dtype, row_m=rm, row_l=rl,
+                        **overrides)
+    torch.cuda.synchronize()
+    if row_stats:
+        return Y.float().cpu().numpy(), rm.cpu().numpy(), rl.cpu().numpy()
+    return Y.float().cpu().numpy()
+
+
+def _allow(w, x):
+    return allowed_set(w.B, w.n_q, w.n_k, causal=w.causal, key_len=x["key_len"])
+
+
+# ---------------------------------------------------------------------------
+# the page's worked example, on the GPU
+# ---------------------------------------------------------------------------
+
+def test_worked_example_two_tokens():
+    Qh = torch.tensor([[[[1.0, 1.0]]]], device=DEV)
+    Kh = torch.tensor([[[[1.0, 1.0], [1.0, -1.0]]]], device=DEV)
+    Vh = torch.tensor([[[[1.0, 0.0], [0.0, 1.0]]]], device=DEV)
+    rm = torch.empty((1, 1, 1), device=DEV)
+    rl = torch.empty((1, 1, 1), device=DEV)
+    Z = mha.attn_core(Qh, Kh, Vh, scale=1 / math.sqrt(2.0), row_m=rm, row_l=rl)
+    torch.cuda.synchronize()
+    w1 = 1.0 / (1.0 + math.exp(-math.sqrt(2.0)))
+    np.testing.assert_allclose(Z.cpu().numpy()[0, 0], [w1, 1 - w1], atol=1e-6)
+    assert abs(float(rm) - math.sqrt(2.0)) < 1e-6
+    assert abs(float(rl) * math.exp(float(rm)) - (1 + math.exp(math.sqrt(2.0)))) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# the benchmark workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", [
+    "self-f32-B2-T64-dm64-h4-dh16-causal",
+    "self-f32-B8-T512-dm512-h8-dh64-keypad",
+    "cross-bf16-B16-nq512-nk2048-h12-dh64-dvh96-keypad",
+])
+def test_workload_full_parity(name):
+    w = WORKLOADS[name]
+    _say(f"[parity full] {name}")
+    x = make_inputs(w)
+    Y, rm, rl = _run_forward(w, x, row_stats=True)
+    ref = mha_ref(x["Q"], x["K"], x["V"], x["W_Q"], x["W_K"], x["W_V"], x["W_O"], w.h, w.d_h,
+                  w.d_vh, w.scale, _allow(w, x))
+    err = _rel_err(Y, ref["Y"])
+    _say(f"  Y err {err:.3e} (bar {TOL[w.dtype]})")
+    assert err <= TOL[w.dtype]
+    # the summaries' final (m, l): m in natural-log units
+    np.testing.assert_allclose(rm, ref["m"], rtol=0, atol=2e-2 if w.dtype == "bf16" else 1e-4)
+    np.testing.assert_allclose(rl, ref["l"], rtol=3e-2 if w.dtype == "bf16" else 1e-4)
+
+
+SAMPLE_ROWS = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, 255, 256, 1000, 2047, 2048, 4095]
+
+
+@pytest.mark.parametrize("name", [
+    "self-bf16-B4-T4096-dm1024-h16-dh64-causal",
+    "self-bf16-B1-T16384-dm2048-h16-dh128-causal",
+])
+def test_workload_sampled_parity(name):
+    w = WORKLOADS[name]
+    _say(f"[parity sampled] {name}")
+    x = make_inputs(w)
+    Y = _run_forward(w, x)
+    rng = np.random.default_rng(99)
+    rows = sorted(set([r for r in SAMPLE_ROWS if r < w.n_q] + [w.n_q - 1] +
+                      list(rng.integers(0, w.n_q, 16))))
+    allow = _allow(w, x)
+    outs, refs = [], []
+    for b in sorted({0, w.B - 1}):
+        Yr, _, _, _ = mha_ref_rows(x["Q"], x["K"], x["V"], x["W_Q"], x["W_K"], x["W_V"],
+                                   x["W_O"], w.h, w.d_h, w.d_vh, w.scale, allow, b, rows)
+        outs.append(Y[b, rows])
+        refs.append(Yr)
+    err = _rel_err(np.concatenate(outs), np.concatenate(refs))
+    _say(f"  Y err on {len(rows)} rows x {len(outs)} items: {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
+# ---------------------------------------------------------------------------
+# attention core on ragged shapes (tails of every tile, odd widths)
+# ---------------------------------------------------------------------------
+
+CORE_CASES = [
+    # dtype, B, h, n_q, n_k, d_h, d_vh, causal, pad, bool
+    ("f32", 2, 3, 100, 333, 40, 24, False, None, False),
+    ("f32", 1, 2, 200, 200, 64, 64, True, None, False),
+    ("f32", 3, 1, 77, 77, 8, 12, True, (1, 77), False),
+    ("bf16", 2, 3, 130, 257, 64, 96, False, (1, 257), False),
+    ("bf16", 2, 2, 300, 300, 128, 128, True, None, False),
+    ("bf16", 1, 4, 65, 65, 32, 32, True, (10, 65), True),
+    ("f32", 2, 2, 50, 70, 16, 16, False, None, True),
+    ("bf16", 3, 2, 1, 129, 64, 64, False, (1, 129), False),
+]
+
+
+@pytest.mark.parametrize("case", CORE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_attn_core_ragged(case):
+    dt, B, h, n_q, n_k, d_h, d_vh, causal, pad, use_bool = case
+    _say(f"[core ragged] {case}")
+    Qh, Kh, Vh = make_heads(B, h, n_q, n_k, d_h, d_vh, dt, seed=B * 1000 + n_q)
+    rng = np.random.default_rng(n_k)
+    kl = None if pad is None else rng.integers(pad[0], pad[1], size=B, endpoint=True).astype(np.int32)
+    G = None
+    if use_bool:
+        G = rng.random((B, n_q, n_k)) < 0.5
+        G[:, :, 0] = True
+    allow = allowed_set(B, n_q, n_k, causal=causal, key_len=kl, allowed=G)
+    scale = 1.0 / math.sqrt(d_h)
+    ref = attn_core_ref(Qh, Kh, Vh, scale, allow)
+    rm = torch.empty((B, h, n_q), device=DEV)
+    rl = torch.empty_like(rm)
+    Z = mha.attn_core(_to_dev(Qh, dt), _to_dev(Kh, dt), _to_dev(Vh, dt), scale=scale,
+                      causal=causal, key_len=None if kl is None else torch.from_numpy(kl).to(DEV),
+                      allowed=None if G is None else torch.from_numpy(G).to(DEV),
+                      row_m=rm, row_l=rl)
+    torch.cuda.synchronize()
+    err = _rel_err(Z.cpu().numpy(), ref["Z"])
+    _say(f"  Z err {err:.3e}")
+    assert err <= TOL[dt]
+    np.testing.assert_allclose(rm.cpu().numpy(), ref["m"], rtol=0, atol=1e-5)
+    np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-5 if dt == "f32" else 1e-3)
+
+
+def test_attn_core_bool_mask_broadcast():
+    B, h, n = 3, 2, 96
+    Qh, Kh, Vh = make_heads(B, h, n, n, 64, 64, "f32", seed=5)
+    G = np.random.default_rng(6).random((1, n, n)) < 0.3
+    G[:, np.arange(n), np.arange(n)] = True
+    allow = allowed_set(B, n, n, allowed=G)
+    ref = attn_core_ref(Qh, Kh, Vh, 0.125, allow)["Z"]
+    Z = mha.attn_core(_to_dev(Qh, "f32"), _to_dev(Kh, "f32"), _to_dev(Vh, "f32"), scale=0.125,
+                      allowed=torch.from_numpy(G).to(DEV))
+    torch.cuda.synchronize()
+    assert _rel_err(Z.cpu().numpy(), ref) <= 1e-4
+
+
+# ---------------------------------------------------------------------------
+# closed forms and exact properties
+# ---------------------------------------------------------------------------
+
+def test_zero_scale_prefix_mean_at_full_size():
+    """c = 0: every allowed weight is equal, so row i returns the mean of v_0..v_i."""
+    B, h, T, d = 4, 16, 4096, 64
+    _say("[zero scale] B=4 h=16 T=4096 d=64 causal")
+    Qh, Kh, Vh = make_heads(B, h, T, T, d, d, "bf16", seed=7)
+    Z = mha.attn_core(_to_dev(Qh, "bf16"), _to_dev(Kh, "bf16"), _to_dev(Vh, "bf16"), scale=0.0,
+                      causal=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Z = Z.cpu().numpy().reshape(B, T, h, d)
+    for b in (0, B - 1):
+        for r in (0, h - 1):
+            ref = np.cumsum(Vh[b, r].astype(np.float64), axis=0) / np.arange(1, T + 1)[:, None]
+            assert _rel_err(Z[b, :, r], ref) < 1e-5
+
+
+def test_single_allowed_key_returns_value_exactly():
+    B, h, T = 2, 3, 256
+    for dt in ("f32", "bf16"):
+        Qh, Kh, Vh = make_heads(B, h, T, T, 64, 64, dt, seed=8)
+        Z = mha.attn_core(_to_dev(Qh, dt), _to_dev(Kh, dt), _to_dev(Vh, dt), causal=True,
+                          out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        Z = Z.cpu().numpy()
+        for r in range(h):
+            assert np.array_equal(Z[:, 0, r * 64:(r + 1) * 64], Vh[:, r, 0].astype(np.float32))
+
+
+def test_forbidden_keys_do_not_matter_exactly():
+    B, h, T, d = 2, 2, 384, 64
+    for dt in ("f32", "bf16"):
+        Qh, Kh, Vh = make_heads(B, h, T, T, d, d, dt, seed=9)
+        kl = np.array([300, 200], np.int32)
+        t0 = 150
+        args = dict(causal=True, key_len=torch.from_numpy(kl).to(DEV))
+        Z1 = mha.attn_core(_to_dev(Qh, dt), _to_dev(Kh, dt), _to_dev(Vh, dt), **args)
+        K2, V2 = Kh.copy(), Vh.copy()
+        K2[:, :, t0:] = 3.0 * np.flip(K2[:, :, t0:], axis=2)   # finite, different
+        V2[:, :, t0:] = -7.0
+        Z2 = mha.attn_core(_to_dev(Qh, dt), _to_dev(K2, dt), _to_dev(V2, dt), **args)
+        torch.cuda.synchronize()
+        # rows before t0 never see keys >= t0 (causal)
+        assert torch.equal(Z1[:, :t0], Z2[:, :t0])
+        # padding: item 1 never sees keys >= 200
+        K3, V3 = Kh.copy(), Vh.copy()
+        K3[1, :, 200:] = 5.0
+        V3[1, :, 200:] = 9.0
+        Z3 = mha.attn_core(_to_dev(Qh, dt), _to_dev(K3, dt), _to_dev(V3, dt), **args)
+        torch.cuda.synchronize()
+        assert torch.equal(Z1[1], Z3[1])
+
+
+def test_batch_items_do_not_mix_and_runs_repeat():
+    w = WORKLOADS["self-f32-B8-T512-dm512-h8-dh64-keypad"]
+    x = make_inputs(w)
+    Y1 = _run_forward(w, x)
+    Y1b = _run_forward(w, x)
+    assert np.array_equal(Y1, Y1b)          # deterministic
+    x2 = dict(x)
+    Q2 = x["Q"].copy()
+    Q2[3] = np.random.default_rng(3).standard_normal(Q2[3].shape).astype(np.float32)
+    x2["Q"] = x2["K"] = x2["V"] = Q2
+    Y2 = _run_forward(w, x2)
+    keep = [b for b in range(w.B) if b != 3]
+    assert np.array_equal(Y1[keep], Y2[keep])
+    assert not np.allclose(Y1[3], Y2[3])
+
+
+def test_output_projection_zero_gives_exact_zero():
+    w = WORKLOADS["cross-bf16-B16-nq512-nk2048-h12-dh64-dvh96-keypad"]
+    x = make_inputs(w)
+    x["W_O"] = np.zeros_like(x["W_O"])
+    Y = _run_forward(w, x)
+    assert np.all(Y == 0.0)
+
+
+def test_value_projection_leaves_weights_exactly():
+    w = WORKLOADS["self-f32-B2-T64-dm64-h4-dh16-causal"]
+    x = make_inputs(w)
+    _, rm1, rl1 = _run_forward(w, x, row_stats=True)
+    x2 = dict(x)
+    x2["W_V"] = np.random.default_rng(4).standard_normal(x["W_V"].shape).astype(np.float32)
+    _, rm2, rl2 = _run_forward(w, x2, row_stats=True)
+    assert np.array_equal(rm1, rm2) and np.array_equal(rl1, rl2)
+
+
+def test_self_attention_equals_general_path_with_copies():
+    w = WORKLOADS["self-f32-B2-T64-dm64-h4-dh16-causal"]
+    x = make_inputs(w)
+    Y1 = _run_forward(w, x)
+    wc = custom_workload(kind="cross", dtype="f32", B=w.B, n_q=w.n_q, n_k=w.n_k, d_q=w.d_q,
+                         d_k=w.d_k, d_v=w.d_v, h=w.h, d_h=w.d_h, d_vh=w.d_vh, d_o=w.d_o,
+                         causal=True)
+    xc = dict(x)
+    xc["K"] = x["Q"].copy()
+    xc["V"] = x["Q"].copy()
+    Y2 = _run_forward(wc, xc)
+    assert np.array_equal(Y1, Y2)
+
+
+def test_head_permutation_invariance_gpu():
+    w = WORKLOADS["self-f32-B2-T64-dm64-h4-dh16-causal"]
+    x = make_inputs(w)
+    Y1 = _run_forward(w, x)
+    perm = [2, 0, 3, 1]
+    cq = np.concatenate([np.arange(r * w.d_h, (r + 1) * w.d_h) for r in perm])
+    cv = np.concatenate([np.arange(r * w.d_vh, (r + 1) * w.d_vh) for r in perm])
+    xp = dict(x)
+    xp["W_Q"], xp["W_K"] = x["W_Q"][:, cq].copy(), x["W_K"][:, cq].copy()
+    xp["W_V"], xp["W_O"] = x["W_V"][:, cv].copy(), x["W_O"][cv].copy()
+    Y2 = _run_forward(w, xp)
+    assert _rel_err(Y2, Y1) <= 1e-5
+
+
+def test_empty_allowed_row_gives_nan():
+    """key_len = 0 leaves no allowed key: the documented result is a NaN row."""
+    B, h, n = 2, 2, 64
+    Qh, Kh, Vh = make_heads(B, h, n, n, 32, 32, "f32", seed=10)
+    rm = torch.empty((B, h, n), device=DEV)
+    rl = torch.empty_like(rm)
+    Z = mha.attn_core(_to_dev(Qh, "f32"), _to_dev(Kh, "f32"), _to_dev(Vh, "f32"),
+                      key_len=torch.tensor([0, n], dtype=torch.int32, device=DEV),
+                      row_m=rm, row_l=rl)
+    torch.cuda.synchronize()
+    Z = Z.cpu().numpy()
+    assert np.all(np.isnan(Z[0]))
+    assert np.all(np.isfinite(Z[1]))
+    assert np.all(rm.cpu().numpy()[0] == -np.inf) and np.all(rl.cpu().numpy()[0] == 0)
+
+
+def test_bf16_output_dtype():
+    w = WORKLOADS["cross-bf16-B16-nq512-nk2048-h12-dh64-dvh96-keypad"]
+    x = make_inputs(w)
+    Y = _run_forward(w, x, out_dtype=torch.bfloat16)
+    ref = mha_ref(x["Q"], x["K"], x["V"], x["W_Q"], x["W_K"], x["W_V"], x["W_O"], w.h, w.d_h,
+                  w.d_vh, w.scale, _allow(w, x))["Y"]
+    # bf16 storage of Y adds up to half an ulp (2^-9 relative) per element
+    err = float(np.max(np.abs(Y - ref) / (np.abs(ref) * 2.0 ** -8 + 2e-2 * np.sqrt(np.mean(ref ** 2)))))
+    assert err <= 1.0

@@ -1,0 +1,197 @@
+"""MI355X (gfx950) multi-head attention forward: Python binding of libmha.so.
+
+The functions here only marshal arguments: they turn torch tensors into
+device pointers and sizes, allocate outputs and scratch with torch, and call
+the C ABI declared in ``include/mha.h`` on torch's current HIP stream.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback, and every call raises if the library is missing or returns an error.
+
+Entry points (same names as the C ABI):
+* ``mha_forward``  projections, fused attention, concatenation, W^O.
+* ``attn_core``    fused attention on already projected heads.
+* ``mha_workspace_bytes``, ``mha_status_string``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "MhaError", "MhaDims", "MhaMask", "lib", "mha_forward", "attn_core",
+    "mha_workspace_bytes", "mha_status_string", "MHA_F32", "MHA_BF16",
+    "MHA_MASK_CAUSAL", "MHA_MASK_KEY_PADDING", "MHA_MASK_BOOL",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmha.so")
+
+MHA_F32, MHA_BF16 = 0, 1
+MHA_MASK_CAUSAL, MHA_MASK_KEY_PADDING, MHA_MASK_BOOL = 1, 2, 4
+
+
+class MhaError(RuntimeError):
+    def __init__(self, status, where=""):
+        self.status = int(status)
+        super().__init__(f"{where}: {mha_status_string(status)} ({status})")
+
+
+class MhaDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "h", "n_q", "n_k", "d_q", "d_k", "d_v", "d_h", "d_vh", "d_o")] + [
+        ("scale", ctypes.c_float), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+class MhaMask(ctypes.Structure):
+    _fields_ = [("flags", ctypes.c_uint32), ("key_len", ctypes.c_void_p),
+                ("allowed", ctypes.c_void_p), ("allowed_batch_stride", ctypes.c_int64)]
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded libmha.so (ctypes), with argument types declared."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                "(hipcc, gfx950) before calling the library")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, P = ctypes.c_void_p, ctypes.POINTER
+        L.mha_workspace_bytes.argtypes = [P(MhaDims)]
+        L.mha_workspace_bytes.restype = ctypes.c_size_t
+        L.mha_forward.argtypes = [P(MhaDims), P(MhaMask)] + [vp] * 8 + [vp, vp, vp,
+                                                                          ctypes.c_size_t, vp]
+        L.mha_forward.restype = ctypes.c_int
+        L.attn_core.argtypes = [P(MhaDims), P(MhaMask), vp, vp, vp, vp, vp, vp, vp]
+        L.attn_core.restype = ctypes.c_int
+        L.mha_status_string.argtypes = [ctypes.c_int]
+        L.mha_status_string.restype = ctypes.c_char_p
+        L.mha_max_head_dim.argtypes = []
+        L.mha_max_head_dim.restype = ctypes.c_int32
+        _LIB = L
+    return _LIB
+
+
+def mha_status_string(status):
+    return lib().mha_status_string(int(status)).decode()
+
+
+def mha_workspace_bytes(dims: MhaDims):
+    return int(lib().mha_workspace_bytes(ctypes.byref(dims)))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t == torch.float32:
+        return MHA_F32
+    if t == torch.bfloat16:
+        return MHA_BF16
+    raise TypeError(f"unsupported element type {t}; use float32 or bfloat16")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _mask(B, n_q, n_k, causal, key_len, allowed, device):
+    torch = _torch()
+    m = MhaMask()
+    m.flags = 0
+    keep = []
+    if causal:
+        m.flags |= MHA_MASK_CAUSAL
+    if key_len is not None:
+        kl = torch.as_tensor(key_len, dtype=torch.int32, device=device).contiguous()
+        keep.append(kl)
+        m.flags |= MHA_MASK_KEY_PADDING
+        m.key_len = kl.data_ptr()
+    if allowed is not None:
+        G = torch.as_tensor(allowed, device=device).to(torch.uint8).contiguous()
+        if G.dim() != 3 or G.shape[1:] != (n_q, n_k) or G.shape[0] not in (1, B):
+            raise ValueError("allowed must have shape [B or 1, n_q, n_k]")
+        keep.append(G)
+        m.flags |= MHA_MASK_BOOL
+        m.allowed = G.data_ptr()
+        m.allowed_batch_stride = 0 if G.shape[0] == 1 else n_q * n_k
+    return m, keep
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def mha_forward(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, *, scale=None, causal=False,
+                key_len=None, allowed=None, out_dtype=None, Y=None, row_m=None, row_l=None,
+                workspace=None, stream=None):
+    """Y [B, n_q, d_o] = MHA(Q, K, V) for Q [B,n_q,d_q], K [B,n_k,d_k], V [B,n_k,d_v].
+
+    Weights are combined (head r in column block r): W_Q [d_q, h*d_h],
+    W_K [d_k, h*d_h], W_V [d_v, h*d_vh], W_O [h*d_vh, d_o].  ``scale``
+    defaults to 1/sqrt(d_h).  ``out_dtype`` defaults to float32.
+    """
+    torch = _torch()
+    B, n_q, d_q = Q.shape
+    n_k, d_k = K.shape[1], K.shape[2]
+    d_v = V.shape[2]
+    d_o = W_O.shape[1]
+    in_code = _dtype_code(Q.dtype)
+    for t in (K, V, W_Q, W_K, W_V, W_O):
+        if t.dtype != Q.dtype:
+            raise TypeError("Q, K, V and the weights must share one element type")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    dims = MhaDims(B=B, h=h, n_q=n_q, n_k=n_k, d_q=d_q, d_k=d_k, d_v=d_v, d_h=d_h, d_vh=d_vh,
+                   d_o=d_o, scale=(1.0 / math.sqrt(d_h)) if scale is None else float(scale),
+                   in_dtype=in_code, out_dtype=_dtype_code(out_dtype))
+    m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Q.device)
+    if Y is None:
+        Y = torch.empty((B, n_q, d_o), dtype=out_dtype, device=Q.device)
+    need = mha_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    st = lib().mha_forward(ctypes.byref(dims), ctypes.byref(m), _ptr(Q), _ptr(K), _ptr(V),
+                           _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_O), _ptr(Y), _ptr(row_m),
+                           _ptr(row_l), _ptr(workspace), workspace.numel(), _stream(stream))
+    del keep
+    if st != 0:
+        raise MhaError(st, "mha_forward")
+    return Y
+
+
+def attn_core(Qh, Kh, Vh, *, scale=None, causal=False, key_len=None, allowed=None,
+              out_dtype=None, Z=None, row_m=None, row_l=None, stream=None):
+    """Z [B, n_q, h*d_vh] from heads Qh [B,h,n_q,d_h], Kh [B,h,n_k,d_h], Vh [B,h,n_k,d_vh]."""
+    torch = _torch()
+    B, h, n_q, d_h = Qh.shape
+    n_k = Kh.shape[2]
+    d_vh = Vh.shape[3]
+    if Kh.dtype != Qh.dtype or Vh.dtype != Qh.dtype:
+        raise TypeError("Qh, Kh and Vh must share one element type")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    dims = MhaDims(B=B, h=h, n_q=n_q, n_k=n_k, d_q=1, d_k=1, d_v=1, d_h=d_h, d_vh=d_vh, d_o=1,
+                   scale=(1.0 / math.sqrt(d_h)) if scale is None else float(scale),
+                   in_dtype=_dtype_code(Qh.dtype), out_dtype=_dtype_code(out_dtype))
+    m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Qh.device)
+    if Z is None:
+        Z = torch.empty((B, n_q, h * d_vh), dtype=out_dtype, device=Qh.device)
+    st = lib().attn_core(ctypes.byref(dims), ctypes.byref(m), _ptr(Qh), _ptr(Kh), _ptr(Vh),
+                         _ptr(Z), _ptr(row_m), _ptr(row_l), _stream(stream))
+    del keep
+    if st != 0:
+        raise MhaError(st, "attn_core")
+    return Z

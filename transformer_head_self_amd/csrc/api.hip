@@ -1,0 +1,259 @@
+// C ABI of the multi-head attention forward library (declared in include/mha.h).
+//
+// Host side only: argument validation (before any launch), workspace carving
+// and the three launches of the forward pass, all on the caller's stream.
+// Page "Multi-head attention and self-attention", Definition: head i attends
+// over (Q W_i^Q, K W_i^K, V W_i^V) and the concatenated heads are multiplied
+// by W^O.  Review page "Multi-Head Attention", "The Complete Multi-Head
+// Operation": project, attend per head, concatenate, project once more.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/mha.h"
+#include "internal.hpp"
+
+namespace mha {
+hipError_t launch_attention_bf16(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream);
+
+hipError_t launch_attention(const AttnParams& p, int in_dtype, hipStream_t stream) {
+  return in_dtype == kBF16 ? launch_attention_bf16(p, stream) : launch_attention_f32(p, stream);
+}
+}  // namespace mha
+
+namespace {
+
+constexpr int64_t kIntMax = 2147483647LL;
+
+size_t esize(int dtype) { return dtype == MHA_BF16 ? 2 : 4; }
+int vec_elems(int dtype) { return dtype == MHA_BF16 ? 8 : 4; }
+bool valid_dtype(int dt) { return dt == MHA_F32 || dt == MHA_BF16; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Dims used by the attention core: B, h, n_q, n_k, d_h, d_vh, scale, dtypes.
+mha_status check_core_dims(const mha_dims* d) {
+  if (!d) return MHA_ERR_NULL;
+  if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return MHA_ERR_DTYPE;
+  if (d->B <= 0 || d->h <= 0 || d->n_q <= 0 || d->n_k <= 0 || d->d_h <= 0 || d->d_vh <= 0)
+    return MHA_ERR_DIM;
+  if (!isfinite(d->scale)) return MHA_ERR_SCALE;
+  // every row index and flattened row count must stay below 2^31
+  const int64_t B = d->B, h = d->h;
+  if (B * d->n_q > kIntMax || B * d->n_k > kIntMax || B * h * d->n_q > kIntMax ||
+      B * h * d->n_k > kIntMax || h * d->d_h > kIntMax || h * d->d_vh > kIntMax)
+    return MHA_ERR_DIM;
+  if (d->d_h > mha::kMaxHeadDim || d->d_vh > mha::kMaxHeadDim) return MHA_ERR_UNSUPPORTED;
+  return MHA_OK;
+}
+
+mha_status check_full_dims(const mha_dims* d) {
+  mha_status s = check_core_dims(d);
+  if (s != MHA_OK) return s;
+  if (d->d_q <= 0 || d->d_k <= 0 || d->d_v <= 0 || d->d_o <= 0) return MHA_ERR_DIM;
+  return MHA_OK;
+}
+
+mha_status check_mask(const mha_dims* d, const mha_mask* m) {
+  if (!m) return MHA_OK;
+  const uint32_t known = MHA_MASK_CAUSAL | MHA_MASK_KEY_PADDING | MHA_MASK_BOOL;
+  if (m->flags & ~known) return MHA_ERR_MASK;
+  if ((m->flags & MHA_MASK_CAUSAL) && d->n_q != d->n_k) return MHA_ERR_MASK;
+  if ((m->flags & MHA_MASK_KEY_PADDING) && !m->key_len) return MHA_ERR_MASK;
+  if (m->flags & MHA_MASK_BOOL) {
+    if (!m->allowed) return MHA_ERR_MASK;
+    const int64_t plane = (int64_t)d->n_q * d->n_k;
+    if (m->allowed_batch_stride != 0 && m->allowed_batch_stride < plane) return MHA_ERR_MASK;
+  }
+  if ((m->flags & MHA_MASK_KEY_PADDING) && !aligned(m->key_len, 4)) return MHA_ERR_ALIGN;
+  return MHA_OK;
+}
+
+void fill_mask(mha::AttnParams& p, const mha_mask* m) {
+  p.causal = 0;
+  p.key_len = nullptr;
+  p.allowed = nullptr;
+  p.allowed_batch_stride = 0;
+  if (!m) return;
+  p.causal = (m->flags & MHA_MASK_CAUSAL) ? 1 : 0;
+  if (m->flags & MHA_MASK_KEY_PADDING) p.key_len = m->key_len;
+  if (m->flags & MHA_MASK_BOOL) {
+    p.allowed = m->allowed;
+    p.allowed_batch_stride = m->allowed_batch_stride;
+  }
+}
+
+struct Workspace {
+  size_t q, k, v, z, total;
+};
+
+Workspace carve(const mha_dims* d) {
+  const size_t es = esize(d->in_dtype);
+  const size_t B = d->B, h = d->h;
+  Workspace w;
+  w.q = 0;
+  w.k = w.q + round256(B * h * d->n_q * d->d_h * es);
+  w.v = w.k + round256(B * h * d->n_k * d->d_h * es);
+  w.z = w.v + round256(B * h * d->n_k * d->d_vh * es);
+  w.total = w.z + round256(B * d->n_q * h * d->d_vh * es);
+  return w;
+}
+
+void attn_params(mha::AttnParams& p, const mha_dims* d, const void* Qh, const void* Kh,
+                 const void* Vh, void* Z, int z_dtype, float* row_m, float* row_l) {
+  const int vin = vec_elems(d->in_dtype);
+  p.Q = Qh;
+  p.K = Kh;
+  p.V = Vh;
+  p.Z = Z;
+  p.row_m = row_m;
+  p.row_l = row_l;
+  p.B = d->B;
+  p.h = d->h;
+  p.n_q = d->n_q;
+  p.n_k = d->n_k;
+  p.d_h = d->d_h;
+  p.d_vh = d->d_vh;
+  p.ldq = d->d_h;
+  p.ldk = d->d_h;
+  p.ldv = d->d_vh;
+  p.ldz = d->h * d->d_vh;
+  p.scale_log2 = d->scale * 1.4426950408889634f;
+  p.out_dtype = z_dtype;
+  p.vec_q = aligned(Qh, 16) && (p.ldq % vin == 0);
+  p.vec_k = aligned(Kh, 16) && (p.ldk % vin == 0);
+  p.vec_v = aligned(Vh, 16) && (p.ldv % vin == 0);
+  p.vec_z = aligned(Z, z_dtype == MHA_BF16 ? 8 : 16) && (p.ldz % 4 == 0) && (d->d_vh % 4 == 0);
+  p.num_q_tiles = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mha_workspace_bytes(const mha_dims* d) {
+  if (check_full_dims(d) != MHA_OK) return 0;
+  return carve(d).total;
+}
+
+int32_t mha_max_head_dim(void) { return mha::kMaxHeadDim; }
+
+const char* mha_status_string(int s) {
+  switch (s) {
+    case MHA_OK: return "MHA_OK";
+    case MHA_ERR_NULL: return "MHA_ERR_NULL: a required pointer is NULL";
+    case MHA_ERR_DIM: return "MHA_ERR_DIM: a dimension is not positive or is too large";
+    case MHA_ERR_DTYPE: return "MHA_ERR_DTYPE: unknown element type";
+    case MHA_ERR_MASK: return "MHA_ERR_MASK: invalid mask descriptor";
+    case MHA_ERR_ALIGN: return "MHA_ERR_ALIGN: a pointer is misaligned for its element type";
+    case MHA_ERR_WORKSPACE: return "MHA_ERR_WORKSPACE: workspace missing or too small";
+    case MHA_ERR_UNSUPPORTED: return "MHA_ERR_UNSUPPORTED: head width above the instantiated maximum";
+    case MHA_ERR_LAUNCH: return "MHA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    case MHA_ERR_SCALE: return "MHA_ERR_SCALE: the score scale is not finite";
+    default: return "unknown mha_status";
+  }
+}
+
+mha_status attn_core(const mha_dims* d, const mha_mask* m, const void* Qh, const void* Kh,
+                     const void* Vh, void* Z, float* row_m, float* row_l, void* stream) {
+  mha_status s = check_core_dims(d);
+  if (s != MHA_OK) return s;
+  if ((s = check_mask(d, m)) != MHA_OK) return s;
+  if (!Qh || !Kh || !Vh || !Z) return MHA_ERR_NULL;
+  const size_t ei = esize(d->in_dtype), eo = esize(d->out_dtype);
+  if (!aligned(Qh, ei) || !aligned(Kh, ei) || !aligned(Vh, ei) || !aligned(Z, eo) ||
+      !aligned(row_m, 4) || !aligned(row_l, 4))
+    return MHA_ERR_ALIGN;
+  mha::AttnParams p;
+  memset(&p, 0, sizeof(p));
+  attn_params(p, d, Qh, Kh, Vh, Z, d->out_dtype, row_m, row_l);
+  fill_mask(p, m);
+  if (mha::launch_attention(p, d->in_dtype, (hipStream_t)stream) != hipSuccess)
+    return MHA_ERR_LAUNCH;
+  return MHA_OK;
+}
+
+mha_status mha_forward(const mha_dims* d, const mha_mask* m, const void* Q, const void* K,
+                       const void* V, const void* W_Q, const void* W_K, const void* W_V,
+                       const void* W_O, void* Y, float* row_m, float* row_l, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  mha_status s = check_full_dims(d);
+  if (s != MHA_OK) return s;
+  if ((s = check_mask(d, m)) != MHA_OK) return s;
+  if (!Q || !K || !V || !W_Q || !W_K || !W_V || !W_O || !Y) return MHA_ERR_NULL;
+  const size_t ei = esize(d->in_dtype), eo = esize(d->out_dtype);
+  if (!aligned(Q, ei) || !aligned(K, ei) || !aligned(V, ei) || !aligned(W_Q, ei) ||
+      !aligned(W_K, ei) || !aligned(W_V, ei) || !aligned(W_O, ei) || !aligned(Y, eo) ||
+      !aligned(row_m, 4) || !aligned(row_l, 4))
+    return MHA_ERR_ALIGN;
+  const Workspace w = carve(d);
+  if (!workspace || workspace_bytes < w.total) return MHA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MHA_ERR_ALIGN;
+
+  char* ws = static_cast<char*>(workspace);
+  void* Qh = ws + w.q;
+  void* Kh = ws + w.k;
+  void* Vh = ws + w.v;
+  void* Z = ws + w.z;
+  const int vin = vec_elems(d->in_dtype);
+  hipStream_t st = (hipStream_t)stream;
+
+  // K1: the three head projections in one launch, stored head-major.
+  mha::GemmBatch gb;
+  memset(&gb, 0, sizeof(gb));
+  gb.count = 3;
+  const void* srcs[3] = {Q, K, V};
+  const void* ws3[3] = {W_Q, W_K, W_V};
+  void* dst[3] = {Qh, Kh, Vh};
+  const int Ms[3] = {d->B * d->n_q, d->B * d->n_k, d->B * d->n_k};
+  const int Ks[3] = {d->d_q, d->d_k, d->d_v};
+  const int dhs[3] = {d->d_h, d->d_h, d->d_vh};
+  const int ntoks[3] = {d->n_q, d->n_k, d->n_k};
+  for (int i = 0; i < 3; ++i) {
+    mha::GemmProblem& p = gb.p[i];
+    p.A = srcs[i];
+    p.W = ws3[i];
+    p.C = dst[i];
+    p.M = Ms[i];
+    p.N = d->h * dhs[i];
+    p.K = Ks[i];
+    p.epilogue = mha::kHeads;
+    p.out_dtype = d->in_dtype;
+    p.heads = d->h;
+    p.dh = dhs[i];
+    p.ntok = ntoks[i];
+    p.vec_a = aligned(p.A, 16) && (p.K % vin == 0);
+    p.vec_w = aligned(p.W, 16) && (p.N % vin == 0);
+    p.vec_c = 1;
+  }
+  if (mha::launch_gemm(gb, d->in_dtype, st) != hipSuccess) return MHA_ERR_LAUNCH;
+
+  // K2: fused attention, written into the concatenation Z (in_dtype).
+  mha::AttnParams ap;
+  memset(&ap, 0, sizeof(ap));
+  attn_params(ap, d, Qh, Kh, Vh, Z, d->in_dtype, row_m, row_l);
+  fill_mask(ap, m);
+  if (mha::launch_attention(ap, d->in_dtype, st) != hipSuccess) return MHA_ERR_LAUNCH;
+
+  // K3: Y = Z W^O, row-major.
+  mha::GemmBatch ob;
+  memset(&ob, 0, sizeof(ob));
+  ob.count = 1;
+  mha::GemmProblem& o = ob.p[0];
+  o.A = Z;
+  o.W = W_O;
+  o.C = Y;
+  o.M = d->B * d->n_q;
+  o.N = d->d_o;
+  o.K = d->h * d->d_vh;
+  o.epilogue = mha::kRowMajor;
+  o.out_dtype = d->out_dtype;
+  o.vec_a = (o.K % vin == 0);
+  o.vec_w = aligned(W_O, 16) && (o.N % vin == 0);
+  o.vec_c = aligned(Y, 16);
+  if (mha::launch_gemm(ob, d->in_dtype, st) != hipSuccess) return MHA_ERR_LAUNCH;
+  return MHA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,8 @@
+// bf16 instantiations of the fused attention kernel.
+#include "attn_launch.hpp"
+
+namespace mha {
+hipError_t launch_attention_bf16(const AttnParams& p, hipStream_t stream) {
+  return launch_attn_typed<bf16>(p, stream);
+}
+}  // namespace mha

@@ -1,0 +1,37 @@
+// Head-width dispatch for the fused attention kernel of one element type.
+#pragma once
+
+#include "attn.hpp"
+
+namespace mha {
+
+template <typename T, int DH, int DV>
+hipError_t launch_attn_fixed(AttnParams p, hipStream_t stream) {
+  constexpr int WAVES = 4;
+  typedef AttnCfg<T, DH, DV, WAVES> C;
+  p.num_q_tiles = (p.n_q + C::QT - 1) / C::QT;
+  const long long grid = (long long)p.num_q_tiles * p.B * p.h;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES>), dim3((unsigned)grid), dim3(C::NT), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int DH>
+hipError_t launch_attn_dv(const AttnParams& p, hipStream_t stream) {
+  if (p.d_vh <= 32) return launch_attn_fixed<T, DH, 32>(p, stream);
+  if (p.d_vh <= 64) return launch_attn_fixed<T, DH, 64>(p, stream);
+  if (p.d_vh <= 96) return launch_attn_fixed<T, DH, 96>(p, stream);
+  if (p.d_vh <= 128) return launch_attn_fixed<T, DH, 128>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_attn_typed(const AttnParams& p, hipStream_t stream) {
+  if (p.d_h <= 32) return launch_attn_dv<T, 32>(p, stream);
+  if (p.d_h <= 64) return launch_attn_dv<T, 64>(p, stream);
+  if (p.d_h <= 128) return launch_attn_dv<T, 128>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mha

@@ -1,0 +1,71 @@
+// Internal interfaces between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mha {
+
+enum DType : int { kF32 = 0, kBF16 = 1 };
+
+// ---------------------------------------------------------------------------
+// Projection GEMM: C = A[M,K] * W[K,N], both row-major, fp32 accumulation.
+// Up to three independent problems per launch (the Q, K and V projections).
+// Epilogue modes:
+//   kHeads: column n -> head r = n / dh, e = n % dh; row m -> item b = m / ntok,
+//           position t = m % ntok; stores out[((b*h + r)*ntok + t)*dh + e]
+//           (the (B,T,h*d) -> (B,h,T,d) reshape/transpose folded into the store)
+//   kRowMajor: out[m*N + n]
+// ---------------------------------------------------------------------------
+enum GemmEpilogue : int { kHeads = 0, kRowMajor = 1 };
+
+struct GemmProblem {
+  const void* A;     // [M, K]
+  const void* W;     // [K, N]
+  void* C;           // see epilogue
+  int M, N, K;
+  int epilogue;      // GemmEpilogue
+  int out_dtype;     // DType of C
+  int heads, dh, ntok;  // kHeads only
+  int tiles_m, tiles_n, tile_begin;  // filled by the launcher
+  int vec_a, vec_w;  // 16-byte vector loads allowed for A / W rows
+  int vec_c;         // vector stores allowed for C (kRowMajor)
+};
+
+struct GemmBatch {
+  GemmProblem p[3];
+  int count;
+  int total_tiles;
+};
+
+hipError_t launch_gemm(const GemmBatch& batch, int in_dtype, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Fused attention: Z[b, i, r*d_vh + e] = sum_j softmax_j(c * q_i . k_j | mask) v_j[e]
+// computed with running (m, l, z) summaries over key blocks.
+// ---------------------------------------------------------------------------
+struct AttnParams {
+  const void* Q;     // [B, h, n_q, ldq]   (first d_h columns used)
+  const void* K;     // [B, h, n_k, ldk]
+  const void* V;     // [B, h, n_k, ldv]   (first d_vh columns used)
+  void* Z;           // [B, n_q, ldz], head r at column r*d_vh
+  float* row_m;      // optional [B, h, n_q]
+  float* row_l;      // optional [B, h, n_q]
+  const int32_t* key_len;   // optional [B]
+  const uint8_t* allowed;   // optional [Bm, n_q, n_k]
+  long long allowed_batch_stride;
+  int B, h, n_q, n_k, d_h, d_vh;
+  int ldq, ldk, ldv, ldz;
+  float scale_log2;  // c * log2(e)
+  int causal;
+  int out_dtype;
+  int vec_q, vec_k, vec_v, vec_z;
+  int num_q_tiles;   // filled by the launcher
+};
+
+hipError_t launch_attention(const AttnParams& p, int in_dtype, hipStream_t stream);
+
+// Largest head widths with an instantiated kernel.
+constexpr int kMaxHeadDim = 128;
+
+}  // namespace mha

@@ -19,10 +19,15 @@
  * ---------------------------------------
  * - Every tensor is dense, row-major, with the shapes given below, and lives
  *   in device memory (hipMalloc'd or equivalent) unless a comment says host.
- * - Element type of Q, K, V, the weights and the projected heads is
- *   mha_dims.in_dtype; accumulation is always fp32.  With in_dtype BF16 the
- *   projected heads, the softmax weights fed to the value product and the
- *   concatenated heads are rounded to bfloat16 (round to nearest even).
+ * - Q, K, V and the weights have element type mha_dims.in_dtype.  The
+ *   intermediates of mha_forward (projected heads, the softmax weights fed
+ *   to the value product, the concatenated heads) have element type
+ *   mha_dims.work_dtype, rounded to nearest even; every sum is accumulated
+ *   in fp32.  Allowed (in, work) pairs: (F32, F32), (BF16, F16),
+ *   (BF16, BF16), (F16, F16).  (BF16, F16) is the precise choice for bf16
+ *   inputs: fp16 keeps three more mantissa bits than bf16 at the same
+ *   matrix-core rate, provided every intermediate stays below 65504 in
+ *   magnitude (projected values of order one are far inside that range).
  * - The library allocates nothing, keeps no state between calls, never
  *   synchronises, and enqueues its kernels on `stream` (a hipStream_t; NULL
  *   means the null stream).  The caller owns every buffer.
@@ -52,7 +57,7 @@ typedef enum {
   MHA_OK = 0,
   MHA_ERR_NULL = -1,        /* a required pointer is NULL                           */
   MHA_ERR_DIM = -2,         /* a dimension is <= 0, or an index would overflow       */
-  MHA_ERR_DTYPE = -3,       /* unknown in_dtype / out_dtype                          */
+  MHA_ERR_DTYPE = -3,       /* unknown dtype, or an unsupported (in, work) pair      */
   MHA_ERR_MASK = -4,        /* bad mask flags, causal with n_q != n_k, missing data  */
   MHA_ERR_ALIGN = -5,       /* a pointer is not aligned to its element size          */
   MHA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than mha_workspace_bytes()  */
@@ -61,7 +66,7 @@ typedef enum {
   MHA_ERR_SCALE = -9        /* scale is not a finite number                          */
 } mha_status;
 
-typedef enum { MHA_F32 = 0, MHA_BF16 = 1 } mha_dtype;
+typedef enum { MHA_F32 = 0, MHA_BF16 = 1, MHA_F16 = 2 } mha_dtype;
 
 /* Mask rules, OR-able; 0 means every key is allowed.  The allowed set of a
  * query row is the AND of every selected rule.  Page "From Attention to
@@ -94,13 +99,16 @@ typedef struct mha_dims {
   int32_t d_vh;  /* per-head value width                              */
   int32_t d_o;   /* output width                                      */
   float scale;   /* score scale c; the usual choice is 1/sqrt(d_h)    */
-  int32_t in_dtype;  /* mha_dtype of inputs, weights, projected heads */
-  int32_t out_dtype; /* mha_dtype of Y (mha_forward) or Z (attn_core)  */
+  int32_t in_dtype;   /* mha_dtype of Q, K, V, weights (mha_forward) or
+                          of Qh, Kh, Vh (attn_core)                    */
+  int32_t out_dtype;  /* mha_dtype of Y (mha_forward) or Z (attn_core) */
+  int32_t work_dtype; /* mha_forward intermediates (see above); ignored
+                          by attn_core, whose weights use in_dtype      */
 } mha_dims;
 
 /* Bytes of scratch mha_forward needs for these dims: the projected heads
  * Qh [B,h,n_q,d_h], Kh [B,h,n_k,d_h], Vh [B,h,n_k,d_vh] and the
- * concatenation Z [B,n_q,h*d_vh], all in in_dtype, each 256-byte aligned.
+ * concatenation Z [B,n_q,h*d_vh], all in work_dtype, each 256-byte aligned.
  * Returns 0 if `d` is NULL or invalid. */
 size_t mha_workspace_bytes(const mha_dims* d);
 

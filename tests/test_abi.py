@@ -54,9 +54,9 @@ def test_struct_layout_matches_header():
     #include <stddef.h>
     #include "mha.h"
     int main(void) {
-      printf("%zu %zu %zu %zu %zu %zu\n", sizeof(mha_dims), offsetof(mha_dims, scale),
-             offsetof(mha_dims, out_dtype), sizeof(mha_mask), offsetof(mha_mask, key_len),
-             offsetof(mha_mask, allowed_batch_stride));
+      printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(mha_dims), offsetof(mha_dims, scale),
+             offsetof(mha_dims, out_dtype), offsetof(mha_dims, work_dtype), sizeof(mha_mask),
+             offsetof(mha_mask, key_len), offsetof(mha_mask, allowed_batch_stride));
       return 0;
     }
     """
@@ -69,13 +69,13 @@ def test_struct_layout_matches_header():
         vals = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
                                                check=True).stdout.split()]
     assert vals == [ctypes.sizeof(MhaDims), MhaDims.scale.offset, MhaDims.out_dtype.offset,
-                    ctypes.sizeof(MhaMask), MhaMask.key_len.offset,
+                    MhaDims.work_dtype.offset, ctypes.sizeof(MhaMask), MhaMask.key_len.offset,
                     MhaMask.allowed_batch_stride.offset]
 
 
 def _dims(**kw):
     base = dict(B=2, h=4, n_q=64, n_k=64, d_q=64, d_k=64, d_v=64, d_h=16, d_vh=16, d_o=64,
-                scale=0.25, in_dtype=mha.MHA_F32, out_dtype=mha.MHA_F32)
+                scale=0.25, in_dtype=mha.MHA_F32, out_dtype=mha.MHA_F32, work_dtype=mha.MHA_F32)
     base.update(kw)
     return MhaDims(**base)
 
@@ -131,6 +131,12 @@ def test_null_dims_and_pointers():
 def test_bad_dtype_and_scale():
     assert _fwd(_dims(in_dtype=7)) == -3
     assert _core(_dims(out_dtype=-1)) == -3
+    # (in, work) pairs: fp32 inputs need fp32 intermediates; 2-byte inputs 2-byte ones
+    assert _fwd(_dims(in_dtype=mha.MHA_F32, work_dtype=mha.MHA_F16)) == -3
+    assert _fwd(_dims(in_dtype=mha.MHA_BF16, work_dtype=mha.MHA_F32)) == -3
+    assert _fwd(_dims(in_dtype=mha.MHA_F16, work_dtype=mha.MHA_BF16)) == -3
+    # attn_core ignores work_dtype
+    assert _core(_dims(work_dtype=9, scale=float("nan"))) == -9
     assert _fwd(_dims(scale=float("inf"))) == -9
     assert _core(_dims(scale=float("nan"))) == -9
 
@@ -165,7 +171,7 @@ def test_misaligned_pointers():
     p = [FAKE] * 8
     p[0] = FAKE + 2                              # bf16 accepts 2-byte alignment ...
     p[7] = FAKE + 2                              # ... but Y (fp32 out) does not
-    assert _fwd(_dims(in_dtype=mha.MHA_BF16), ptrs=p) == -5
+    assert _fwd(_dims(in_dtype=mha.MHA_BF16, work_dtype=mha.MHA_F16), ptrs=p) == -5
     q = [FAKE] * 4
     q[3] = FAKE + 1
     assert _core(_dims(), ptrs=q) == -5
@@ -183,8 +189,9 @@ def test_workspace_checks():
 def test_workspace_bytes_formula_and_monotonicity():
     def r256(x):
         return (x + 255) // 256 * 256
-    for dt, es in ((mha.MHA_F32, 4), (mha.MHA_BF16, 2)):
-        d = _dims(B=3, h=5, n_q=37, n_k=101, d_h=24, d_vh=40, in_dtype=dt)
+    for dt, wt, es in ((mha.MHA_F32, mha.MHA_F32, 4), (mha.MHA_BF16, mha.MHA_F16, 2),
+                       (mha.MHA_BF16, mha.MHA_BF16, 2), (mha.MHA_F16, mha.MHA_F16, 2)):
+        d = _dims(B=3, h=5, n_q=37, n_k=101, d_h=24, d_vh=40, in_dtype=dt, work_dtype=wt)
         expect = (r256(3 * 5 * 37 * 24 * es) + r256(3 * 5 * 101 * 24 * es) +
                   r256(3 * 5 * 101 * 40 * es) + r256(3 * 37 * 5 * 40 * es))
         assert mha.mha_workspace_bytes(d) == expect

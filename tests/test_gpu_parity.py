@@ -187,7 +187,8 @@ def test_attn_core_ragged(case):
     _say(f"  Z err {err:.3e}")
     assert err <= TOL[dt]
     np.testing.assert_allclose(rm.cpu().numpy(), ref["m"], rtol=0, atol=1e-5)
-    np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-5 if dt == "f32" else 1e-3)
+    # bf16: l sums the rounded weights (2^-9 relative each)
+    np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-5 if dt == "f32" else 4e-3)
 
 
 def test_attn_core_bool_mask_broadcast():
@@ -334,6 +335,49 @@ def test_empty_allowed_row_gives_nan():
     assert np.all(np.isnan(Z[0]))
     assert np.all(np.isfinite(Z[1]))
     assert np.all(rm.cpu().numpy()[0] == -np.inf) and np.all(rl.cpu().numpy()[0] == 0)
+
+
+def test_bf16_intermediates_option():
+    """work_dtype=bfloat16 keeps bf16 intermediates: it runs, within its own bound.
+
+    Rounding the projected heads, weights and concatenation to bf16 costs about
+    3e-2 of the output RMS on this workload (emulated in float64 on the CPU), so
+    the spec bar needs fp16 intermediates, the default; this option is
+    checked against a 6e-2 bar.
+    """
+    w = WORKLOADS["cross-bf16-B16-nq512-nk2048-h12-dh64-dvh96-keypad"]
+    x = make_inputs(w)
+    Y = _run_forward(w, x, work_dtype=torch.bfloat16)
+    ref = mha_ref(x["Q"], x["K"], x["V"], x["W_Q"], x["W_K"], x["W_V"], x["W_O"], w.h, w.d_h,
+                  w.d_vh, w.scale, _allow(w, x))["Y"]
+    err = _rel_err(Y, ref)
+    _say(f"  bf16 intermediates: Y err {err:.3e}")
+    assert err <= 6e-2
+
+
+def test_attn_core_f16_heads():
+    B, h, n = 2, 4, 300
+    Qh, Kh, Vh = make_heads(B, h, n, n, 64, 64, "f32", seed=12)
+    to16 = lambda a: torch.from_numpy(a).to(DEV).to(torch.float16)
+    Qh16, Kh16, Vh16 = (t.float().cpu().numpy() for t in (to16(Qh), to16(Kh), to16(Vh)))
+    ref = attn_core_ref(Qh16, Kh16, Vh16, 0.125, allowed_set(B, n, n, causal=True))["Z"]
+    Z = mha.attn_core(to16(Qh), to16(Kh), to16(Vh), scale=0.125, causal=True)
+    torch.cuda.synchronize()
+    err = _rel_err(Z.cpu().numpy(), ref)
+    _say(f"  f16 heads: Z err {err:.3e}")
+    assert err <= 2e-3
+
+
+def test_negative_and_zero_scale_match_oracle():
+    B, h, n = 1, 2, 200
+    for dt in ("f32", "bf16"):
+        Qh, Kh, Vh = make_heads(B, h, n, n, 64, 64, dt, seed=13)
+        for c in (-0.3, 0.0):
+            ref = attn_core_ref(Qh, Kh, Vh, c, allowed_set(B, n, n, causal=True))["Z"]
+            Z = mha.attn_core(_to_dev(Qh, dt), _to_dev(Kh, dt), _to_dev(Vh, dt), scale=c,
+                              causal=True)
+            torch.cuda.synchronize()
+            assert _rel_err(Z.cpu().numpy(), ref) <= TOL[dt]
 
 
 def test_bf16_output_dtype():

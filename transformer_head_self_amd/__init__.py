@@ -20,13 +20,13 @@ import os
 
 __all__ = [
     "MhaError", "MhaDims", "MhaMask", "lib", "mha_forward", "attn_core",
-    "mha_workspace_bytes", "mha_status_string", "MHA_F32", "MHA_BF16",
+    "mha_workspace_bytes", "mha_status_string", "MHA_F32", "MHA_BF16", "MHA_F16",
     "MHA_MASK_CAUSAL", "MHA_MASK_KEY_PADDING", "MHA_MASK_BOOL",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmha.so")
 
-MHA_F32, MHA_BF16 = 0, 1
+MHA_F32, MHA_BF16, MHA_F16 = 0, 1, 2
 MHA_MASK_CAUSAL, MHA_MASK_KEY_PADDING, MHA_MASK_BOOL = 1, 2, 4
 
 
@@ -39,7 +39,8 @@ class MhaError(RuntimeError):
 class MhaDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "h", "n_q", "n_k", "d_q", "d_k", "d_v", "d_h", "d_vh", "d_o")] + [
-        ("scale", ctypes.c_float), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+        ("scale", ctypes.c_float), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("work_dtype", ctypes.c_int32)]
 
 
 class MhaMask(ctypes.Structure):
@@ -94,7 +95,9 @@ def _dtype_code(t):
         return MHA_F32
     if t == torch.bfloat16:
         return MHA_BF16
-    raise TypeError(f"unsupported element type {t}; use float32 or bfloat16")
+    if t == torch.float16:
+        return MHA_F16
+    raise TypeError(f"unsupported element type {t}; use float32, bfloat16 or float16")
 
 
 def _ptr(t):
@@ -136,14 +139,21 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def default_work_dtype(in_dtype):
+    """Intermediate element type used when the caller does not choose one."""
+    torch = _torch()
+    return torch.float16 if in_dtype in (torch.bfloat16, torch.float16) else torch.float32
+
+
 def mha_forward(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, *, scale=None, causal=False,
-                key_len=None, allowed=None, out_dtype=None, Y=None, row_m=None, row_l=None,
-                workspace=None, stream=None):
+                key_len=None, allowed=None, out_dtype=None, work_dtype=None, Y=None,
+                row_m=None, row_l=None, workspace=None, stream=None):
     """Y [B, n_q, d_o] = MHA(Q, K, V) for Q [B,n_q,d_q], K [B,n_k,d_k], V [B,n_k,d_v].
 
     Weights are combined (head r in column block r): W_Q [d_q, h*d_h],
     W_K [d_k, h*d_h], W_V [d_v, h*d_vh], W_O [h*d_vh, d_o].  ``scale``
-    defaults to 1/sqrt(d_h).  ``out_dtype`` defaults to float32.
+    defaults to 1/sqrt(d_h); ``out_dtype`` to float32; ``work_dtype`` (the
+    intermediates' element type) to float16 for 2-byte inputs, else float32.
     """
     torch = _torch()
     B, n_q, d_q = Q.shape
@@ -155,9 +165,11 @@ def mha_forward(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, *, scale=None, causal
         if t.dtype != Q.dtype:
             raise TypeError("Q, K, V and the weights must share one element type")
     out_dtype = torch.float32 if out_dtype is None else out_dtype
+    work_dtype = default_work_dtype(Q.dtype) if work_dtype is None else work_dtype
     dims = MhaDims(B=B, h=h, n_q=n_q, n_k=n_k, d_q=d_q, d_k=d_k, d_v=d_v, d_h=d_h, d_vh=d_vh,
                    d_o=d_o, scale=(1.0 / math.sqrt(d_h)) if scale is None else float(scale),
-                   in_dtype=in_code, out_dtype=_dtype_code(out_dtype))
+                   in_dtype=in_code, out_dtype=_dtype_code(out_dtype),
+                   work_dtype=_dtype_code(work_dtype))
     m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Q.device)
     if Y is None:
         Y = torch.empty((B, n_q, d_o), dtype=out_dtype, device=Q.device)
@@ -185,7 +197,8 @@ def attn_core(Qh, Kh, Vh, *, scale=None, causal=False, key_len=None, allowed=Non
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     dims = MhaDims(B=B, h=h, n_q=n_q, n_k=n_k, d_q=1, d_k=1, d_v=1, d_h=d_h, d_vh=d_vh, d_o=1,
                    scale=(1.0 / math.sqrt(d_h)) if scale is None else float(scale),
-                   in_dtype=_dtype_code(Qh.dtype), out_dtype=_dtype_code(out_dtype))
+                   in_dtype=_dtype_code(Qh.dtype), out_dtype=_dtype_code(out_dtype),
+                   work_dtype=_dtype_code(Qh.dtype))
     m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Qh.device)
     if Z is None:
         Z = torch.empty((B, n_q, h * d_vh), dtype=out_dtype, device=Qh.device)

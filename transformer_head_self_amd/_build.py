@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libmha.so")
 
-SOURCES = ["api.hip", "gemm.hip", "attn_bf16.hip", "attn_f32.hip"]
+SOURCES = ["api.hip", "gemm.hip", "attn_bf16.hip", "attn_f16.hip", "attn_f32.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -27,6 +27,9 @@ FLAGS = [
     "-Wno-unused-function",
     # no packed fp32 arithmetic in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs (no accumulator-register copies
+    # around the softmax arithmetic)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

@@ -15,10 +15,16 @@
 
 namespace mha {
 hipError_t launch_attention_bf16(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attention_f16(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream);
 
-hipError_t launch_attention(const AttnParams& p, int in_dtype, hipStream_t stream) {
-  return in_dtype == kBF16 ? launch_attention_bf16(p, stream) : launch_attention_f32(p, stream);
+hipError_t launch_attention(const AttnParams& p, int elem_dtype, hipStream_t stream) {
+  switch (elem_dtype) {
+    case kBF16: return launch_attention_bf16(p, stream);
+    case kF16: return launch_attention_f16(p, stream);
+    case kF32: return launch_attention_f32(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 }  // namespace mha
 
@@ -26,9 +32,13 @@ namespace {
 
 constexpr int64_t kIntMax = 2147483647LL;
 
-size_t esize(int dtype) { return dtype == MHA_BF16 ? 2 : 4; }
-int vec_elems(int dtype) { return dtype == MHA_BF16 ? 8 : 4; }
-bool valid_dtype(int dt) { return dt == MHA_F32 || dt == MHA_BF16; }
+size_t esize(int dtype) { return dtype == MHA_F32 ? 4 : 2; }
+int vec_elems(int dtype) { return dtype == MHA_F32 ? 4 : 8; }
+bool valid_dtype(int dt) { return dt == MHA_F32 || dt == MHA_BF16 || dt == MHA_F16; }
+bool valid_work_pair(int in, int work) {
+  return (in == MHA_F32 && work == MHA_F32) || (in == MHA_BF16 && work == MHA_F16) ||
+         (in == MHA_BF16 && work == MHA_BF16) || (in == MHA_F16 && work == MHA_F16);
+}
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -51,6 +61,7 @@ mha_status check_core_dims(const mha_dims* d) {
 mha_status check_full_dims(const mha_dims* d) {
   mha_status s = check_core_dims(d);
   if (s != MHA_OK) return s;
+  if (!valid_work_pair(d->in_dtype, d->work_dtype)) return MHA_ERR_DTYPE;
   if (d->d_q <= 0 || d->d_k <= 0 || d->d_v <= 0 || d->d_o <= 0) return MHA_ERR_DIM;
   return MHA_OK;
 }
@@ -89,7 +100,7 @@ struct Workspace {
 };
 
 Workspace carve(const mha_dims* d) {
-  const size_t es = esize(d->in_dtype);
+  const size_t es = esize(d->work_dtype);
   const size_t B = d->B, h = d->h;
   Workspace w;
   w.q = 0;
@@ -100,9 +111,10 @@ Workspace carve(const mha_dims* d) {
   return w;
 }
 
-void attn_params(mha::AttnParams& p, const mha_dims* d, const void* Qh, const void* Kh,
-                 const void* Vh, void* Z, int z_dtype, float* row_m, float* row_l) {
-  const int vin = vec_elems(d->in_dtype);
+void attn_params(mha::AttnParams& p, const mha_dims* d, int elem_dtype, const void* Qh,
+                 const void* Kh, const void* Vh, void* Z, int z_dtype, float* row_m,
+                 float* row_l) {
+  const int vin = vec_elems(elem_dtype);
   p.Q = Qh;
   p.K = Kh;
   p.V = Vh;
@@ -124,7 +136,7 @@ void attn_params(mha::AttnParams& p, const mha_dims* d, const void* Qh, const vo
   p.vec_q = aligned(Qh, 16) && (p.ldq % vin == 0);
   p.vec_k = aligned(Kh, 16) && (p.ldk % vin == 0);
   p.vec_v = aligned(Vh, 16) && (p.ldv % vin == 0);
-  p.vec_z = aligned(Z, z_dtype == MHA_BF16 ? 8 : 16) && (p.ldz % 4 == 0) && (d->d_vh % 4 == 0);
+  p.vec_z = aligned(Z, z_dtype == MHA_F32 ? 16 : 8) && (p.ldz % 4 == 0) && (d->d_vh % 4 == 0);
   p.num_q_tiles = 0;
 }
 
@@ -167,7 +179,7 @@ mha_status attn_core(const mha_dims* d, const mha_mask* m, const void* Qh, const
     return MHA_ERR_ALIGN;
   mha::AttnParams p;
   memset(&p, 0, sizeof(p));
-  attn_params(p, d, Qh, Kh, Vh, Z, d->out_dtype, row_m, row_l);
+  attn_params(p, d, d->in_dtype, Qh, Kh, Vh, Z, d->out_dtype, row_m, row_l);
   fill_mask(p, m);
   if (mha::launch_attention(p, d->in_dtype, (hipStream_t)stream) != hipSuccess)
     return MHA_ERR_LAUNCH;
@@ -197,6 +209,7 @@ mha_status mha_forward(const mha_dims* d, const mha_mask* m, const void* Q, cons
   void* Vh = ws + w.v;
   void* Z = ws + w.z;
   const int vin = vec_elems(d->in_dtype);
+  const int vwork = vec_elems(d->work_dtype);
   hipStream_t st = (hipStream_t)stream;
 
   // K1: the three head projections in one launch, stored head-major.
@@ -219,7 +232,7 @@ mha_status mha_forward(const mha_dims* d, const mha_mask* m, const void* Q, cons
     p.N = d->h * dhs[i];
     p.K = Ks[i];
     p.epilogue = mha::kHeads;
-    p.out_dtype = d->in_dtype;
+    p.out_dtype = d->work_dtype;
     p.heads = d->h;
     p.dh = dhs[i];
     p.ntok = ntoks[i];
@@ -227,14 +240,14 @@ mha_status mha_forward(const mha_dims* d, const mha_mask* m, const void* Q, cons
     p.vec_w = aligned(p.W, 16) && (p.N % vin == 0);
     p.vec_c = 1;
   }
-  if (mha::launch_gemm(gb, d->in_dtype, st) != hipSuccess) return MHA_ERR_LAUNCH;
+  if (mha::launch_gemm(gb, d->in_dtype, d->in_dtype, st) != hipSuccess) return MHA_ERR_LAUNCH;
 
-  // K2: fused attention, written into the concatenation Z (in_dtype).
+  // K2: fused attention, written into the concatenation Z (work_dtype).
   mha::AttnParams ap;
   memset(&ap, 0, sizeof(ap));
-  attn_params(ap, d, Qh, Kh, Vh, Z, d->in_dtype, row_m, row_l);
+  attn_params(ap, d, d->work_dtype, Qh, Kh, Vh, Z, d->work_dtype, row_m, row_l);
   fill_mask(ap, m);
-  if (mha::launch_attention(ap, d->in_dtype, st) != hipSuccess) return MHA_ERR_LAUNCH;
+  if (mha::launch_attention(ap, d->work_dtype, st) != hipSuccess) return MHA_ERR_LAUNCH;
 
   // K3: Y = Z W^O, row-major.
   mha::GemmBatch ob;
@@ -249,10 +262,10 @@ mha_status mha_forward(const mha_dims* d, const mha_mask* m, const void* Q, cons
   o.K = d->h * d->d_vh;
   o.epilogue = mha::kRowMajor;
   o.out_dtype = d->out_dtype;
-  o.vec_a = (o.K % vin == 0);
+  o.vec_a = (o.K % vwork == 0);
   o.vec_w = aligned(W_O, 16) && (o.N % vin == 0);
   o.vec_c = aligned(Y, 16);
-  if (mha::launch_gemm(ob, d->in_dtype, st) != hipSuccess) return MHA_ERR_LAUNCH;
+  if (mha::launch_gemm(ob, d->work_dtype, d->in_dtype, st) != hipSuccess) return MHA_ERR_LAUNCH;
   return MHA_OK;
 }
 

@@ -13,18 +13,22 @@
 //
 // Mapping onto the matrix cores (our design, not the pages'):
 // * each wave owns 32 query rows; a workgroup of WAVES waves shares K/V
-//   blocks of BN = 64 keys staged through LDS;
+//   blocks of BN = 64 keys staged through two LDS buffers (the next block is
+//   written while the current one is read; one barrier per block);
 // * the score block is computed transposed, S^T = K Q^T, with a 32x32 MFMA:
 //   lane l then holds 16 scores of query (l % 32) per 32-key sub-block, so a
-//   row's maximum and sum need one exchange with the other half-wave only;
+//   row's maximum needs one exchange with the other half-wave only;
 // * the value product is computed as O^T = V^T P^T: the transposed score
 //   fragment is already in the B-operand layout of the next MFMA, and V is
 //   staged transposed (d-major) in LDS so that each lane reads its keys
 //   contiguously;
 // * O^T leaves every lane with one query's output features, so the final
 //   division by l and the concatenated store need no cross-lane traffic.
-// Base-2 exponentials: scores are multiplied by c*log2(e), so
-// 2^(x - m2) = e^(s - m) and l, z are the page's quantities exactly.
+// Base-2 exponentials: scores are carried in units of log2(e) (see the
+// query set-up below), so 2^(x - m2) = e^(s - m) and l and z are the page's
+// quantities.  Weights feed the value product rounded to T; the
+// normaliser sums the same rounded weights (fp32 accumulation), so z / l is
+// an exact convex combination of the values the product used.
 #pragma once
 
 #include "common.hpp"
@@ -41,29 +45,62 @@ struct AttnCfg {
   static constexpr int KCH = DH / (2 * VEC);    // k-chunks of the score MFMA
   static constexpr int NDV = DV / 32;           // 32-row blocks of V^T
   static constexpr int KPAD = DH + VEC;         // LDS row stride of K (elements)
-  static constexpr int VPAD = BN + (sizeof(T) == 2 ? 4 : 4);  // LDS row stride of V^T
+  static constexpr int VPAD = BN + 4;           // LDS row stride of V^T (elements)
+  static constexpr int KBUF = BN * KPAD;        // elements per K buffer
+  static constexpr int VBUF = DV * VPAD;        // elements per V^T buffer
   static constexpr int K_CHUNKS = BN * DH / VEC;
   static constexpr int V_CHUNKS = BN * DV / VEC;
   static constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
   static constexpr int V_PER_T = (V_CHUNKS + NT - 1) / NT;
-  static constexpr int LDS_BYTES = (BN * KPAD + DV * VPAD) * (int)sizeof(T);
   static_assert(DH % (2 * VEC) == 0, "DH must be a multiple of a k-chunk");
   static_assert(DV % 32 == 0, "DV must be a multiple of 32");
 };
 
-template <typename T, int DH, int DV, int WAVES>
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::vec negate_chunk(typename Elem<T>::vec v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 u = __builtin_bit_cast(u32x4, v);
+  u ^= (sizeof(T) == 4) ? 0x80000000u : 0x80008000u;
+  return __builtin_bit_cast(typename Elem<T>::vec, u);
+}
+
+// Sum of eight rounded weights (fp32 accumulation) for the 2-byte types.
+__device__ __forceinline__ float sum8(const bf16x8& p, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  #pragma unroll
+  for (int t = 0; t < 8; t += 2) {
+    const bf16x2 pr = {p[t], p[t + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+  }
+  return acc;
+}
+__device__ __forceinline__ float sum8(const f16x8& p, float acc) {
+  const f16x2 one = {(f16)1.0f, (f16)1.0f};
+  #pragma unroll
+  for (int t = 0; t < 8; t += 2) {
+    const f16x2 pr = {p[t], p[t + 1]};
+    acc = __builtin_amdgcn_fdot2(pr, one, acc, false);
+  }
+  return acc;
+}
+
+// FAST: every row of Q, K, V is exactly DH / DV wide with 16-byte aligned
+// rows, and there is no boolean mask; the host selects it when that holds.
+// The general variant predicates every column and reads the boolean mask.
+template <typename T, int DH, int DV, int WAVES, bool FAST>
 __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
   typedef AttnCfg<T, DH, DV, WAVES> C;
   typedef typename Elem<T>::vec vec;
+  typedef typename Elem<T>::vec4 vec4;
   constexpr int VEC = C::VEC;
   constexpr int BN = C::BN;
 
-  __shared__ __attribute__((aligned(16))) T Ks[BN * C::KPAD];
-  __shared__ __attribute__((aligned(16))) T Vt[DV * C::VPAD];
+  __shared__ __attribute__((aligned(16))) T Ks[2 * C::KBUF];
+  __shared__ __attribute__((aligned(16))) T Vt[2 * C::VBUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int g = lane >> 5;      // lane half
   const int l32 = lane & 31;
 
@@ -92,22 +129,46 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
   const T* Qb = reinterpret_cast<const T*>(p.Q) + (size_t)bh * p.n_q * p.ldq;
   const T* Kb = reinterpret_cast<const T*>(p.K) + (size_t)bh * p.n_k * p.ldk;
   const T* Vb = reinterpret_cast<const T*>(p.V) + (size_t)bh * p.n_k * p.ldv;
-  const uint8_t* Gb = p.allowed ? p.allowed + (size_t)b * p.allowed_batch_stride : nullptr;
-  const bool vq = p.vec_q, vk = p.vec_k, vv = p.vec_v;
+  const uint8_t* Gb =
+      (!FAST && p.allowed) ? p.allowed + (size_t)b * p.allowed_batch_stride : nullptr;
+  const bool vq = FAST || p.vec_q, vk = FAST || p.vec_k, vv = FAST || p.vec_v;
+  const int dh = FAST ? DH : p.d_h;
+  const int dvh = FAST ? DV : p.d_vh;
+  // fp32 elements: the query is multiplied by c log2(e) once, in registers,
+  // so scores arrive in base-2 units and a weight is 2^(s - m), exactly 1 at
+  // the row maximum.  2-byte elements keep the query as given (no second
+  // rounding); the scale enters as c' = |c| log2(e) in one fused
+  // multiply-add per score, and the sign of c is moved into the query.
+  constexpr bool PRESCALE = sizeof(T) == 4;
+  const float cs = PRESCALE ? 1.0f : fabsf(p.scale_log2);
 
-  // This lane's query row as the B operand of S^T = K Q^T (registers, whole kernel).
+  // This lane's query row as the B operand of S^T = K Q^T (registers, whole
+  // kernel).
   vec qf[C::KCH];
   #pragma unroll
-  for (int c = 0; c < C::KCH; ++c)
-    qf[c] = (qi < p.n_q) ? load_chunk<T>(Qb + (size_t)qi * p.ldq, c * 2 * VEC + g * VEC, p.d_h, vq)
-                         : zero_vec<vec>();
+  for (int c = 0; c < C::KCH; ++c) {
+    if constexpr (FAST) {
+      // rows past n_q read the last row (their results are never stored)
+      const int qc = min(qi, p.n_q - 1);
+      qf[c] = *reinterpret_cast<const vec*>(Qb + (size_t)qc * DH + c * 2 * VEC + g * VEC);
+    } else {
+      qf[c] = (qi < p.n_q) ? load_chunk<T>(Qb + (size_t)qi * p.ldq, c * 2 * VEC + g * VEC, dh, vq)
+                           : zero_vec<vec>();
+    }
+    if constexpr (PRESCALE) {
+      #pragma unroll
+      for (int e = 0; e < VEC; ++e) qf[c][e] = (float)qf[c][e] * p.scale_log2;
+    } else {
+      if (p.scale_log2 < 0.f) qf[c] = negate_chunk<T>(qf[c]);
+    }
+  }
 
   floatx16 o[C::NDV];
   #pragma unroll
   for (int d = 0; d < C::NDV; ++d)
     #pragma unroll
     for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
-  float m_run = -INFINITY;  // running maximum (base-2 units)
+  float m_run = -INFINITY;  // running maximum of c' s (base-2 units)
   float l_run = 0.f;        // this half-wave's part of the running normaliser
 
   vec kreg[C::K_PER_T];
@@ -121,9 +182,16 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
       const int row = ci / (DH / VEC);
       const int cc = ci - row * (DH / VEC);
       const int key = k0 + row;
-      kreg[t] = (ci < C::K_CHUNKS && key < p.n_k)
-                    ? load_chunk<T>(Kb + (size_t)key * p.ldk, cc * VEC, p.d_h, vk)
-                    : zero_vec<vec>();
+      if constexpr (FAST) {
+        // keys past n_k read the last key; they are masked out (weight 0)
+        const int kc = min(key, p.n_k - 1);
+        if (ci < C::K_CHUNKS)
+          kreg[t] = *reinterpret_cast<const vec*>(Kb + (size_t)kc * DH + cc * VEC);
+      } else {
+        kreg[t] = (ci < C::K_CHUNKS && key < p.n_k)
+                      ? load_chunk<T>(Kb + (size_t)key * p.ldk, cc * VEC, dh, vk)
+                      : zero_vec<vec>();
+      }
     }
     #pragma unroll
     for (int t = 0; t < C::V_PER_T; ++t) {
@@ -131,19 +199,27 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
       const int cc = ci / BN;          // consecutive threads take consecutive keys,
       const int row = ci - cc * BN;    // so the transposed LDS stores are contiguous
       const int key = k0 + row;
-      vreg[t] = (ci < C::V_CHUNKS && key < p.n_k)
-                    ? load_chunk<T>(Vb + (size_t)key * p.ldv, cc * VEC, p.d_vh, vv)
-                    : zero_vec<vec>();
+      if constexpr (FAST) {
+        const int kc = min(key, p.n_k - 1);
+        if (ci < C::V_CHUNKS)
+          vreg[t] = *reinterpret_cast<const vec*>(Vb + (size_t)kc * DV + cc * VEC);
+      } else {
+        vreg[t] = (ci < C::V_CHUNKS && key < p.n_k)
+                      ? load_chunk<T>(Vb + (size_t)key * p.ldv, cc * VEC, dvh, vv)
+                      : zero_vec<vec>();
+      }
     }
   };
-  auto store_kv = [&]() {
+  auto store_kv = [&](int buf) {
+    T* ks = Ks + buf * C::KBUF;
+    T* vt = Vt + buf * C::VBUF;
     #pragma unroll
     for (int t = 0; t < C::K_PER_T; ++t) {
       const int ci = tid + t * C::NT;
       if (ci < C::K_CHUNKS) {
         const int row = ci / (DH / VEC);
         const int cc = ci - row * (DH / VEC);
-        *reinterpret_cast<vec*>(&Ks[row * C::KPAD + cc * VEC]) = kreg[t];
+        *reinterpret_cast<vec*>(&ks[row * C::KPAD + cc * VEC]) = kreg[t];
       }
     }
     #pragma unroll
@@ -153,120 +229,139 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
         const int cc = ci / BN;
         const int row = ci - cc * BN;
         #pragma unroll
-        for (int e = 0; e < VEC; ++e) Vt[(cc * VEC + e) * C::VPAD + row] = vreg[t][e];
+        for (int e = 0; e < VEC; ++e) vt[(cc * VEC + e) * C::VPAD + row] = vreg[t][e];
       }
     }
   };
 
-  if (nblk > 0) load_kv(0);
+  if (nblk > 0) {
+    load_kv(0);
+    store_kv(0);
+  }
+  __syncthreads();
+  if (nblk > 1) load_kv(1);
 
   for (int blk = 0; blk < nblk; ++blk) {
-    __syncthreads();  // every wave is done reading the previous block
-    store_kv();
-    __syncthreads();
-    if (blk + 1 < nblk) load_kv(blk + 1);  // in flight while this block computes
-
+    const int cur = blk & 1;
+    const T* ks = Ks + cur * C::KBUF;
+    const T* vt = Vt + cur * C::VBUF;
     const int k0 = blk * BN;
     // A wave whose rows all precede this block's first key (causal) sees an
     // empty key set here: its summary is the empty state, a no-op merge.
     const bool active = (qw < p.n_q) && !(p.causal && k0 > qw + 31);
-    if (!active) continue;
-
-    // ---- scores S^T (two 32-key sub-blocks) --------------------------------
-    floatx16 s[2];
-    #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    if (active) {
+      // ---- raw products S^T (two 32-key sub-blocks) ------------------------
+      floatx16 s[2];
       #pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-      #pragma unroll
-      for (int c = 0; c < C::KCH; ++c) {
-        const vec kf = *reinterpret_cast<const vec*>(
-            &Ks[(kb * 32 + l32) * C::KPAD + c * 2 * VEC + g * VEC]);
-        mfma_chunk(s[kb], kf, qf[c]);
-      }
-    }
-
-    // ---- scale, mask, block maximum -----------------------------------------
-    const bool need_mask = (k0 + BN > kvalid) || (p.causal && k0 + BN - 1 > qw) || Gb != nullptr;
-    float mx = -INFINITY;
-    #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[kb][i] * p.scale_log2;
-        if (need_mask) {
-          const int j = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          bool ok = j < kvalid;
-          if (p.causal) ok = ok && (j <= qi);
-          if (Gb != nullptr && ok) ok = qi < p.n_q && Gb[(size_t)qi * p.n_k + j] != 0;
-          x = ok ? x : -INFINITY;
-        }
-        s[kb][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
-    mx = fmaxf(mx, wave_xor32(mx));
-
-    // ---- merge: new shift, rescale the running summary ----------------------
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    float lsum = 0.f;
-    #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pe = __builtin_amdgcn_exp2f(s[kb][i] - m_use);
-        s[kb][i] = pe;
-        lsum += pe;
-      }
-    l_run = l_run * alpha + lsum;
-    #pragma unroll
-    for (int d = 0; d < C::NDV; ++d)
-      #pragma unroll
-      for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
-
-    // ---- z += P V  (as O^T += V^T P^T) -------------------------------------
-    #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if constexpr (sizeof(T) == 2) {
+      for (int kb = 0; kb < 2; ++kb) {
         #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          bf16x8 pb;
-          #pragma unroll
-          for (int t = 0; t < 8; t += 2) {
-            floatx2 f2 = {s[kb][8 * st + t], s[kb][8 * st + t + 1]};
-            bf16x2 b2 = __builtin_convertvector(f2, bf16x2);
-            pb[t] = b2.x;
-            pb[t + 1] = b2.y;
-          }
-          #pragma unroll
-          for (int d = 0; d < C::NDV; ++d) {
-            const T* vrow = &Vt[(d * 32 + l32) * C::VPAD + kb * 32 + 16 * st + 4 * g];
-            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 8);
-            const bf16x8 va = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            mfma_chunk(o[d], va, pb);
-          }
+        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+        #pragma unroll
+        for (int c = 0; c < C::KCH; ++c) {
+          const vec kf = *reinterpret_cast<const vec*>(
+              &ks[(kb * 32 + l32) * C::KPAD + c * 2 * VEC + g * VEC]);
+          mfma_chunk(s[kb], kf, qf[c]);
         }
+      }
+
+      // ---- mask and block maximum -----------------------------------------
+      const bool need_mask =
+          (k0 + BN > kvalid) || (p.causal && k0 + BN - 1 > qw) || (!FAST && Gb != nullptr);
+      uint32_t okbits = 0xffffffffu;   // bit 16*kb + i: key allowed for this row
+      float mx = -INFINITY;
+      if (need_mask) {
+        #pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+            bool ok = j < kvalid;
+            if (p.causal) ok = ok && (j <= qi);
+            if (!FAST && Gb != nullptr && ok)
+              ok = qi < p.n_q && Gb[(size_t)qi * p.n_k + j] != 0;
+            if (!ok) okbits &= ~(1u << (16 * kb + i));
+            mx = fmaxf(mx, ok ? s[kb][i] : -INFINITY);
+          }
       } else {
         #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const floatx4 pf = {s[kb][4 * a], s[kb][4 * a + 1], s[kb][4 * a + 2], s[kb][4 * a + 3]};
+        for (int kb = 0; kb < 2; ++kb)
           #pragma unroll
-          for (int d = 0; d < C::NDV; ++d) {
-            const floatx4 va = *reinterpret_cast<const floatx4*>(
-                &Vt[(d * 32 + l32) * C::VPAD + kb * 32 + 8 * a + 4 * g]);
-            mfma_chunk(o[d], va, pf);
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      }
+      mx = half_max(mx);
+
+      // ---- merge: new shift, rescale the running summary ------------------
+      const float mblk = (mx == -INFINITY) ? -INFINITY : mx * cs;
+      const float m_new = fmaxf(m_run, mblk);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_new;
+      if (__any(alpha != 1.0f)) {     // some row's maximum moved
+        l_run *= alpha;
+        #pragma unroll
+        for (int d = 0; d < C::NDV; ++d)
+          #pragma unroll
+          for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+      }
+      if (need_mask) {
+        #pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][i], cs, -m_use));
+            s[kb][i] = ((okbits >> (16 * kb + i)) & 1u) ? e : 0.f;
+          }
+      } else {
+        #pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          #pragma unroll
+          for (int i = 0; i < 16; ++i)
+            s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], cs, -m_use));
+      }
+
+      // ---- z += P V  (as O^T += V^T P^T), l += sum of the rounded weights --
+      #pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if constexpr (sizeof(T) == 2) {
+          #pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            floatx8 pf;
+            #pragma unroll
+            for (int t = 0; t < 8; ++t) pf[t] = s[kb][8 * st + t];
+            const vec pb = Cvt<T>::eight(pf);
+            l_run = sum8(pb, l_run);
+            #pragma unroll
+            for (int d = 0; d < C::NDV; ++d) {
+              const T* vrow = &vt[(d * 32 + l32) * C::VPAD + kb * 32 + 16 * st + 4 * g];
+              const vec4 lo = *reinterpret_cast<const vec4*>(vrow);
+              const vec4 hi = *reinterpret_cast<const vec4*>(vrow + 8);
+              const vec va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              mfma_chunk(o[d], va, pb);
+            }
+          }
+        } else {
+          #pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const floatx4 pf = {s[kb][4 * a], s[kb][4 * a + 1], s[kb][4 * a + 2],
+                                s[kb][4 * a + 3]};
+            l_run += (pf[0] + pf[1]) + (pf[2] + pf[3]);
+            #pragma unroll
+            for (int d = 0; d < C::NDV; ++d) {
+              const floatx4 va = *reinterpret_cast<const floatx4*>(
+                  &vt[(d * 32 + l32) * C::VPAD + kb * 32 + 8 * a + 4 * g]);
+              mfma_chunk(o[d], va, pf);
+            }
           }
         }
       }
     }
+    if (blk + 1 < nblk) store_kv(cur ^ 1);  // next block into the other buffer
+    __syncthreads();
+    if (blk + 2 < nblk) load_kv(blk + 2);   // in flight during the next block
   }
 
   // ---- finalise: z / l, store into the concatenation --------------------------
-  const float l_tot = l_run + wave_xor32(l_run);
+  const float l_tot = half_sum(l_run);
   const float inv = 1.0f / l_tot;
   if (qi < p.n_q) {
     const size_t zbase = ((size_t)b * p.n_q + qi) * p.ldz + (size_t)r * p.d_vh;
@@ -275,7 +370,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
       #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int e0 = d * 32 + 8 * a + 4 * g;
-        store4(p.Z, p.out_dtype, zbase + e0, p.vec_z, p.d_vh - e0, o[d][4 * a] * inv,
+        store4(p.Z, p.out_dtype, zbase + e0, p.vec_z, dvh - e0, o[d][4 * a] * inv,
                o[d][4 * a + 1] * inv, o[d][4 * a + 2] * inv, o[d][4 * a + 3] * inv);
       }
     }

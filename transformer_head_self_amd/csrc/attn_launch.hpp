@@ -12,8 +12,14 @@ hipError_t launch_attn_fixed(AttnParams p, hipStream_t stream) {
   p.num_q_tiles = (p.n_q + C::QT - 1) / C::QT;
   const long long grid = (long long)p.num_q_tiles * p.B * p.h;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES>), dim3((unsigned)grid), dim3(C::NT), 0,
-                     stream, p);
+  const bool fast = p.d_h == DH && p.d_vh == DV && p.vec_q && p.vec_k && p.vec_v &&
+                    p.allowed == nullptr;
+  if (fast)
+    hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, true>), dim3((unsigned)grid),
+                       dim3(C::NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, false>), dim3((unsigned)grid),
+                       dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 

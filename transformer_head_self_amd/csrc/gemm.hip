@@ -3,7 +3,9 @@
 
 namespace mha {
 
-hipError_t launch_gemm(const GemmBatch& in, int in_dtype, hipStream_t stream) {
+// compute_dtype: element type of A and of the MFMA operands; w_dtype: storage
+// type of W.  Supported pairs: (f32, f32), (bf16, bf16), (f16, f16), (f16, bf16).
+hipError_t launch_gemm(const GemmBatch& in, int compute_dtype, int w_dtype, hipStream_t stream) {
   GemmBatch b = in;
   const int BM = 128, BN = 128;  // GemmCfg<T>::BM/BN for both element types
   int total = 0;
@@ -16,10 +18,16 @@ hipError_t launch_gemm(const GemmBatch& in, int in_dtype, hipStream_t stream) {
   }
   b.total_tiles = total;
   if (total == 0) return hipSuccess;
-  if (in_dtype == kBF16)
-    hipLaunchKernelGGL(gemm_kernel<bf16>, dim3(total), dim3(256), 0, stream, b);
+  if (compute_dtype == kBF16 && w_dtype == kBF16)
+    hipLaunchKernelGGL((gemm_kernel<bf16, bf16>), dim3(total), dim3(256), 0, stream, b);
+  else if (compute_dtype == kF16 && w_dtype == kF16)
+    hipLaunchKernelGGL((gemm_kernel<f16, f16>), dim3(total), dim3(256), 0, stream, b);
+  else if (compute_dtype == kF16 && w_dtype == kBF16)
+    hipLaunchKernelGGL((gemm_kernel<f16, bf16>), dim3(total), dim3(256), 0, stream, b);
+  else if (compute_dtype == kF32 && w_dtype == kF32)
+    hipLaunchKernelGGL((gemm_kernel<float, float>), dim3(total), dim3(256), 0, stream, b);
   else
-    hipLaunchKernelGGL(gemm_kernel<float>, dim3(total), dim3(256), 0, stream, b);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

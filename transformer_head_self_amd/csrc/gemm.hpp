@@ -46,10 +46,15 @@ __device__ __forceinline__ int xcd_contiguous_tile(int id, int total) {
   return (x < rem) ? x * (full + 1) + j : rem * (full + 1) + (x - rem) * full + j;
 }
 
-template <typename T>
+// T: element type of A, of the LDS tiles and of the MFMA operands.
+// TW: storage type of W (same size as T); a 2-byte W of the other kind is
+// re-rounded to T (nearest even) as it is staged into LDS.
+template <typename T, typename TW>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmBatch batch) {
+  static_assert(sizeof(T) == sizeof(TW), "W must have the element size of T");
   typedef GemmCfg<T> C;
   typedef typename Elem<T>::vec vec;
+  typedef typename Elem<TW>::vec wvec;
   constexpr int VEC = C::VEC;
 
   __shared__ __attribute__((aligned(16))) T Xs[C::BM * C::XPAD];
@@ -57,7 +62,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmBatch batch) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int g = lane >> 5;
   const int l32 = lane & 31;
   const int wm = wave >> 1, wn = wave & 1;
@@ -75,7 +80,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmBatch batch) {
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   const int M = P.M, N = P.N, K = P.K;
   const T* A = reinterpret_cast<const T*>(P.A);
-  const T* W = reinterpret_cast<const T*>(P.W);
+  const TW* W = reinterpret_cast<const TW*>(P.W);
   const bool va = P.vec_a, vw = P.vec_w;
 
   floatx16 acc[2][2];
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmBatch batch) {
       for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
 
   vec xreg[C::X_PER_T];
-  vec wreg[C::W_PER_T];
+  wvec wreg[C::W_PER_T];
 
   auto load_stage = [&](int k0) {
     #pragma unroll
@@ -105,8 +110,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmBatch batch) {
       const int nc = ci / C::BK;         // consecutive threads: consecutive k rows
       const int kr = ci - nc * C::BK;
       const int k = k0 + kr;
-      wreg[t] = (k < K) ? load_chunk<T>(W + (size_t)k * N + n0, nc * VEC, N - n0, vw)
-                        : zero_vec<vec>();
+      wreg[t] = (k < K) ? load_chunk<TW>(W + (size_t)k * N + n0, nc * VEC, N - n0, vw)
+                        : zero_vec<wvec>();
     }
   };
   auto store_stage = [&]() {
@@ -122,8 +127,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmBatch batch) {
       const int ci = tid + t * C::NT;
       const int nc = ci / C::BK;
       const int kr = ci - nc * C::BK;
+      const vec wv = convert_chunk<T, TW>(wreg[t]);
       #pragma unroll
-      for (int e = 0; e < VEC; ++e) Wt[(nc * VEC + e) * C::WPAD + kr] = wreg[t][e];
+      for (int e = 0; e < VEC; ++e) Wt[(nc * VEC + e) * C::WPAD + kr] = wv[e];
     }
   };
 

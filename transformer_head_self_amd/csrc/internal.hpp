@@ -4,9 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace mha {
 
-enum DType : int { kF32 = 0, kBF16 = 1 };
 
 // ---------------------------------------------------------------------------
 // Projection GEMM: C = A[M,K] * W[K,N], both row-major, fp32 accumulation.
@@ -38,7 +39,7 @@ struct GemmBatch {
   int total_tiles;
 };
 
-hipError_t launch_gemm(const GemmBatch& batch, int in_dtype, hipStream_t stream);
+hipError_t launch_gemm(const GemmBatch& batch, int compute_dtype, int w_dtype, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Fused attention: Z[b, i, r*d_vh + e] = sum_j softmax_j(c * q_i . k_j | mask) v_j[e]
@@ -63,7 +64,9 @@ struct AttnParams {
   int num_q_tiles;   // filled by the launcher
 };
 
-hipError_t launch_attention(const AttnParams& p, int in_dtype, hipStream_t stream);
+// elem_dtype: element type of Q, K, V (and of the softmax weights fed to
+// the value product).
+hipError_t launch_attention(const AttnParams& p, int elem_dtype, hipStream_t stream);
 
 // Largest head widths with an instantiated kernel.
 constexpr int kMaxHeadDim = 128;

@@ -30,6 +30,19 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MHA fwd TFLOP/s and % bf16 MFMA peak (T=4096, h=16, d_k=64, causal)"
+# sources that define the attention kernel; a traffic measurement is only
+# reported while their hash matches the one recorded with it
+ATTN_SOURCES = ["transformer_head_self_amd/csrc/attn.hpp", "transformer_head_self_amd/csrc/common.hpp",
+                "transformer_head_self_amd/csrc/attn_launch.hpp", "transformer_head_self_amd/csrc/internal.hpp"]
+
+
+def attn_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense matrix-core peaks
 HBM_PEAK_GBS = 8000.0
 
@@ -41,6 +54,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "forward", "core"], default="all",
+                    help="profiling aid: time only the whole forward or only the attention core")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="profiling aid: run a plain device-to-device copy of this many bytes "
+                         "(three times) and exit; calibrates the HBM byte counters")
+    ap.add_argument("--print-source-hash", action="store_true",
+                    help="print the hash of the attention kernel sources and exit")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters (optional)")
     return ap.parse_args()
@@ -96,6 +116,19 @@ def main():
     import numpy as np
     import torch
 
+    if args.print_source_hash:
+        print(attn_source_hash())
+        return
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "launches": 3}), flush=True)
+        return
+
     import transformer_head_self_amd as mha
     from transformer_head_self_amd.inputs import HEADLINE, WORKLOADS, make_inputs
 
@@ -126,17 +159,22 @@ def main():
                         stream=stream)
 
     # ---- whole forward --------------------------------------------------------
-    for _ in range(args.warmup):
+    ms_step = float("nan")
+    steps_fwd = args.steps if args.only != "core" else 1
+    for _ in range(args.warmup if args.only != "core" else 1):
         step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps_fwd):
         step()
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = e0.elapsed_time(e1) / steps_fwd
+    if args.only == "forward":
+        print(json.dumps({"ms_per_step": ms_step}), flush=True)
+        return
 
     # ---- the dominant kernel alone: attention core on the projected heads ----
     # (the same launch configuration mha_forward uses: fp16 heads, fp16 Z)
@@ -169,7 +207,8 @@ def main():
         try:
             tj = json.load(open(args.traffic_json))
             entry = tj.get(w.name, {}).get("attn_core")
-            traffic = None if entry is None else entry.get("hbm_bytes_per_launch")
+            if entry is not None and entry.get("source_hash") == attn_source_hash():
+                traffic = entry.get("hbm_bytes_per_launch")
         except Exception:
             traffic = None
 

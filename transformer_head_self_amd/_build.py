@@ -27,11 +27,13 @@ FLAGS = [
     "-Wno-unused-function",
     # no packed fp32 arithmetic in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # matrix-core results in ordinary VGPRs (no accumulator-register copies
-    # around the softmax arithmetic)
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
+# Attention kernels: matrix-core results in ordinary VGPRs (no accumulator-
+# register copies around the softmax arithmetic).  The GEMMs keep their
+# accumulators wherever the compiler prefers (accumulation registers).
+PER_SOURCE_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+                    for src in ("attn_bf16.hip", "attn_f16.hip", "attn_f32.hip")}
 
 
 def _hipcc():
@@ -43,7 +45,8 @@ def _hipcc():
 
 def _compile(src):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *PER_SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")

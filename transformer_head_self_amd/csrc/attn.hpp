@@ -19,16 +19,17 @@
 //   lane l then holds 16 scores of query (l % 32) per 32-key sub-block, so a
 //   row's maximum needs one exchange with the other half-wave only;
 // * the value product is computed as O^T = V^T P^T: the transposed score
-//   fragment is already in the B-operand layout of the next MFMA, and V is
-//   staged transposed (d-major) in LDS so that each lane reads its keys
-//   contiguously;
+//   fragment is already in the B-operand layout of the next MFMA.  The
+//   A operand needs, per lane, one feature of V for several keys: 2-byte V
+//   tiles are stored row-major in LDS and read with the transposing LDS
+//   load (ds_read_b64_tr_b16); fp32 V tiles are stored transposed;
 // * O^T leaves every lane with one query's output features, so the final
 //   division by l and the concatenated store need no cross-lane traffic.
 // Base-2 exponentials: scores are carried in units of log2(e) (see the
 // query set-up below), so 2^(x - m2) = e^(s - m) and l and z are the page's
-// quantities.  Weights feed the value product rounded to T; the
-// normaliser sums the same rounded weights (fp32 accumulation), so z / l is
-// an exact convex combination of the values the product used.
+// quantities.  Weights feed the value product rounded to T; the normaliser
+// sums the same rounded weights (fp32 accumulation), so z / l is an exact
+// convex combination of the values the product used.
 #pragma once
 
 #include "common.hpp"
@@ -39,6 +40,7 @@ namespace mha {
 template <typename T, int DH, int DV, int WAVES, int BN_ = 64>
 struct AttnCfg {
   static constexpr int VEC = Elem<T>::VEC;
+  static constexpr bool TR = sizeof(T) == 2;   // V row-major + transposing reads
   static constexpr int BN = BN_;                // keys per block
   static constexpr int NKB = BN / 32;           // 32-key sub-blocks per block
   static constexpr int NT = 64 * WAVES;         // threads per workgroup
@@ -46,9 +48,11 @@ struct AttnCfg {
   static constexpr int KCH = DH / (2 * VEC);    // k-chunks of the score MFMA
   static constexpr int NDV = DV / 32;           // 32-row blocks of V^T
   static constexpr int KPAD = DH + VEC;         // LDS row stride of K (elements)
-  static constexpr int VPAD = BN + 4;           // LDS row stride of V^T (elements)
+  // V: row-major rows of DV (+ pad so the rows one transposing read touches
+  // fall in different banks), or transposed rows of BN keys for fp32.
+  static constexpr int VROW = TR ? DV + ((DV % 64 == 0) ? 32 : 0) : BN + 4;
   static constexpr int KBUF = BN * KPAD;        // elements per K buffer
-  static constexpr int VBUF = DV * VPAD;        // elements per V^T buffer
+  static constexpr int VBUF = TR ? BN * VROW : DV * VROW;
   static constexpr int K_CHUNKS = BN * DH / VEC;
   static constexpr int V_CHUNKS = BN * DV / VEC;
   static constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
@@ -86,11 +90,35 @@ __device__ __forceinline__ float sum8(const f16x8& p, float acc) {
   return acc;
 }
 
+// Transposing LDS read of four 16-bit values (gfx950).  Within each group of
+// 16 lanes, output lane i receives, in slot e, the value at position i % 4 of
+// the four-element run addressed by lane 4e + i/4 of the same group.
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::vec4 lds_read_tr4(const T* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s4*)(const_cast<T*>(p)));
+  return __builtin_bit_cast(typename Elem<T>::vec4, v);
+}
+
 // FAST: every row of Q, K, V is exactly DH / DV wide with 16-byte aligned
 // rows, and there is no boolean mask; the host selects it when that holds.
 // The general variant predicates every column and reads the boolean mask.
-template <typename T, int DH, int DV, int WAVES, int BN_, bool FAST>
-__global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
+//
+// LAZY (deferred shift): the running state of a row is kept as (m, l*, z*)
+// with l* = l e^(m - mu), z* = z e^(m - mu) for a reference shift mu <= m
+// that is moved up to m only when a block's maximum exceeds mu by more than
+// kLazyTau (base-2 units), so weights stay below 2^kLazyTau.  Between moves
+// the page's merge of a block at the common shift mu is l* += sum e^(s-mu),
+// z* += sum e^(s-mu) v; when mu moves, both sides are rescaled by the
+// page's factor.  m itself is tracked exactly, and at the end l = l* e^(mu-m)
+// is returned; z*/l* = z/l.  With mu fixed between moves, -mu is fed to the
+// score MFMA as its accumulator input, so a weight costs one exponential.
+constexpr float kLazyTau = 8.0f;
+
+// OCC: minimum waves per SIMD the register allocation must allow.
+template <typename T, int DH, int DV, int WAVES, int BN_, bool FAST, bool LAZY = false, int OCC = 1>
+__global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p) {
   typedef AttnCfg<T, DH, DV, WAVES, BN_> C;
   constexpr int NKB = C::NKB;
   typedef typename Elem<T>::vec vec;
@@ -99,7 +127,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
   constexpr int BN = C::BN;
 
   __shared__ __attribute__((aligned(16))) T Ks[2 * C::KBUF];
-  __shared__ __attribute__((aligned(16))) T Vt[2 * C::VBUF];
+  __shared__ __attribute__((aligned(16))) T Vs[2 * C::VBUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -137,12 +165,18 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
   const bool vq = FAST || p.vec_q, vk = FAST || p.vec_k, vv = FAST || p.vec_v;
   const int dh = FAST ? DH : p.d_h;
   const int dvh = FAST ? DV : p.d_vh;
+  const int ldk = FAST ? DH : p.ldk;
+  const int ldv = FAST ? DV : p.ldv;
+
   // fp32 elements: the query is multiplied by c log2(e) once, in registers,
   // so scores arrive in base-2 units and a weight is 2^(s - m), exactly 1 at
   // the row maximum.  2-byte elements keep the query as given (no second
   // rounding); the scale enters as c' = |c| log2(e) in one fused
   // multiply-add per score, and the sign of c is moved into the query.
-  constexpr bool PRESCALE = sizeof(T) == 4;
+  // The deferred-shift variant also scales 2-byte queries once (one extra
+  // rounding of q c log2(e) to T), so that the score MFMA alone forms
+  // c' s - mu.
+  constexpr bool PRESCALE = sizeof(T) == 4 || LAZY;
   const float cs = PRESCALE ? 1.0f : fabsf(p.scale_log2);
 
   // This lane's query row as the B operand of S^T = K Q^T (registers, whole
@@ -160,7 +194,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
     }
     if constexpr (PRESCALE) {
       #pragma unroll
-      for (int e = 0; e < VEC; ++e) qf[c][e] = (float)qf[c][e] * p.scale_log2;
+      for (int e = 0; e < VEC; ++e) qf[c][e] = (T)((float)qf[c][e] * p.scale_log2);
     } else {
       if (p.scale_log2 < 0.f) qf[c] = negate_chunk<T>(qf[c]);
     }
@@ -171,68 +205,84 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
   for (int d = 0; d < C::NDV; ++d)
     #pragma unroll
     for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
-  float m_run = -INFINITY;  // running maximum of c' s (base-2 units)
+  float m_run = -INFINITY;  // running maximum of the scores (base-2 units)
   float l_run = 0.f;        // this half-wave's part of the running normaliser
+  float mu = -INFINITY;     // LAZY: reference shift (l_run, o are kept at mu)
+  floatx16 negmu;           // LAZY: -mu in every slot, the score MFMA's C input
+  #pragma unroll
+  for (int i = 0; i < 16; ++i) negmu[i] = 0.f;
 
+  // ---- staging of K/V blocks: global -> registers -> LDS ----------------------
+  // Thread chunk t of a block covers tile row krow[t] / vrow[t] (a key) and
+  // columns kcol[t] / vcol[t]; consecutive threads take consecutive 16-byte
+  // chunks of one row (fp32 V: consecutive keys, for the transposed store).
+  int krow[C::K_PER_T], kcol[C::K_PER_T], vrow[C::V_PER_T], vcol[C::V_PER_T];
+  #pragma unroll
+  for (int t = 0; t < C::K_PER_T; ++t) {
+    const int ci = tid + t * C::NT;
+    krow[t] = ci / (DH / VEC);
+    kcol[t] = (ci - krow[t] * (DH / VEC)) * VEC;
+  }
+  #pragma unroll
+  for (int t = 0; t < C::V_PER_T; ++t) {
+    const int ci = tid + t * C::NT;
+    if constexpr (C::TR) {
+      vrow[t] = ci / (DV / VEC);
+      vcol[t] = (ci - vrow[t] * (DV / VEC)) * VEC;
+    } else {
+      const int cc = ci / BN;
+      vrow[t] = ci - cc * BN;
+      vcol[t] = cc * VEC;
+    }
+  }
   vec kreg[C::K_PER_T];
   vec vreg[C::V_PER_T];
 
   auto load_kv = [&](int blk) {
     const int k0 = blk * BN;
+    const bool tail = k0 + BN > p.n_k;   // uniform: only the last block can run past n_k
     #pragma unroll
     for (int t = 0; t < C::K_PER_T; ++t) {
-      const int ci = tid + t * C::NT;
-      const int row = ci / (DH / VEC);
-      const int cc = ci - row * (DH / VEC);
-      const int key = k0 + row;
+      if (C::K_CHUNKS % C::NT != 0 && tid + t * C::NT >= C::K_CHUNKS) continue;
+      int key = k0 + krow[t];
       if constexpr (FAST) {
         // keys past n_k read the last key; they are masked out (weight 0)
-        const int kc = min(key, p.n_k - 1);
-        if (ci < C::K_CHUNKS)
-          kreg[t] = *reinterpret_cast<const vec*>(Kb + (size_t)kc * DH + cc * VEC);
+        if (tail) key = min(key, p.n_k - 1);
+        kreg[t] = *reinterpret_cast<const vec*>(Kb + (size_t)key * DH + kcol[t]);
       } else {
-        kreg[t] = (ci < C::K_CHUNKS && key < p.n_k)
-                      ? load_chunk<T>(Kb + (size_t)key * p.ldk, cc * VEC, dh, vk)
-                      : zero_vec<vec>();
+        kreg[t] = (key < p.n_k) ? load_chunk<T>(Kb + (size_t)key * ldk, kcol[t], dh, vk)
+                                : zero_vec<vec>();
       }
     }
     #pragma unroll
     for (int t = 0; t < C::V_PER_T; ++t) {
-      const int ci = tid + t * C::NT;
-      const int cc = ci / BN;          // consecutive threads take consecutive keys,
-      const int row = ci - cc * BN;    // so the transposed LDS stores are contiguous
-      const int key = k0 + row;
+      if (C::V_CHUNKS % C::NT != 0 && tid + t * C::NT >= C::V_CHUNKS) continue;
+      int key = k0 + vrow[t];
       if constexpr (FAST) {
-        const int kc = min(key, p.n_k - 1);
-        if (ci < C::V_CHUNKS)
-          vreg[t] = *reinterpret_cast<const vec*>(Vb + (size_t)kc * DV + cc * VEC);
+        if (tail) key = min(key, p.n_k - 1);
+        vreg[t] = *reinterpret_cast<const vec*>(Vb + (size_t)key * DV + vcol[t]);
       } else {
-        vreg[t] = (ci < C::V_CHUNKS && key < p.n_k)
-                      ? load_chunk<T>(Vb + (size_t)key * p.ldv, cc * VEC, dvh, vv)
-                      : zero_vec<vec>();
+        vreg[t] = (key < p.n_k) ? load_chunk<T>(Vb + (size_t)key * ldv, vcol[t], dvh, vv)
+                                : zero_vec<vec>();
       }
     }
   };
   auto store_kv = [&](int buf) {
     T* ks = Ks + buf * C::KBUF;
-    T* vt = Vt + buf * C::VBUF;
+    T* vs = Vs + buf * C::VBUF;
     #pragma unroll
     for (int t = 0; t < C::K_PER_T; ++t) {
-      const int ci = tid + t * C::NT;
-      if (ci < C::K_CHUNKS) {
-        const int row = ci / (DH / VEC);
-        const int cc = ci - row * (DH / VEC);
-        *reinterpret_cast<vec*>(&ks[row * C::KPAD + cc * VEC]) = kreg[t];
-      }
+      if (C::K_CHUNKS % C::NT != 0 && tid + t * C::NT >= C::K_CHUNKS) continue;
+      *reinterpret_cast<vec*>(&ks[krow[t] * C::KPAD + kcol[t]]) = kreg[t];
     }
     #pragma unroll
     for (int t = 0; t < C::V_PER_T; ++t) {
-      const int ci = tid + t * C::NT;
-      if (ci < C::V_CHUNKS) {
-        const int cc = ci / BN;
-        const int row = ci - cc * BN;
+      if (C::V_CHUNKS % C::NT != 0 && tid + t * C::NT >= C::V_CHUNKS) continue;
+      if constexpr (C::TR) {
+        *reinterpret_cast<vec*>(&vs[vrow[t] * C::VROW + vcol[t]]) = vreg[t];
+      } else {
         #pragma unroll
-        for (int e = 0; e < VEC; ++e) vt[(cc * VEC + e) * C::VPAD + row] = vreg[t][e];
+        for (int e = 0; e < VEC; ++e) vs[(vcol[t] + e) * C::VROW + vrow[t]] = vreg[t][e];
       }
     }
   };
@@ -247,18 +297,26 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
   for (int blk = 0; blk < nblk; ++blk) {
     const int cur = blk & 1;
     const T* ks = Ks + cur * C::KBUF;
-    const T* vt = Vt + cur * C::VBUF;
+    const T* vs = Vs + cur * C::VBUF;
     const int k0 = blk * BN;
     // A wave whose rows all precede this block's first key (causal) sees an
     // empty key set here: its summary is the empty state, a no-op merge.
     const bool active = (qw < p.n_q) && !(p.causal && k0 > qw + 31);
     if (active) {
-      // ---- raw products S^T (two 32-key sub-blocks) ------------------------
+      // ---- raw products S^T (NKB sub-blocks of 32 keys) ----------------------
       floatx16 s[NKB];
+      // LAZY: from the second block on every row has a finite mu (the first
+      // block always holds key 0, which causal and padding masks allow), so
+      // the accumulator starts at -mu; the first block starts at 0.
+      const bool shifted = LAZY && blk > 0;
       #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+        if (shifted) {
+          s[kb] = negmu;
+        } else {
+          #pragma unroll
+          for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+        }
         #pragma unroll
         for (int c = 0; c < C::KCH; ++c) {
           const vec kf = *reinterpret_cast<const vec*>(
@@ -293,6 +351,55 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
       }
       mx = half_max(mx);
 
+      if constexpr (LAZY) {
+        if (shifted) {
+          // mx = (block maximum) - mu for every row (-inf: no allowed key)
+          m_run = fmaxf(m_run, mx + mu);
+          if (__any(mx > kLazyTau)) {       // some row ran too far above its shift
+            const float dmu = fmaxf(mx, 0.f);  // move mu to max(mu, block max)
+            const float a = __builtin_amdgcn_exp2f(-dmu);
+            l_run *= a;
+            #pragma unroll
+            for (int d = 0; d < C::NDV; ++d)
+              #pragma unroll
+              for (int i = 0; i < 16; ++i) o[d][i] *= a;
+            #pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+              #pragma unroll
+              for (int i = 0; i < 16; ++i) s[kb][i] -= dmu;
+            mu += dmu;
+            #pragma unroll
+            for (int i = 0; i < 16; ++i) negmu[i] = -mu;
+          }
+          if (need_mask) {
+            #pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+              #pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const float e = __builtin_amdgcn_exp2f(s[kb][i]);
+                s[kb][i] = ((okbits >> (16 * kb + i)) & 1ull) ? e : 0.f;
+              }
+          } else {
+            #pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+              #pragma unroll
+              for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(s[kb][i]);
+          }
+        } else {
+          // first block: the exact block maximum becomes both m and mu
+          m_run = mx;
+          mu = (mx == -INFINITY) ? 0.f : mx;
+          #pragma unroll
+          for (int i = 0; i < 16; ++i) negmu[i] = -mu;
+          #pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const float e = __builtin_amdgcn_exp2f(s[kb][i] - mu);
+              s[kb][i] = (!need_mask || ((okbits >> (16 * kb + i)) & 1ull)) ? e : 0.f;
+            }
+        }
+      } else {
       // ---- merge: new shift, rescale the running summary ------------------
       const float mblk = (mx == -INFINITY) ? -INFINITY : mx * cs;
       const float m_new = fmaxf(m_run, mblk);
@@ -321,11 +428,18 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
           for (int i = 0; i < 16; ++i)
             s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], cs, -m_use));
       }
+      }  // exact shift
 
       // ---- z += P V  (as O^T += V^T P^T), l += sum of the rounded weights --
       #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (C::TR) {
+          // A-operand slot t of lane half g holds key kb*32 + 16*st + 4*g + t
+          // (t < 4) or kb*32 + 16*st + 8 + 4*g + (t - 4) (t >= 4), the same
+          // keys as the B operand's score slots; this lane feeds the read
+          // with 4 features of key row srow, starting at column scol.
+          const int srow = kb * 32 + 4 * g + ((lane & 15) >> 2);
+          const int scol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
           #pragma unroll
           for (int st = 0; st < 2; ++st) {
             floatx8 pf;
@@ -335,9 +449,9 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
             l_run = sum8(pb, l_run);
             #pragma unroll
             for (int d = 0; d < C::NDV; ++d) {
-              const T* vrow = &vt[(d * 32 + l32) * C::VPAD + kb * 32 + 16 * st + 4 * g];
-              const vec4 lo = *reinterpret_cast<const vec4*>(vrow);
-              const vec4 hi = *reinterpret_cast<const vec4*>(vrow + 8);
+              const T* v0 = &vs[(srow + 16 * st) * C::VROW + d * 32 + scol];
+              const vec4 lo = lds_read_tr4<T>(v0);
+              const vec4 hi = lds_read_tr4<T>(v0 + 8 * C::VROW);
               const vec va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
               mfma_chunk(o[d], va, pb);
             }
@@ -351,7 +465,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
             #pragma unroll
             for (int d = 0; d < C::NDV; ++d) {
               const floatx4 va = *reinterpret_cast<const floatx4*>(
-                  &vt[(d * 32 + l32) * C::VPAD + kb * 32 + 8 * a + 4 * g]);
+                  &vs[(d * 32 + l32) * C::VROW + kb * 32 + 8 * a + 4 * g]);
               mfma_chunk(o[d], va, pf);
             }
           }
@@ -364,8 +478,12 @@ __global__ __launch_bounds__(64 * WAVES) void attn_fwd_kernel(AttnParams p) {
   }
 
   // ---- finalise: z / l, store into the concatenation --------------------------
-  const float l_tot = half_sum(l_run);
+  float l_tot = half_sum(l_run);
   const float inv = 1.0f / l_tot;
+  if constexpr (LAZY) {
+    // l at the exact maximum: l* e^(mu - m)   (z / l is unchanged)
+    if (m_run != -INFINITY) l_tot *= __builtin_amdgcn_exp2f(mu - m_run);
+  }
   if (qi < p.n_q) {
     const size_t zbase = ((size_t)b * p.n_q + qi) * p.ldz + (size_t)r * p.d_vh;
     #pragma unroll

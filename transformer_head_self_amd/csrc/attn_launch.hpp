@@ -12,6 +12,7 @@ namespace mha {
 #define MHA_ATTN_BN 64
 #endif
 
+
 template <typename T, int DH, int DV>
 hipError_t launch_attn_fixed(AttnParams p, hipStream_t stream) {
   constexpr int WAVES = MHA_ATTN_WAVES;
@@ -22,9 +23,18 @@ hipError_t launch_attn_fixed(AttnParams p, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   const bool fast = p.d_h == DH && p.d_vh == DV && p.vec_q && p.vec_k && p.vec_v &&
                     p.allowed == nullptr;
+  // The deferred-shift variant is used for the fast path (causal / key
+  // padding masks only, where every row's first block holds an allowed key)
+  // except for bf16, whose extra rounding of the scaled query would cost
+  // accuracy.
+  constexpr bool lazy = !__is_same(T, bf16);
+  // Three waves per SIMD (at most 168 VGPRs) for the fp16 fast path with
+  // head widths up to 64: measured 6-8 % faster than two; wider heads need
+  // more registers than that.
+  constexpr int occ = (__is_same(T, f16) && DH <= 64 && DV <= 64) ? 3 : 1;
   if (fast)
-    hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true>), dim3((unsigned)grid),
-                       dim3(C::NT), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, lazy, occ>),
+                       dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, false>), dim3((unsigned)grid),
                        dim3(C::NT), 0, stream, p);

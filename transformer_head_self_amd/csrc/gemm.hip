@@ -1,13 +1,29 @@
 // Launchers for the projection GEMM (fp32 and bf16 instantiations).
 #include "gemm.hpp"
+#include "gemm2.hpp"
 
 namespace mha {
 
 // compute_dtype: element type of A and of the MFMA operands; w_dtype: storage
 // type of W.  Supported pairs: (f32, f32), (bf16, bf16), (f16, f16), (f16, bf16).
+// The 256x128 2-byte kernel applies when every problem has K a multiple of
+// 64, N a multiple of 8, 16-byte aligned rows, element offsets below 2^31
+// and (head-major store) a head width that is a multiple of 4.
+static bool gemm2_applies(const GemmBatch& b, int compute_dtype, int w_dtype) {
+  if (compute_dtype == kF32 || w_dtype == kF32) return false;
+  for (int i = 0; i < b.count; ++i) {
+    const GemmProblem& p = b.p[i];
+    if (p.K % 64 != 0 || p.N % 8 != 0 || p.N < 8 || !p.vec_a || !p.vec_w) return false;
+    if (p.epilogue == kHeads && p.dh % 4 != 0) return false;
+    if ((long long)p.M * p.K >= (1LL << 31) || (long long)p.K * p.N >= (1LL << 31)) return false;
+  }
+  return true;
+}
+
 hipError_t launch_gemm(const GemmBatch& in, int compute_dtype, int w_dtype, hipStream_t stream) {
   GemmBatch b = in;
-  const int BM = 128, BN = 128;  // GemmCfg<T>::BM/BN for both element types
+  const bool big = gemm2_applies(b, compute_dtype, w_dtype);
+  const int BM = big ? 256 : 128, BN = 128;
   int total = 0;
   for (int i = 0; i < b.count; ++i) {
     GemmProblem& p = b.p[i];
@@ -18,6 +34,17 @@ hipError_t launch_gemm(const GemmBatch& in, int compute_dtype, int w_dtype, hipS
   }
   b.total_tiles = total;
   if (total == 0) return hipSuccess;
+  if (big) {
+    if (compute_dtype == kBF16 && w_dtype == kBF16)
+      hipLaunchKernelGGL((gemm2_kernel<bf16, bf16>), dim3(total), dim3(256), 0, stream, b);
+    else if (compute_dtype == kF16 && w_dtype == kF16)
+      hipLaunchKernelGGL((gemm2_kernel<f16, f16>), dim3(total), dim3(256), 0, stream, b);
+    else if (compute_dtype == kF16 && w_dtype == kBF16)
+      hipLaunchKernelGGL((gemm2_kernel<f16, bf16>), dim3(total), dim3(256), 0, stream, b);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (compute_dtype == kBF16 && w_dtype == kBF16)
     hipLaunchKernelGGL((gemm_kernel<bf16, bf16>), dim3(total), dim3(256), 0, stream, b);
   else if (compute_dtype == kF16 && w_dtype == kF16)

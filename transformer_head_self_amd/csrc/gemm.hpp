@@ -73,7 +73,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmBatch batch) {
   #pragma unroll
   for (int q = 1; q < 3; ++q)
     if (q < batch.count && tile >= batch.p[q].tile_begin) pi = q;
-  const GemmProblem& P = batch.p[pi];
+  // constant indices: the selected problem stays in scalar registers
+  const GemmProblem P = (pi == 0) ? batch.p[0] : (pi == 1) ? batch.p[1] : batch.p[2];
   const int t_local = tile - P.tile_begin;
   const int tm = t_local / P.tiles_n;
   const int tn = t_local - tm * P.tiles_n;

@@ -90,17 +90,6 @@ __device__ __forceinline__ float sum8(const f16x8& p, float acc) {
   return acc;
 }
 
-// Transposing LDS read of four 16-bit values (gfx950).  Within each group of
-// 16 lanes, output lane i receives, in slot e, the value at position i % 4 of
-// the four-element run addressed by lane 4e + i/4 of the same group.
-template <typename T>
-__device__ __forceinline__ typename Elem<T>::vec4 lds_read_tr4(const T* p) {
-  typedef short s4 __attribute__((ext_vector_type(4)));
-  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s4*)(const_cast<T*>(p)));
-  return __builtin_bit_cast(typename Elem<T>::vec4, v);
-}
-
 // FAST: every row of Q, K, V is exactly DH / DV wide with 16-byte aligned
 // rows, and there is no boolean mask; the host selects it when that holds.
 // The general variant predicates every column and reads the boolean mask.

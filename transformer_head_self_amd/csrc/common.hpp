@@ -162,6 +162,18 @@ __device__ __forceinline__ void store4(void* base, int dtype, size_t idx, bool v
   }
 }
 
+// Transposing LDS read of four 16-bit values (gfx950 ds_read_b64_tr_b16).
+// Within each group of 16 lanes, output lane i receives, in slot e, the
+// value at position i % 4 of the four-element run addressed by lane
+// 4e + i/4 of the same group (lane layout measured on the hardware).
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::vec4 lds_read_tr4(const T* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s4*)(const_cast<T*>(p)));
+  return __builtin_bit_cast(typename Elem<T>::vec4, v);
+}
+
 // Combine a per-lane value with the lane 32 positions away (the other half
 // of the wave).  v_permlane32_swap exchanges the halves of two registers;
 // with both operands equal, the two results hold the lower half's and the

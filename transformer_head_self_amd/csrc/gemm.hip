@@ -1,6 +1,7 @@
 // Launchers for the projection GEMM (fp32 and bf16 instantiations).
 #include "gemm.hpp"
 #include "gemm2.hpp"
+#include "gemm3.hpp"
 
 namespace mha {
 
@@ -8,6 +9,7 @@ namespace mha {
 // type of W.  Supported pairs: (f32, f32), (bf16, bf16), (f16, f16), (f16, bf16).
 // The 256x128 2-byte kernel applies when every problem has K a multiple of
 // 64, N a multiple of 8, 16-byte aligned rows, element offsets below 2^31
+// (byte offsets below 2^32: the direct-to-LDS kernel's lane offsets)
 // and (head-major store) a head width that is a multiple of 4.
 static bool gemm2_applies(const GemmBatch& b, int compute_dtype, int w_dtype) {
   if (compute_dtype == kF32 || w_dtype == kF32) return false;
@@ -20,9 +22,15 @@ static bool gemm2_applies(const GemmBatch& b, int compute_dtype, int w_dtype) {
   return true;
 }
 
+#ifndef MHA_GEMM_DMA
+#define MHA_GEMM_DMA 1
+#endif
+
 hipError_t launch_gemm(const GemmBatch& in, int compute_dtype, int w_dtype, hipStream_t stream) {
   GemmBatch b = in;
   const bool big = gemm2_applies(b, compute_dtype, w_dtype);
+  // direct-to-LDS variant: same conditions, plus one element type for A and W
+  const bool dma = MHA_GEMM_DMA && big && compute_dtype == w_dtype;
   const int BM = big ? 256 : 128, BN = 128;
   int total = 0;
   for (int i = 0; i < b.count; ++i) {
@@ -31,9 +39,18 @@ hipError_t launch_gemm(const GemmBatch& in, int compute_dtype, int w_dtype, hipS
     p.tiles_n = (p.N + BN - 1) / BN;
     p.tile_begin = total;
     total += p.tiles_m * p.tiles_n;
+    p.dh_div = make_fastdiv(p.dh > 0 ? (unsigned)p.dh : 1u);
+    p.ntok_div = make_fastdiv(p.ntok > 0 ? (unsigned)p.ntok : 1u);
   }
   b.total_tiles = total;
   if (total == 0) return hipSuccess;
+  if (dma) {
+    if (compute_dtype == kBF16)
+      hipLaunchKernelGGL((gemm3_kernel<bf16>), dim3(total), dim3(256), 0, stream, b);
+    else
+      hipLaunchKernelGGL((gemm3_kernel<f16>), dim3(total), dim3(256), 0, stream, b);
+    return hipGetLastError();
+  }
   if (big) {
     if (compute_dtype == kBF16 && w_dtype == kBF16)
       hipLaunchKernelGGL((gemm2_kernel<bf16, bf16>), dim3(total), dim3(256), 0, stream, b);

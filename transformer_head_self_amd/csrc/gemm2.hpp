@@ -20,6 +20,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "gemm_store.hpp"
 #include "internal.hpp"
 
 namespace mha {
@@ -34,14 +35,6 @@ struct Gemm2Cfg {
   static constexpr int X_PER_T = BM * BK / VEC / NT;   // 8
   static constexpr int W_PER_T = BK * BN / VEC / NT;   // 4
 };
-
-template <typename T>
-__device__ __forceinline__ typename Elem<T>::vec4 lds_tr4(const T* p) {
-  typedef short s4 __attribute__((ext_vector_type(4)));
-  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s4*)(const_cast<T*>(p)));
-  return __builtin_bit_cast(typename Elem<T>::vec4, v);
-}
 
 // T: element type of A, of the LDS tiles and of the MFMA operands (bf16/f16).
 // TW: storage type of W (2 bytes); a W of the other kind is re-rounded to T
@@ -147,8 +140,8 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmBatch batch) {
       #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const T* wp = &Ws[woff + kc * 16 * C::WROW + j * 32];
-        const vec4 lo = lds_tr4<T>(wp);
-        const vec4 hi = lds_tr4<T>(wp + 4 * C::WROW);
+        const vec4 lo = lds_read_tr4<T>(wp);
+        const vec4 hi = lds_read_tr4<T>(wp + 4 * C::WROW);
         wf[j] = vec{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
       #pragma unroll
@@ -161,51 +154,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_kernel(GemmBatch batch) {
     }
   }
 
-  // ---- epilogue (as gemm_kernel).  The layout and element-type choices are
-  // made once, outside the fully unrolled store loop, so acc stays in registers.
-  auto store_all = [&](auto dt_tag, auto heads_tag) {
-    constexpr int DT = decltype(dt_tag)::value;
-    constexpr bool HEADS = decltype(heads_tag)::value;
-    #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 128 + i * 32 + l32;
-      const int bb = m / P.ntok, t = m - bb * P.ntok;
-      #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int n = n0 + wn * 64 + j * 32 + 8 * a + 4 * g;
-          if (m < M && n < N) {
-            size_t idx;
-            bool vec_ok;
-            if constexpr (HEADS) {   // dh % 4 == 0: four columns stay in one head
-              const int r = n / P.dh, e = n - r * P.dh;
-              idx = (((size_t)bb * P.heads + r) * P.ntok + t) * P.dh + e;
-              vec_ok = true;
-            } else {
-              idx = (size_t)m * N + n;
-              vec_ok = P.vec_c && (N % 4) == 0;
-            }
-            store4(P.C, DT, idx, vec_ok, N - n, acc[j][i][4 * a], acc[j][i][4 * a + 1],
-                   acc[j][i][4 * a + 2], acc[j][i][4 * a + 3]);
-          }
-        }
-    }
-  };
-  typedef std::integral_constant<int, kF32> F32T;
-  typedef std::integral_constant<int, kBF16> BF16T;
-  typedef std::integral_constant<int, kF16> F16T;
-  typedef std::integral_constant<bool, true> HeadsT;
-  typedef std::integral_constant<bool, false> RowsT;
-  if (P.epilogue == kHeads) {   // head width a multiple of 4 (host-checked)
-    if (P.out_dtype == kF32) store_all(F32T(), HeadsT());
-    else if (P.out_dtype == kBF16) store_all(BF16T(), HeadsT());
-    else store_all(F16T(), HeadsT());
-  } else {
-    if (P.out_dtype == kF32) store_all(F32T(), RowsT());
-    else if (P.out_dtype == kBF16) store_all(BF16T(), RowsT());
-    else store_all(F16T(), RowsT());
-  }
+  store_wave_block_any(P, acc, m0 + wm * 128, n0 + wn * 64, g, l32);
 }
 
 }  // namespace mha

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "common.hpp"
+#include "fastdiv.hpp"
 
 namespace mha {
 
@@ -31,6 +32,7 @@ struct GemmProblem {
   int tiles_m, tiles_n, tile_begin;  // filled by the launcher
   int vec_a, vec_w;  // 16-byte vector loads allowed for A / W rows
   int vec_c;         // vector stores allowed for C (kRowMajor)
+  FastDiv dh_div, ntok_div;  // filled by the launcher
 };
 
 struct GemmBatch {

@@ -392,3 +392,35 @@ def test_bf16_output_dtype():
     # bf16 storage of Y adds up to half an ulp (2^-9 relative) per element
     err = float(np.max(np.abs(Y - ref) / (np.abs(ref) * 2.0 ** -8 + 2e-2 * np.sqrt(np.mean(ref ** 2)))))
     assert err <= 1.0
+
+
+@pytest.mark.parametrize("shape", [
+    # K3 on the small-tile kernel: h*d_vh = 36, h*d_vh*d_o = 1332 (ragged tail of 4)
+    dict(B=3, n_q=45, n_k=77, d_q=40, d_k=24, d_v=56, h=3, d_h=8, d_vh=12, d_o=37),
+    # K3 on the direct-to-LDS kernel: h*d_vh = 64, d_o = 200 (ragged column tile)
+    dict(B=2, n_q=130, n_k=130, d_q=64, d_k=64, d_v=64, h=4, d_h=16, d_vh=16, d_o=200),
+])
+@pytest.mark.parametrize("wo_offset", [0, 1, 3])
+def test_bf16_forward_ragged_shapes_and_unaligned_w_o(shape, wo_offset):
+    """bf16 inputs with fp16 intermediates: W^O is re-rounded to fp16 into the
+    workspace before the output projection; that copy must handle element
+    counts that are not a multiple of 8 and a W^O that is only element-aligned."""
+    w = custom_workload(kind="cross", dtype="bf16", causal=False, pad_range=(1, shape["n_k"]),
+                        seed=31, **shape)
+    _say(f"[bf16 ragged] {shape} W_O offset {wo_offset}")
+    x = make_inputs(w)
+    Q, K, V = (_to_dev(x[k], "bf16") for k in ("Q", "K", "V"))
+    W = {k: _to_dev(x[k], "bf16") for k in ("W_Q", "W_K", "W_V")}
+    n_wo = x["W_O"].size
+    buf = torch.zeros(n_wo + wo_offset, dtype=torch.bfloat16, device=DEV)
+    buf[wo_offset:] = _to_dev(x["W_O"], "bf16").reshape(-1)
+    W_O = buf[wo_offset:].view(x["W_O"].shape)
+    kl = torch.from_numpy(x["key_len"]).to(DEV)
+    Y = mha.mha_forward(Q, K, V, W["W_Q"], W["W_K"], W["W_V"], W_O, w.h, w.d_h, w.d_vh,
+                        key_len=kl)
+    torch.cuda.synchronize()
+    ref = mha_ref(x["Q"], x["K"], x["V"], x["W_Q"], x["W_K"], x["W_V"], x["W_O"], w.h, w.d_h,
+                  w.d_vh, w.scale, _allow(w, x))["Y"]
+    err = _rel_err(Y.float().cpu().numpy(), ref)
+    _say(f"  Y err {err:.3e}")
+    assert err <= TOL["bf16"]

@@ -1,17 +1,17 @@
-// Launchers for the projection GEMM (fp32 and bf16 instantiations).
+// Launchers for the projection GEMMs: the direct-to-LDS 2-byte kernel where
+// its conditions hold, else the general 128x128 kernel (every element type).
 #include "gemm.hpp"
-#include "gemm2.hpp"
-#include "gemm3.hpp"
+#include "gemm_dma.hpp"
 
 namespace mha {
 
 // compute_dtype: element type of A and of the MFMA operands; w_dtype: storage
 // type of W.  Supported pairs: (f32, f32), (bf16, bf16), (f16, f16), (f16, bf16).
-// The 256x128 2-byte kernel applies when every problem has K a multiple of
+// The 256x128 direct-to-LDS kernel applies when every problem has K a multiple of
 // 64, N a multiple of 8, 16-byte aligned rows, element offsets below 2^31
 // (byte offsets below 2^32: the direct-to-LDS kernel's lane offsets)
 // and (head-major store) a head width that is a multiple of 4.
-static bool gemm2_applies(const GemmBatch& b, int compute_dtype, int w_dtype) {
+static bool dma_gemm_applies(const GemmBatch& b, int compute_dtype, int w_dtype) {
   if (compute_dtype == kF32 || w_dtype == kF32) return false;
   for (int i = 0; i < b.count; ++i) {
     const GemmProblem& p = b.p[i];
@@ -22,15 +22,9 @@ static bool gemm2_applies(const GemmBatch& b, int compute_dtype, int w_dtype) {
   return true;
 }
 
-#ifndef MHA_GEMM_DMA
-#define MHA_GEMM_DMA 1
-#endif
-
 hipError_t launch_gemm(const GemmBatch& in, int compute_dtype, int w_dtype, hipStream_t stream) {
   GemmBatch b = in;
-  const bool big = gemm2_applies(b, compute_dtype, w_dtype);
-  // direct-to-LDS variant: same conditions, plus one element type for A and W
-  const bool dma = MHA_GEMM_DMA && big && compute_dtype == w_dtype;
+  const bool big = dma_gemm_applies(b, compute_dtype, w_dtype);
   const int BM = big ? 256 : 128, BN = 128;
   int total = 0;
   for (int i = 0; i < b.count; ++i) {
@@ -44,20 +38,13 @@ hipError_t launch_gemm(const GemmBatch& in, int compute_dtype, int w_dtype, hipS
   }
   b.total_tiles = total;
   if (total == 0) return hipSuccess;
-  if (dma) {
-    if (compute_dtype == kBF16)
-      hipLaunchKernelGGL((gemm3_kernel<bf16>), dim3(total), dim3(256), 0, stream, b);
-    else
-      hipLaunchKernelGGL((gemm3_kernel<f16>), dim3(total), dim3(256), 0, stream, b);
-    return hipGetLastError();
-  }
   if (big) {
     if (compute_dtype == kBF16 && w_dtype == kBF16)
-      hipLaunchKernelGGL((gemm2_kernel<bf16, bf16>), dim3(total), dim3(256), 0, stream, b);
+      hipLaunchKernelGGL((gemm_dma_kernel<bf16, bf16>), dim3(total), dim3(256), 0, stream, b);
     else if (compute_dtype == kF16 && w_dtype == kF16)
-      hipLaunchKernelGGL((gemm2_kernel<f16, f16>), dim3(total), dim3(256), 0, stream, b);
+      hipLaunchKernelGGL((gemm_dma_kernel<f16, f16>), dim3(total), dim3(256), 0, stream, b);
     else if (compute_dtype == kF16 && w_dtype == kBF16)
-      hipLaunchKernelGGL((gemm2_kernel<f16, bf16>), dim3(total), dim3(256), 0, stream, b);
+      hipLaunchKernelGGL((gemm_dma_kernel<f16, bf16>), dim3(total), dim3(256), 0, stream, b);
     else
       return hipErrorInvalidValue;
     return hipGetLastError();

@@ -1,10 +1,12 @@
 // Projection GEMM with direct global->LDS loads (gfx950), 2-byte elements.
 //
-// Same products and epilogues as gemm_kernel / gemm2_kernel (page "Multi-head
+// Same products and epilogues as gemm_kernel (page "Multi-head
 // attention and self-attention", Definition; review page "Multi-Head
-// Attention", "Separate and Combined Projections").  Used when A and W have
-// the same 2-byte element type, K is a multiple of 64, N a multiple of 8,
-// rows are 16-byte aligned and byte offsets into A and W fit in 32 bits.
+// Attention", "Separate and Combined Projections").  Used for 2-byte A and W
+// when K is a multiple of 64, N a multiple of 8, rows are 16-byte aligned
+// and byte offsets into A and W fit in 32 bits.  A W stored in the other
+// 2-byte type (bf16 weights with fp16 operands) is moved as stored and
+// re-rounded (nearest even) after it is read from LDS.
 //
 // Design (ours): a 256 x 128 workgroup tile, four waves of 128 x 64, k
 // stages of 32.  Tiles move from global memory into LDS with
@@ -28,7 +30,7 @@
 
 namespace mha {
 
-struct Gemm3Cfg {
+struct GemmDmaCfg {
   static constexpr int BM = 256, BN = 128, BK = 32, NS = 3;
   static constexpr int NT = 256;
   static constexpr int XBYTES = BM * BK * 2;           // 16 KB per stage
@@ -66,13 +68,15 @@ __device__ __forceinline__ void wait_vm_lds() {
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" : : : "memory"); }
 
-template <typename T>
+// T: element type of A and of the MFMA operands; TW: storage type of W.
+template <typename T, typename TW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm3_kernel(GemmBatch batch) {
-  static_assert(sizeof(T) == 2, "2-byte elements only");
-  typedef Gemm3Cfg C;
+void gemm_dma_kernel(GemmBatch batch) {
+  static_assert(sizeof(T) == 2 && sizeof(TW) == 2, "2-byte elements only");
+  typedef GemmDmaCfg C;
   typedef typename Elem<T>::vec vec;
-  typedef typename Elem<T>::vec4 vec4;
+  typedef typename Elem<TW>::vec wvec;
+  typedef typename Elem<TW>::vec4 wvec4;
 
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
@@ -174,9 +178,9 @@ void gemm3_kernel(GemmBatch batch) {
       #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const char* p = ws + wr[j] + kc * 16 * 256;
-        const vec4 lo = lds_read_tr4<T>(reinterpret_cast<const T*>(p));
-        const vec4 hi = lds_read_tr4<T>(reinterpret_cast<const T*>(p + 4 * 256));
-        wf[j] = vec{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const wvec4 lo = lds_read_tr4<TW>(reinterpret_cast<const TW*>(p));
+        const wvec4 hi = lds_read_tr4<TW>(reinterpret_cast<const TW*>(p + 4 * 256));
+        wf[j] = convert_chunk<T, TW>(wvec{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       }
       #pragma unroll
       for (int i = 0; i < 4; ++i)

@@ -424,3 +424,44 @@ def test_bf16_forward_ragged_shapes_and_unaligned_w_o(shape, wo_offset):
     err = _rel_err(Y.float().cpu().numpy(), ref)
     _say(f"  Y err {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("row_stats", [False, True])
+def test_attn_core_f16_late_score_jumps(row_stats):
+    """Scores that jump far above every earlier key's score, late in the row.
+
+    Feature 0 of every query is 4; keys 200 and 450 carry 40 and 300 there
+    (scale 1/8): their scores exceed the earlier keys' by about 20 and 150
+    nats.  The fp16 fast path keeps its running state at a deferred shift;
+    the first jump is past its threshold (2^8 in base 2) and forces a move of
+    the shift, and the second overflows a weight computed at the old shift,
+    so the block is redone at the new one.  Both must match the oracle
+    (causal mask: the jumps reach rows 200.. and 450.. only)."""
+    B, h, n, d = 1, 2, 600, 64
+    Qh, Kh, Vh = make_heads(B, h, n, n, d, d, "f32", seed=21)
+    Qh[..., 0] = 4.0
+    Kh[..., 0] *= 0.1
+    Kh[:, :, 200, 0] = 40.0
+    Kh[:, :, 450, 0] = 300.0
+    to16 = lambda a: torch.from_numpy(a).to(DEV).to(torch.float16)
+    Qh16, Kh16, Vh16 = (t.float().cpu().numpy() for t in (to16(Qh), to16(Kh), to16(Vh)))
+    ref = attn_core_ref(Qh16, Kh16, Vh16, 0.125, allowed_set(B, n, n, causal=True))
+    rm = rl = None
+    if row_stats:
+        rm = torch.empty((B, h, n), dtype=torch.float32, device=DEV)
+        rl = torch.empty_like(rm)
+    _say(f"[late jumps] row_stats={row_stats}")
+    Z = mha.attn_core(to16(Qh), to16(Kh), to16(Vh), scale=0.125, causal=True, row_m=rm,
+                      row_l=rl)
+    torch.cuda.synchronize()
+    Zc = Z.cpu().numpy()
+    assert np.isfinite(Zc).all()
+    err = _rel_err(Zc, ref["Z"])
+    _say(f"  Z err {err:.3e}")
+    assert err <= 1e-2
+    # rows past key 450 attend almost only to it: Z is close to v_450 there
+    np.testing.assert_allclose(Zc[0, 451:, :d], np.broadcast_to(Vh16[0, 0, 450], (n - 451, d)),
+                               atol=2e-3)
+    if row_stats:
+        np.testing.assert_allclose(rm.cpu().numpy(), ref["m"], rtol=2e-3, atol=2e-3)
+        np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-2)

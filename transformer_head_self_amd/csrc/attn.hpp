@@ -105,10 +105,22 @@ __device__ __forceinline__ float sum8(const f16x8& p, float acc) {
 // score MFMA as its accumulator input, so a weight costs one exponential.
 constexpr float kLazyTau = 8.0f;
 
+// Block-sum trigger (deferred shift without row statistics): the row's
+// block maximum is not formed.  A weight above 2^kLazyTau makes this lane's
+// partial sum of the block's rounded weights exceed 2^kLazyTau, so that sum
+// decides when the block is redone at an exact new shift; weights are finite
+// and at most 2^kLazyTau whenever it stays below.
+constexpr float kLazyLimit = 256.0f;   // 2^kLazyTau
+static_assert(kLazyLimit == (float)(1 << (int)kLazyTau), "limit = 2^tau");
+
 // OCC: minimum waves per SIMD the register allocation must allow.
-template <typename T, int DH, int DV, int WAVES, int BN_, bool FAST, bool LAZY = false, int OCC = 1>
+// STATS: the caller wants the final (m, l) per row (deferred-shift variant:
+// the exact running maximum is tracked only then).
+template <typename T, int DH, int DV, int WAVES, int BN_, bool FAST, bool LAZY = false, int OCC = 1,
+          bool STATS = true>
 __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p) {
   typedef AttnCfg<T, DH, DV, WAVES, BN_> C;
+  static_assert(STATS || (LAZY && C::TR), "the block-sum trigger is for 2-byte elements");
   constexpr int NKB = C::NKB;
   typedef typename Elem<T>::vec vec;
   typedef typename Elem<T>::vec4 vec4;
@@ -298,60 +310,88 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       // block always holds key 0, which causal and padding masks allow), so
       // the accumulator starts at -mu; the first block starts at 0.
       const bool shifted = LAZY && blk > 0;
-      #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        if (shifted) {
-          s[kb] = negmu;
-        } else {
-          #pragma unroll
-          for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-        }
+      auto raw_scores = [&](bool at_mu) {
         #pragma unroll
-        for (int c = 0; c < C::KCH; ++c) {
-          const vec kf = *reinterpret_cast<const vec*>(
-              &ks[(kb * 32 + l32) * C::KPAD + c * 2 * VEC + g * VEC]);
-          mfma_chunk(s[kb], kf, qf[c]);
+        for (int kb = 0; kb < NKB; ++kb) {
+          if (at_mu) {
+            s[kb] = negmu;
+          } else {
+            #pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+          }
+          #pragma unroll
+          for (int c = 0; c < C::KCH; ++c) {
+            const vec kf = *reinterpret_cast<const vec*>(
+                &ks[(kb * 32 + l32) * C::KPAD + c * 2 * VEC + g * VEC]);
+            mfma_chunk(s[kb], kf, qf[c]);
+          }
         }
-      }
+      };
+      raw_scores(shifted);
 
-      // ---- mask and block maximum -----------------------------------------
+      // ---- mask: forbidden scores become -inf (weight exactly 0) -------------
+      // Score slot (kb, i) of this lane is key k0 + off(kb, i) + 4 g with
+      // off = 32 kb + 8 (i / 4) + i % 4.  Causal and key padding allow exactly
+      // the keys j <= lim = min(qi, kvalid - 1): one compare per score.
       const bool need_mask =
           (k0 + BN > kvalid) || (p.causal && k0 + BN - 1 > qw) || (!FAST && Gb != nullptr);
-      uint64_t okbits = ~0ull;         // bit 16*kb + i: key allowed for this row
-      float mx = -INFINITY;
-      if (need_mask) {
+      auto apply_mask = [&]() {
+        const int lim = p.causal ? min(qi, kvalid - 1) : kvalid - 1;
+        const int t = lim - k0 - 4 * g;
         #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int j = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-            bool ok = j < kvalid;
-            if (p.causal) ok = ok && (j <= qi);
+            const int off = kb * 32 + 8 * (i >> 2) + (i & 3);
+            bool ok = off <= t;
             if (!FAST && Gb != nullptr && ok)
-              ok = qi < p.n_q && Gb[(size_t)qi * p.n_k + j] != 0;
-            if (!ok) okbits &= ~(1ull << (16 * kb + i));
-            mx = fmaxf(mx, ok ? s[kb][i] : -INFINITY);
+              ok = qi < p.n_q && Gb[(size_t)qi * p.n_k + k0 + off + 4 * g] != 0;
+            s[kb][i] = ok ? s[kb][i] : -INFINITY;
           }
-      } else {
+      };
+      if (need_mask) apply_mask();
+      auto block_max = [&]() {
+        float mx = -INFINITY;
         #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      }
-      mx = half_max(mx);
+        return half_max(mx);
+      };
+      // rescale the running (l, z) by a (a row's shift moved up)
+      auto rescale = [&](float a) {
+        l_run *= a;
+        #pragma unroll
+        for (int d = 0; d < C::NDV; ++d)
+          #pragma unroll
+          for (int i = 0; i < 16; ++i) o[d][i] *= a;
+      };
 
-      if constexpr (LAZY) {
+      if constexpr (LAZY && !STATS) {
+        if (!shifted) {
+          // first block: the exact block maximum becomes mu
+          const float mx = block_max();
+          mu = (mx == -INFINITY) ? 0.f : mx;
+          #pragma unroll
+          for (int i = 0; i < 16; ++i) negmu[i] = -mu;
+          #pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            #pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(s[kb][i] - mu);
+        } else {
+          #pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            #pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(s[kb][i]);
+        }
+      } else if constexpr (LAZY) {
+        const float mx = block_max();
         if (shifted) {
           // mx = (block maximum) - mu for every row (-inf: no allowed key)
           m_run = fmaxf(m_run, mx + mu);
           if (__any(mx > kLazyTau)) {       // some row ran too far above its shift
             const float dmu = fmaxf(mx, 0.f);  // move mu to max(mu, block max)
-            const float a = __builtin_amdgcn_exp2f(-dmu);
-            l_run *= a;
-            #pragma unroll
-            for (int d = 0; d < C::NDV; ++d)
-              #pragma unroll
-              for (int i = 0; i < 16; ++i) o[d][i] *= a;
+            rescale(__builtin_amdgcn_exp2f(-dmu));
             #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
               #pragma unroll
@@ -360,20 +400,10 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
             #pragma unroll
             for (int i = 0; i < 16; ++i) negmu[i] = -mu;
           }
-          if (need_mask) {
+          #pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
             #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-              #pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                const float e = __builtin_amdgcn_exp2f(s[kb][i]);
-                s[kb][i] = ((okbits >> (16 * kb + i)) & 1ull) ? e : 0.f;
-              }
-          } else {
-            #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-              #pragma unroll
-              for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(s[kb][i]);
-          }
+            for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(s[kb][i]);
         } else {
           // first block: the exact block maximum becomes both m and mu
           m_run = mx;
@@ -383,69 +413,97 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
           #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
             #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float e = __builtin_amdgcn_exp2f(s[kb][i] - mu);
-              s[kb][i] = (!need_mask || ((okbits >> (16 * kb + i)) & 1ull)) ? e : 0.f;
-            }
+            for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(s[kb][i] - mu);
         }
       } else {
-      // ---- merge: new shift, rescale the running summary ------------------
-      const float mblk = (mx == -INFINITY) ? -INFINITY : mx * cs;
-      const float m_new = fmaxf(m_run, mblk);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-      if (__any(alpha != 1.0f)) {     // some row's maximum moved
-        l_run *= alpha;
-        #pragma unroll
-        for (int d = 0; d < C::NDV; ++d)
+        // ---- merge: new shift, rescale the running summary ------------------
+        const float mx = block_max();
+        const float mblk = (mx == -INFINITY) ? -INFINITY : mx * cs;
+        const float m_new = fmaxf(m_run, mblk);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        m_run = m_new;
+        if (__any(alpha != 1.0f)) rescale(alpha);   // some row's maximum moved
+        if (need_mask) {
+          // a forbidden score is -inf; with c = 0 the product -inf * 0 would
+          // be NaN, so its weight is set to 0 explicitly
           #pragma unroll
-          for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+          for (int kb = 0; kb < NKB; ++kb)
+            #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][i], cs, -m_use));
+              s[kb][i] = (s[kb][i] == -INFINITY) ? 0.f : e;
+            }
+        } else {
+          #pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            #pragma unroll
+            for (int i = 0; i < 16; ++i)
+              s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], cs, -m_use));
+        }
       }
-      if (need_mask) {
-        #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][i], cs, -m_use));
-            s[kb][i] = ((okbits >> (16 * kb + i)) & 1ull) ? e : 0.f;
-          }
-      } else {
-        #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], cs, -m_use));
-      }
-      }  // exact shift
 
       // ---- z += P V  (as O^T += V^T P^T), l += sum of the rounded weights --
-      #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        if constexpr (C::TR) {
-          // A-operand slot t of lane half g holds key kb*32 + 16*st + 4*g + t
-          // (t < 4) or kb*32 + 16*st + 8 + 4*g + (t - 4) (t >= 4), the same
-          // keys as the B operand's score slots; this lane feeds the read
-          // with 4 features of key row srow, starting at column scol.
-          const int srow = kb * 32 + 4 * g + ((lane & 15) >> 2);
-          const int scol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      if constexpr (C::TR) {
+        // weights rounded to T, in the B-operand layout of the value product;
+        // slot t of chunk (kb, st) is key kb*32 + 16*st + 4*g + t (t < 4) or
+        // kb*32 + 16*st + 8 + 4*g + (t - 4) (t >= 4), as in the score block.
+        vec pb[NKB][2];
+        float bsum = 0.f;
+        #pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
           #pragma unroll
           for (int st = 0; st < 2; ++st) {
             floatx8 pf;
             #pragma unroll
             for (int t = 0; t < 8; ++t) pf[t] = s[kb][8 * st + t];
-            const vec pb = Cvt<T>::eight(pf);
-            l_run = sum8(pb, l_run);
+            pb[kb][st] = Cvt<T>::eight(pf);
+            bsum = sum8(pb[kb][st], bsum);
+          }
+        if constexpr (LAZY && !STATS) {
+          if (shifted && __any(!(bsum <= kLazyLimit))) {
+            // rare: some weight exceeded 2^tau (or overflowed).  Redo the
+            // block from its raw scores with mu moved to the exact maximum.
+            raw_scores(false);
+            if (need_mask) apply_mask();
+            const float mx = block_max();
+            const float mu_new = fmaxf(mu, mx);
+            rescale(__builtin_amdgcn_exp2f(mu - mu_new));
+            mu = mu_new;
+            #pragma unroll
+            for (int i = 0; i < 16; ++i) negmu[i] = -mu;
+            bsum = 0.f;
+            #pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+              #pragma unroll
+              for (int st = 0; st < 2; ++st) {
+                floatx8 pf;
+                #pragma unroll
+                for (int t = 0; t < 8; ++t)
+                  pf[t] = __builtin_amdgcn_exp2f(s[kb][8 * st + t] - mu);
+                pb[kb][st] = Cvt<T>::eight(pf);
+                bsum = sum8(pb[kb][st], bsum);
+              }
+          }
+        }
+        l_run += bsum;
+        const int srow = 4 * g + ((lane & 15) >> 2);
+        const int scol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        #pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          #pragma unroll
+          for (int st = 0; st < 2; ++st)
             #pragma unroll
             for (int d = 0; d < C::NDV; ++d) {
-              const T* v0 = &vs[(srow + 16 * st) * C::VROW + d * 32 + scol];
+              const T* v0 = &vs[(kb * 32 + 16 * st + srow) * C::VROW + d * 32 + scol];
               const vec4 lo = lds_read_tr4<T>(v0);
               const vec4 hi = lds_read_tr4<T>(v0 + 8 * C::VROW);
               const vec va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-              mfma_chunk(o[d], va, pb);
+              mfma_chunk(o[d], va, pb[kb][st]);
             }
-          }
-        } else {
+      } else {
+        #pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
           #pragma unroll
           for (int a = 0; a < 4; ++a) {
             const floatx4 pf = {s[kb][4 * a], s[kb][4 * a + 1], s[kb][4 * a + 2],
@@ -469,7 +527,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   // ---- finalise: z / l, store into the concatenation --------------------------
   float l_tot = half_sum(l_run);
   const float inv = 1.0f / l_tot;
-  if constexpr (LAZY) {
+  if constexpr (LAZY && STATS) {
     // l at the exact maximum: l* e^(mu - m)   (z / l is unchanged)
     if (m_run != -INFINITY) l_tot *= __builtin_amdgcn_exp2f(mu - m_run);
   }
@@ -484,7 +542,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
                o[d][4 * a + 1] * inv, o[d][4 * a + 2] * inv, o[d][4 * a + 3] * inv);
       }
     }
-    if (g == 0) {
+    if (STATS && g == 0) {
       const size_t ri = (size_t)bh * p.n_q + qi;
       if (p.row_m) p.row_m[ri] = (m_run == -INFINITY) ? -INFINITY : m_run * kLn2;
       if (p.row_l) p.row_l[ri] = l_tot;

@@ -32,6 +32,16 @@ hipError_t launch_attn_fixed(AttnParams p, hipStream_t stream) {
   // head widths up to 64: measured 6-8 % faster than two; wider heads need
   // more registers than that.
   constexpr int occ = (__is_same(T, f16) && DH <= 64 && DV <= 64) ? 3 : 1;
+  // Without requested row statistics the 2-byte deferred-shift variant
+  // skips the running maximum (block-sum trigger).
+  const bool stats = p.row_m != nullptr || p.row_l != nullptr;
+  if constexpr (lazy && sizeof(T) == 2) {
+    if (fast && !stats) {
+      hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, lazy, occ, false>),
+                         dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
   if (fast)
     hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, lazy, occ>),
                        dim3((unsigned)grid), dim3(C::NT), 0, stream, p);

@@ -34,6 +34,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "lds_dma.hpp"
 
 namespace mha {
 
@@ -57,6 +58,15 @@ struct AttnCfg {
   static constexpr int V_CHUNKS = BN * DV / VEC;
   static constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
   static constexpr int V_PER_T = (V_CHUNKS + NT - 1) / NT;
+  static constexpr int REG_LDS = 2 * (KBUF + VBUF) * (int)sizeof(T);   // register staging
+  // Direct-to-LDS staging (2-byte fast path): unpadded rows of KRB / VRB
+  // bytes, three stages of one K tile and one V tile, K_WIN / V_WIN 1 KB
+  // load instructions per wave per tile.
+  static constexpr int KRB = DH * (int)sizeof(T), VRB = DV * (int)sizeof(T);
+  static constexpr int KTILE = BN * KRB, VTILE = BN * VRB;
+  static constexpr int STAGE = KTILE + VTILE, NS = 3;
+  static constexpr int K_WIN = KTILE / 1024 / WAVES, V_WIN = VTILE / 1024 / WAVES;
+  static constexpr int DMA_LDS = NS * STAGE;
   static_assert(DH % (2 * VEC) == 0, "DH must be a multiple of a k-chunk");
   static_assert(DV % 32 == 0, "DV must be a multiple of 32");
   static_assert(BN == 32 || BN == 64 || BN == 128, "BN must be 32, 64 or 128");
@@ -88,6 +98,30 @@ __device__ __forceinline__ float sum8(const f16x8& p, float acc) {
     acc = __builtin_amdgcn_fdot2(pr, one, acc, false);
   }
   return acc;
+}
+
+// XOR permutations of the 16-byte chunks of a K / V row in LDS (direct-to-LDS
+// staging), chosen so that the two read patterns hit distinct banks:
+// * K rows (RB bytes) are read 16 bytes per lane, 32 consecutive rows at one
+//   chunk: chunk c of row r is stored in slot c ^ ((r / (256 / RB)) % (RB / 16)),
+//   which gives 16 consecutive rows 16 distinct 16-byte bank groups;
+// * V rows are read with the transposing load, 4 rows x 64 bytes per half
+//   wave: for RB = 128 or 256, chunk c of row r is stored in slot
+//   c ^ 4 ((r / (256 / RB)) % (RB / 64)), putting the 4 rows in distinct 64-byte
+//   quarters of the banks; 64- and 192-byte rows are staggered already.
+template <int RB>
+__device__ __forceinline__ int k_swizzle(int row) {
+  constexpr int RPB = RB >= 256 ? 1 : 256 / RB;
+  return (row / RPB) % (RB / 16);
+}
+template <int RB>
+__device__ __forceinline__ int v_swizzle(int row) {
+  if constexpr (RB == 128 || RB == 256) {
+    constexpr int RPB = 256 / RB;
+    return 4 * ((row / RPB) % (RB / 64));
+  } else {
+    return 0;
+  }
 }
 
 // FAST: every row of Q, K, V is exactly DH / DV wide with 16-byte aligned
@@ -127,8 +161,14 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   constexpr int VEC = C::VEC;
   constexpr int BN = C::BN;
 
-  __shared__ __attribute__((aligned(16))) T Ks[2 * C::KBUF];
-  __shared__ __attribute__((aligned(16))) T Vs[2 * C::VBUF];
+  // DMA: K/V tiles move from global memory straight into LDS (three stages in
+  // flight); otherwise they are staged through registers (two buffers).
+  constexpr bool DMA = C::TR && FAST && BN_ == 64;
+  constexpr int LDS_BYTES = DMA ? C::DMA_LDS : C::REG_LDS;
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+  T* Ks = reinterpret_cast<T*>(smem);
+  T* Vs = Ks + 2 * C::KBUF;
+  const unsigned lds_base = (unsigned)(size_t)(__attribute__((address_space(3))) char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -288,17 +328,107 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
     }
   };
 
-  if (nblk > 0) {
-    load_kv(0);
-    store_kv(0);
+  // ---- direct-to-LDS staging -------------------------------------------------
+  // Window q of this wave's share of a tile is LDS bytes (wave*WIN + q) KB;
+  // lane i fills 16 bytes at 16 i, i.e. tile row t / RB, slot (t % RB) / 16
+  // for t = window*1024 + 16 i, from the global chunk the slot holds.
+  unsigned koff[DMA ? C::K_WIN : 1], voff[DMA ? C::V_WIN : 1];
+  auto tile_row = [&](int win, int rb) { return (win * 1024 + 16 * lane) / rb; };
+  auto k_chunk_of = [&](int win) {
+    const int t = win * 1024 + 16 * lane, row = t / C::KRB;
+    return ((t % C::KRB) / 16) ^ k_swizzle<C::KRB>(row);
+  };
+  auto v_chunk_of = [&](int win) {
+    const int t = win * 1024 + 16 * lane, row = t / C::VRB;
+    return ((t % C::VRB) / 16) ^ v_swizzle<C::VRB>(row);
+  };
+  if constexpr (DMA) {
+    #pragma unroll
+    for (int q = 0; q < C::K_WIN; ++q) {
+      const int win = wave * C::K_WIN + q;
+      koff[q] = tile_row(win, C::KRB) * C::KRB + k_chunk_of(win) * 16;
+    }
+    #pragma unroll
+    for (int q = 0; q < C::V_WIN; ++q) {
+      const int win = wave * C::V_WIN + q;
+      voff[q] = tile_row(win, C::VRB) * C::VRB + v_chunk_of(win) * 16;
+    }
   }
-  __syncthreads();
-  if (nblk > 1) load_kv(1);
+  // block blk into stage blk % 3; in the last block, rows past n_k read the
+  // last key (masked out, weight 0)
+  auto issue_kv = [&](int blk) {
+    const int k0 = blk * BN;
+    const unsigned st = lds_base + (unsigned)((blk % C::NS) * C::STAGE);
+    const char* kg = reinterpret_cast<const char*>(Kb) + (size_t)k0 * C::KRB;
+    const char* vg = reinterpret_cast<const char*>(Vb) + (size_t)k0 * C::VRB;
+    if (k0 + BN <= p.n_k) {
+      #pragma unroll
+      for (int q = 0; q < C::K_WIN; ++q)
+        lds_dma16(kg, koff[q], st + (wave * C::K_WIN + q) * 1024);
+      #pragma unroll
+      for (int q = 0; q < C::V_WIN; ++q)
+        lds_dma16(vg, voff[q], st + C::KTILE + (wave * C::V_WIN + q) * 1024);
+    } else {
+      const int last = p.n_k - 1 - k0;
+      #pragma unroll
+      for (int q = 0; q < C::K_WIN; ++q) {
+        const int win = wave * C::K_WIN + q;
+        const unsigned off = min(tile_row(win, C::KRB), last) * C::KRB + k_chunk_of(win) * 16;
+        lds_dma16(kg, off, st + win * 1024);
+      }
+      #pragma unroll
+      for (int q = 0; q < C::V_WIN; ++q) {
+        const int win = wave * C::V_WIN + q;
+        const unsigned off = min(tile_row(win, C::VRB), last) * C::VRB + v_chunk_of(win) * 16;
+        lds_dma16(vg, off, st + C::KTILE + win * 1024);
+      }
+    }
+  };
+  // Per-lane read offsets within a stage (bytes).  K: row kb*32 + l32, chunk
+  // 2c + g; the permutation depends on the row only through l32.  V: the
+  // transposing read's row 32 kb + 16 st + 8 h + 4 g + (lane % 16) / 4 and
+  // columns 32 d + scol; the permutation depends on the row only through
+  // 4 g + (lane % 16) / 4, so kb, st and h are immediates.
+  int kro[DMA ? C::KCH : 1], vro[DMA ? C::NDV : 1];
+  if constexpr (DMA) {
+    #pragma unroll
+    for (int c = 0; c < C::KCH; ++c)
+      kro[c] = l32 * C::KRB + (((2 * c + g) ^ k_swizzle<C::KRB>(l32)) * 16);
+    const int vr = 4 * g + ((lane & 15) >> 2);
+    const int scol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    #pragma unroll
+    for (int d = 0; d < C::NDV; ++d) {
+      const int ch = (d * 32 + scol) / 8;
+      vro[d] = C::KTILE + vr * C::VRB + ((ch ^ v_swizzle<C::VRB>(vr)) * 16) + (scol % 8) * 2;
+    }
+  }
+
+  if constexpr (DMA) {
+    if (nblk > 0) issue_kv(0);
+    if (nblk > 1) issue_kv(1);
+  } else {
+    if (nblk > 0) {
+      load_kv(0);
+      store_kv(0);
+    }
+    __syncthreads();
+    if (nblk > 1) load_kv(1);
+  }
 
   for (int blk = 0; blk < nblk; ++blk) {
+    if constexpr (DMA) {
+      // block blk has landed once only block blk+1's loads are outstanding;
+      // after the barrier no wave reads block blk-1, whose stage is refilled
+      if (blk + 1 < nblk) wait_vm_lds<C::K_WIN + C::V_WIN>();
+      else wait_vm_lds<0>();
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      if (blk + 2 < nblk) issue_kv(blk + 2);
+    }
     const int cur = blk & 1;
     const T* ks = Ks + cur * C::KBUF;
     const T* vs = Vs + cur * C::VBUF;
+    const char* stage = smem + (blk % C::NS) * C::STAGE;   // DMA
     const int k0 = blk * BN;
     // A wave whose rows all precede this block's first key (causal) sees an
     // empty key set here: its summary is the empty state, a no-op merge.
@@ -321,8 +451,12 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
           }
           #pragma unroll
           for (int c = 0; c < C::KCH; ++c) {
-            const vec kf = *reinterpret_cast<const vec*>(
-                &ks[(kb * 32 + l32) * C::KPAD + c * 2 * VEC + g * VEC]);
+            vec kf;
+            if constexpr (DMA)
+              kf = *reinterpret_cast<const vec*>(stage + kb * 32 * C::KRB + kro[c]);
+            else
+              kf = *reinterpret_cast<const vec*>(
+                  &ks[(kb * 32 + l32) * C::KPAD + c * 2 * VEC + g * VEC]);
             mfma_chunk(s[kb], kf, qf[c]);
           }
         }
@@ -495,9 +629,16 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
           for (int st = 0; st < 2; ++st)
             #pragma unroll
             for (int d = 0; d < C::NDV; ++d) {
-              const T* v0 = &vs[(kb * 32 + 16 * st + srow) * C::VROW + d * 32 + scol];
-              const vec4 lo = lds_read_tr4<T>(v0);
-              const vec4 hi = lds_read_tr4<T>(v0 + 8 * C::VROW);
+              vec4 lo, hi;
+              if constexpr (DMA) {
+                const char* v0 = stage + (kb * 32 + 16 * st) * C::VRB + vro[d];
+                lo = lds_read_tr4<T>(reinterpret_cast<const T*>(v0));
+                hi = lds_read_tr4<T>(reinterpret_cast<const T*>(v0 + 8 * C::VRB));
+              } else {
+                const T* v0 = &vs[(kb * 32 + 16 * st + srow) * C::VROW + d * 32 + scol];
+                lo = lds_read_tr4<T>(v0);
+                hi = lds_read_tr4<T>(v0 + 8 * C::VROW);
+              }
               const vec va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
               mfma_chunk(o[d], va, pb[kb][st]);
             }
@@ -519,9 +660,11 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
         }
       }
     }
-    if (blk + 1 < nblk) store_kv(cur ^ 1);  // next block into the other buffer
-    __syncthreads();
-    if (blk + 2 < nblk) load_kv(blk + 2);   // in flight during the next block
+    if constexpr (!DMA) {
+      if (blk + 1 < nblk) store_kv(cur ^ 1);  // next block into the other buffer
+      __syncthreads();
+      if (blk + 2 < nblk) load_kv(blk + 2);   // in flight during the next block
+    }
   }
 
   // ---- finalise: z / l, store into the concatenation --------------------------

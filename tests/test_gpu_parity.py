@@ -426,32 +426,34 @@ def test_bf16_forward_ragged_shapes_and_unaligned_w_o(shape, wo_offset):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("row_stats", [False, True])
-def test_attn_core_f16_late_score_jumps(row_stats):
+def test_attn_core_f16_late_score_jumps(row_stats, d):
     """Scores that jump far above every earlier key's score, late in the row.
 
     Feature 0 of every query is 4; keys 200 and 450 carry 40 and 300 there
-    (scale 1/8): their scores exceed the earlier keys' by about 20 and 150
-    nats.  The fp16 fast path keeps its running state at a deferred shift;
+    (times sqrt(d/64), scale 1/sqrt(d)): their scores exceed the earlier
+    keys' by about 20 and 150 nats.  The fp16 fast path keeps its running state at a deferred shift;
     the first jump is past its threshold (2^8 in base 2) and forces a move of
     the shift, and the second overflows a weight computed at the old shift,
     so the block is redone at the new one.  Both must match the oracle
     (causal mask: the jumps reach rows 200.. and 450.. only)."""
-    B, h, n, d = 1, 2, 600, 64
+    B, h, n = 1, 2, 600
     Qh, Kh, Vh = make_heads(B, h, n, n, d, d, "f32", seed=21)
     Qh[..., 0] = 4.0
     Kh[..., 0] *= 0.1
-    Kh[:, :, 200, 0] = 40.0
-    Kh[:, :, 450, 0] = 300.0
+    Kh[:, :, 200, 0] = 40.0 * math.sqrt(d / 64)      # same jumps at scale 1/sqrt(d)
+    Kh[:, :, 450, 0] = 300.0 * math.sqrt(d / 64)
     to16 = lambda a: torch.from_numpy(a).to(DEV).to(torch.float16)
     Qh16, Kh16, Vh16 = (t.float().cpu().numpy() for t in (to16(Qh), to16(Kh), to16(Vh)))
-    ref = attn_core_ref(Qh16, Kh16, Vh16, 0.125, allowed_set(B, n, n, causal=True))
+    c = 1.0 / math.sqrt(d)
+    ref = attn_core_ref(Qh16, Kh16, Vh16, c, allowed_set(B, n, n, causal=True))
     rm = rl = None
     if row_stats:
         rm = torch.empty((B, h, n), dtype=torch.float32, device=DEV)
         rl = torch.empty_like(rm)
-    _say(f"[late jumps] row_stats={row_stats}")
-    Z = mha.attn_core(to16(Qh), to16(Kh), to16(Vh), scale=0.125, causal=True, row_m=rm,
+    _say(f"[late jumps] d={d} row_stats={row_stats}")
+    Z = mha.attn_core(to16(Qh), to16(Kh), to16(Vh), scale=c, causal=True, row_m=rm,
                       row_l=rl)
     torch.cuda.synchronize()
     Zc = Z.cpu().numpy()
@@ -465,3 +467,33 @@ def test_attn_core_f16_late_score_jumps(row_stats):
     if row_stats:
         np.testing.assert_allclose(rm.cpu().numpy(), ref["m"], rtol=2e-3, atol=2e-3)
         np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-2)
+
+
+@pytest.mark.parametrize("dims", [(128, 128), (64, 96), (64, 64)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_attn_core_f16_ragged_blocks(dims, causal):
+    """fp16 heads, no row statistics, key and query counts that are not
+    multiples of the 64-key block or the 128-row tile, key padding with
+    lengths down to 1: the last K/V block reads past n_k (clamped rows,
+    masked) and some rows see a single allowed key."""
+    d_h, d_vh = dims
+    B, h, n = 3, 2, 301
+    Qh, Kh, Vh = make_heads(B, h, n, n, d_h, d_vh, "f32", seed=23)
+    key_len = np.array([301, 65, 1], dtype=np.int32)
+    to16 = lambda a: torch.from_numpy(a).to(DEV).to(torch.float16)
+    Qh16, Kh16, Vh16 = (t.float().cpu().numpy() for t in (to16(Qh), to16(Kh), to16(Vh)))
+    c = 1.0 / math.sqrt(d_h)
+    allow = allowed_set(B, n, n, causal=causal, key_len=key_len)
+    ref = attn_core_ref(Qh16, Kh16, Vh16, c, allow)["Z"]
+    _say(f"[ragged blocks] d_h={d_h} d_vh={d_vh} causal={causal}")
+    Z = mha.attn_core(to16(Qh), to16(Kh), to16(Vh), scale=c, causal=causal,
+                      key_len=torch.from_numpy(key_len).to(DEV))
+    torch.cuda.synchronize()
+    err = _rel_err(Z.cpu().numpy(), ref)
+    _say(f"  Z err {err:.3e}")
+    assert err <= 1e-2
+    # batch item 2 allows key 0 only: every row is exactly v_0 (weight 1)
+    Zc = Z.float().cpu().numpy()
+    for r in range(h):
+        np.testing.assert_array_equal(Zc[2, :, r * d_vh:(r + 1) * d_vh],
+                                      np.broadcast_to(Vh16[2, r, 0], (n, d_vh)))

@@ -2,6 +2,7 @@
 #pragma once
 
 #include "attn.hpp"
+#include "attn_pipe.hpp"
 
 namespace mha {
 
@@ -10,6 +11,15 @@ namespace mha {
 #endif
 #ifndef MHA_ATTN_BN
 #define MHA_ATTN_BN 64
+#endif
+#ifndef MHA_ATTN_PIPE
+#define MHA_ATTN_PIPE 1
+#endif
+#ifndef MHA_PIPE_NS
+#define MHA_PIPE_NS 4
+#endif
+#ifndef MHA_PIPE_OCC
+#define MHA_PIPE_OCC 2
 #endif
 
 
@@ -37,8 +47,18 @@ hipError_t launch_attn_fixed(AttnParams p, hipStream_t stream) {
   const bool stats = p.row_m != nullptr || p.row_l != nullptr;
   if constexpr (lazy && sizeof(T) == 2) {
     if (fast && !stats) {
-      hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, lazy, occ, false>),
-                         dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
+      // The software-pipelined kernel (two waves per SIMD) wins where a block
+      // carries more matrix work per weight: value rows of 96+ or heads of
+      // 128 (measured 30 % and 10 % faster); for narrower heads three
+      // unpipelined waves per SIMD are faster (measured 7 %).
+      if constexpr (MHA_ATTN_PIPE && (DV >= 96 || DH >= 128)) {
+        static_assert(WAVES == 4 && BN == 64, "the pipelined kernel's tile");
+        hipLaunchKernelGGL((attn_pipe_kernel<T, DH, DV, MHA_PIPE_NS, MHA_PIPE_OCC>),
+                           dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
+      } else {
+        hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, lazy, occ, false>),
+                           dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
+      }
       return hipGetLastError();
     }
   }

@@ -32,8 +32,9 @@ if ROOT not in sys.path:
 METRIC = "MHA fwd TFLOP/s and % bf16 MFMA peak (T=4096, h=16, d_k=64, causal)"
 # sources that define the attention kernel; a traffic measurement is only
 # reported while their hash matches the one recorded with it
-ATTN_SOURCES = ["transformer_head_self_amd/csrc/attn.hpp", "transformer_head_self_amd/csrc/common.hpp",
-                "transformer_head_self_amd/csrc/attn_launch.hpp", "transformer_head_self_amd/csrc/internal.hpp"]
+ATTN_SOURCES = ["transformer_head_self_amd/csrc/attn.hpp", "transformer_head_self_amd/csrc/attn_pipe.hpp",
+                "transformer_head_self_amd/csrc/attn_launch.hpp", "transformer_head_self_amd/csrc/common.hpp",
+                "transformer_head_self_amd/csrc/internal.hpp", "transformer_head_self_amd/csrc/lds_dma.hpp"]
 
 
 def attn_source_hash():

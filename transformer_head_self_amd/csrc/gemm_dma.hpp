@@ -197,7 +197,12 @@ void gemm_dma_kernel(GemmBatch batch) {
   // registers across the whole k loop.
   int m0w = m0 + wm * 128, n0w = n0 + wn * 64, lane_e = lane;
   asm volatile("" : "+s"(m0w), "+s"(n0w), "+v"(lane_e));
-  store_wave_block_any(P, acc, m0w, n0w, lane_e >> 5, lane_e & 31);
+  // every wave has finished reading the stage buffers before they are reused
+  // for the staged stores (18 KB per wave of the 72 KB)
+  __syncthreads();
+  static_assert(C::LDS >= 4 * 128 * 144, "staging space for four waves");
+  store_wave_block_any_lds(P, acc, m0w, n0w, lane_e >> 5, lane_e & 31,
+                           smem + wave * (128 * 144));
 }
 
 }  // namespace mha

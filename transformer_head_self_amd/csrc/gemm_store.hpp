@@ -63,6 +63,89 @@ __device__ __forceinline__ void store_wave_block(const GemmProblem& P, const flo
   }
 }
 
+// The same stores staged through LDS so that every store instruction writes
+// whole row segments: the wave writes its block into its own LDS region
+// (rows padded by 16 bytes: the 8-byte writes of 32 rows and the 16-byte
+// row reads both spread evenly over the banks), then reads back 16
+// consecutive bytes per lane and stores them: 8 rows x 128 bytes per
+// instruction for 2-byte outputs, 4 rows x 256 bytes for fp32 (two passes
+// of 64 rows).  With a head width of 64 a wave's block is one contiguous
+// 16 KB run of the head-major array.  `lds` is this wave's region of at
+// least 128 x 144 bytes (18 KB), free for the wave's exclusive use; LDS
+// operations of one wave complete in order, so no barrier is needed between
+// the writes and the reads.  Conditions (checked by lds_store_ok): 2-byte
+// head-major outputs need a head width that is a multiple of 8; row-major
+// outputs need 16-byte aligned rows.
+template <int DT, bool HEADS>
+__device__ __forceinline__ void store_wave_block_lds(const GemmProblem& P,
+                                                     const floatx16 (&acc)[2][4], int m0w,
+                                                     int n0w, int g, int l32, char* lds) {
+  constexpr int ES = DT == kF32 ? 4 : 2;
+  constexpr int ROWB = 64 * ES + 16;          // padded LDS row
+  constexpr int ROWS = DT == kF32 ? 64 : 128; // rows per pass
+  constexpr int LPR = 64 * ES / 16;           // lanes per row in the read-back
+  constexpr int RPI = 64 / LPR;               // rows per store instruction
+  const int lane = g * 32 + l32;
+  const int M = P.M, N = P.N;
+  #pragma unroll
+  for (int pass = 0; pass < 128 / ROWS; ++pass) {
+    // registers -> LDS: row (32 i + l32) - pass*ROWS, columns 32 j + 8 a + 4 g
+    #pragma unroll
+    for (int ii = 0; ii < ROWS / 32; ++ii) {
+      const int i = pass * (ROWS / 32) + ii;
+      #pragma unroll
+      for (int j = 0; j < 2; ++j)
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          char* dst = lds + (ii * 32 + l32) * ROWB + (32 * j + 8 * a + 4 * g) * ES;
+          const float v0 = acc[j][i][4 * a], v1 = acc[j][i][4 * a + 1];
+          const float v2 = acc[j][i][4 * a + 2], v3 = acc[j][i][4 * a + 3];
+          if constexpr (DT == kF32) {
+            *reinterpret_cast<floatx4*>(dst) = floatx4{v0, v1, v2, v3};
+          } else if constexpr (DT == kBF16) {
+            *reinterpret_cast<bf16x4*>(dst) = Cvt<bf16>::four(v0, v1, v2, v3);
+          } else {
+            *reinterpret_cast<f16x4*>(dst) = Cvt<f16>::four(v0, v1, v2, v3);
+          }
+        }
+    }
+    // LDS -> global: lane covers row q / LPR of each group, 16 bytes at
+    // column (q % LPR) * 16 / ES
+    const int rq = lane / LPR, cq = (lane % LPR) * (16 / ES);
+    const int n = n0w + cq;
+    size_t coff = 0;
+    if constexpr (HEADS) {
+      const int r = (int)fastdiv((uint32_t)n, P.dh_div);
+      coff = (size_t)r * P.ntok * P.dh + (n - r * P.dh);
+    } else {
+      coff = (size_t)n;
+    }
+    #pragma unroll
+    for (int k = 0; k < ROWS / RPI; ++k) {
+      const int row = k * RPI + rq;
+      const int m = m0w + pass * ROWS + row;
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + row * ROWB + cq * ES);
+      if (m < M && n < N) {
+        size_t roff;
+        if constexpr (HEADS) {
+          const int bb = (int)fastdiv((uint32_t)m, P.ntok_div);
+          const int t = m - bb * P.ntok;
+          roff = ((size_t)bb * P.heads * P.ntok + t) * P.dh;
+        } else {
+          roff = (size_t)m * N;
+        }
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(P.C) + (roff + coff) * ES) = v;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ bool lds_store_ok(const GemmProblem& P) {
+  const int es = P.out_dtype == kF32 ? 4 : 2;
+  if (P.epilogue == kHeads) return es == 4 || (P.dh % 8) == 0;
+  return P.vec_c && ((long long)P.N * es) % 16 == 0;
+}
+
 // Dispatch on the problem's output layout and element type once, outside
 // the unrolled stores, so the accumulators stay in registers.
 __device__ __forceinline__ void store_wave_block_any(const GemmProblem& P,
@@ -76,6 +159,29 @@ __device__ __forceinline__ void store_wave_block_any(const GemmProblem& P,
     if (P.out_dtype == kF32) store_wave_block<kF32, false>(P, acc, m0w, n0w, g, l32);
     else if (P.out_dtype == kBF16) store_wave_block<kBF16, false>(P, acc, m0w, n0w, g, l32);
     else store_wave_block<kF16, false>(P, acc, m0w, n0w, g, l32);
+  }
+}
+
+}  // namespace mha
+
+namespace mha {
+
+// As store_wave_block_any, staged through `lds` when lds_store_ok(P).
+__device__ __forceinline__ void store_wave_block_any_lds(const GemmProblem& P,
+                                                         const floatx16 (&acc)[2][4], int m0w,
+                                                         int n0w, int g, int l32, char* lds) {
+  if (!lds_store_ok(P)) {
+    store_wave_block_any(P, acc, m0w, n0w, g, l32);
+    return;
+  }
+  if (P.epilogue == kHeads) {
+    if (P.out_dtype == kF32) store_wave_block_lds<kF32, true>(P, acc, m0w, n0w, g, l32, lds);
+    else if (P.out_dtype == kBF16) store_wave_block_lds<kBF16, true>(P, acc, m0w, n0w, g, l32, lds);
+    else store_wave_block_lds<kF16, true>(P, acc, m0w, n0w, g, l32, lds);
+  } else {
+    if (P.out_dtype == kF32) store_wave_block_lds<kF32, false>(P, acc, m0w, n0w, g, l32, lds);
+    else if (P.out_dtype == kBF16) store_wave_block_lds<kBF16, false>(P, acc, m0w, n0w, g, l32, lds);
+    else store_wave_block_lds<kF16, false>(P, acc, m0w, n0w, g, l32, lds);
   }
 }
 

@@ -399,6 +399,9 @@ def test_bf16_output_dtype():
     dict(B=3, n_q=45, n_k=77, d_q=40, d_k=24, d_v=56, h=3, d_h=8, d_vh=12, d_o=37),
     # K3 on the direct-to-LDS kernel: h*d_vh = 64, d_o = 200 (ragged column tile)
     dict(B=2, n_q=130, n_k=130, d_q=64, d_k=64, d_v=64, h=4, d_h=16, d_vh=16, d_o=200),
+    # K1 and K3 on the 256x256 direct-to-LDS kernel (every N a multiple of 256)
+    # with 300 and 2 x 300 rows (ragged row tiles)
+    dict(B=2, n_q=300, n_k=300, d_q=256, d_k=128, d_v=192, h=4, d_h=64, d_vh=64, d_o=256),
 ])
 @pytest.mark.parametrize("wo_offset", [0, 1, 3])
 def test_bf16_forward_ragged_shapes_and_unaligned_w_o(shape, wo_offset):

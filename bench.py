@@ -62,6 +62,9 @@ def parse():
                          "(three times) and exit; calibrates the HBM byte counters")
     ap.add_argument("--print-source-hash", action="store_true",
                     help="print the hash of the attention kernel sources and exit")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the key-split attention core on a decode step instead "
+                         "(one query row per item and head against 32768 cached keys)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters (optional)")
     return ap.parse_args()
@@ -107,6 +110,61 @@ def cpu_baseline(w, x):
                       f"matrix per head, no causal skipping), FLOPs counted as for the GPU"}
 
 
+DECODE = dict(B=8, h=16, n_k=32768, d=64)
+
+
+def decode_bench(args, torch):
+    """Decode step: Qh [B,h,1,d] against a key/value cache Kh, Vh [B,h,n_k,d]
+    (fp16, the projections' output type), no mask.  Bound by HBM: the cache
+    is read once.  The unsplit kernel (one workgroup per item and head) is
+    timed beside the split form for comparison."""
+    import numpy as np
+    import transformer_head_self_amd as mha
+    from transformer_head_self_amd.inputs import make_heads
+    B, h, n_k, d = DECODE["B"], DECODE["h"], DECODE["n_k"], DECODE["d"]
+    dev = torch.device("cuda:0")
+    Qh, Kh, Vh = (torch.from_numpy(a).to(dev).to(torch.float16)
+                  for a in make_heads(B, h, 1, n_k, d, d, "f32", seed=50))
+    Z = torch.empty((B, 1, h * d), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream()
+    dims = mha.MhaDims(B=B, h=h, n_q=1, n_k=n_k, d_q=1, d_k=1, d_v=1, d_h=d, d_vh=d, d_o=1,
+                       scale=1 / math.sqrt(d), in_dtype=2, out_dtype=2, work_dtype=2)
+    ws = torch.empty(mha.attn_split_workspace_bytes(dims, 0), dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_split = timed(lambda: mha.attn_core_split(Qh, Kh, Vh, splits=0, out_dtype=torch.float16,
+                                                 Z=Z, workspace=ws, stream=stream))
+    ms_plain = timed(lambda: mha.attn_core(Qh, Kh, Vh, out_dtype=torch.float16, Z=Z,
+                                           stream=stream))
+    # algorithmic bytes: the cache once, the query rows, the output rows
+    nbytes = B * h * n_k * 2 * d * 2 + 2 * B * h * d * 2
+    gbs = nbytes / (ms_split * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "split-KV decode attention, HBM GB/s", "value": round(gbs, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_split, 5), "higher_is_better": True, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"decode-f16-B{B}-h{h}-nq1-nk{n_k}-d{d}",
+                   "splits": "auto", "workspace_bytes": int(ws.numel())},
+        "roofline": {"bound": "hbm", "kernel": "attn_fwd_kernel (split) + split_merge_kernel",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": nbytes},
+        "unsplit_ms": round(ms_plain, 5),
+        "unsplit_gbs": round(nbytes / (ms_plain * 1e-3) / 1e9, 1),
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -128,6 +186,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n * 4, "launches": 3}), flush=True)
+        return
+
+    if args.decode:
+        decode_bench(args, torch)
         return
 
     import transformer_head_self_amd as mha

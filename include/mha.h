@@ -60,7 +60,7 @@ typedef enum {
   MHA_ERR_DTYPE = -3,       /* unknown dtype, or an unsupported (in, work) pair      */
   MHA_ERR_MASK = -4,        /* bad mask flags, causal with n_q != n_k, missing data  */
   MHA_ERR_ALIGN = -5,       /* a pointer is not aligned to its element size          */
-  MHA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than mha_workspace_bytes()  */
+  MHA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the *_workspace_bytes() */
   MHA_ERR_UNSUPPORTED = -7, /* d_h or d_vh above the largest instantiated head width */
   MHA_ERR_LAUNCH = -8,      /* the HIP runtime reported an error at launch           */
   MHA_ERR_SCALE = -9        /* scale is not a finite number                          */
@@ -141,6 +141,27 @@ mha_status mha_forward(const mha_dims* d, const mha_mask* m,
 mha_status attn_core(const mha_dims* d, const mha_mask* m,
                      const void* Qh, const void* Kh, const void* Vh, void* Z,
                      float* row_m, float* row_l, void* stream);
+
+/* Key-split form of attn_core, for few query rows against many keys
+ * (decoding, short queries): the key axis is cut into partitions of whole
+ * 64-key blocks, each partition of each row is summarised separately (m, l,
+ * z) and the summaries are merged with the rule of page "Stable summary of
+ * an attention key block", Definition (merge; the empty state, m = -inf,
+ * l = 0, z = 0, is its identity), then z / l is written.  Same arguments,
+ * masks, layouts and results as attn_core (up to fp32 rounding order), plus:
+ *   splits     requested partitions, >= 0; 0 lets the library choose.  The
+ *              count used is ceil(n_k / P), P = ceil(n_k / splits) rounded
+ *              up to a multiple of 64 (at most 65536 partitions).
+ *   workspace  device scratch of at least attn_split_workspace_bytes(d,
+ *              splits) bytes, 256-byte aligned (hipMalloc's alignment):
+ *              the partitions' fp32 summaries m, l [S, B, h, n_q] and
+ *              z [S, B, h, n_q, d_vh].
+ * Two launches on `stream`: the partitions, then the merge. */
+size_t attn_split_workspace_bytes(const mha_dims* d, int32_t splits);
+mha_status attn_core_split(const mha_dims* d, const mha_mask* m,
+                           const void* Qh, const void* Kh, const void* Vh, void* Z,
+                           float* row_m, float* row_l, int32_t splits,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a status code (host memory, never freed). */
 const char* mha_status_string(int status);

@@ -200,3 +200,74 @@ def test_workspace_bytes_formula_and_monotonicity():
         bigger = _dims(**{f: getattr(_dims(), f) * 2})
         assert mha.mha_workspace_bytes(bigger) > base
     assert mha.mha_workspace_bytes(_dims(B=0)) == 0
+
+
+# ---- key-split form -------------------------------------------------------
+
+def _split(d, m=None, ptrs=None, splits=0, ws=FAKE, ws_bytes=1 << 40):
+    p = ptrs if ptrs is not None else [FAKE] * 4
+    return mha.lib().attn_core_split(
+        ctypes.byref(d) if d is not None else None, ctypes.byref(m) if m is not None else None,
+        p[0], p[1], p[2], p[3], None, None, splits, ws, ws_bytes, None)
+
+
+def _split_layout(d, splits):
+    """Partitions and workspace bytes the header specifies for explicit splits."""
+    P = -(-d.n_k // splits)
+    P = -(-P // 64) * 64
+    S = -(-d.n_k // P)
+    rows = d.B * d.h * d.n_q
+
+    def r256(x):
+        return (x + 255) // 256 * 256
+    return S, 2 * r256(S * rows * 4) + r256(S * rows * d.d_vh * 4)
+
+
+def test_split_workspace_bytes_explicit():
+    for B, h, n_q, n_k, d_vh, splits in ((1, 16, 1, 4096, 64, 8), (2, 3, 5, 1000, 40, 7),
+                                         (1, 1, 1, 65, 8, 100), (3, 2, 9, 64, 64, 1),
+                                         (1, 2, 3, 130, 128, 2)):
+        d = _dims(B=B, h=h, n_q=n_q, n_k=n_k, d_vh=d_vh)
+        S, need = _split_layout(d, splits)
+        assert 1 <= S <= splits
+        assert mha.attn_split_workspace_bytes(d, splits) == need
+    # 65 keys asked in 100 partitions: whole 64-key blocks, so two partitions
+    assert _split_layout(_dims(n_k=65), 100)[0] == 2
+
+
+def test_split_workspace_bytes_auto_is_one_of_the_explicit_layouts():
+    for B, h, n_q, n_k in ((1, 16, 1, 8192), (4, 16, 4096, 4096), (1, 1, 1, 100), (8, 8, 2, 300)):
+        d = _dims(B=B, h=h, n_q=n_q, n_k=n_k)
+        auto = mha.attn_split_workspace_bytes(d, 0)
+        options = {_split_layout(d, s)[1] for s in range(1, -(-n_k // 64) + 1)}
+        assert auto in options
+    # many query tiles already fill the chip: no split
+    d = _dims(B=4, h=16, n_q=4096, n_k=4096)
+    assert mha.attn_split_workspace_bytes(d, 0) == _split_layout(d, 1)[1]
+    # one query row against 8192 keys: many partitions of >= 256 keys
+    d = _dims(B=1, h=16, n_q=1, n_k=8192)
+    assert mha.attn_split_workspace_bytes(d, 0) == _split_layout(d, 32)[1]
+
+
+def test_split_argument_errors():
+    d = _dims()
+    need = mha.attn_split_workspace_bytes(d, 4)
+    assert need > 0
+    assert mha.attn_split_workspace_bytes(d, -1) == 0
+    assert mha.attn_split_workspace_bytes(None, 1) == 0
+    assert _split(d, splits=-1) == -2
+    assert _split(None) == -1
+    for i in range(4):
+        p = [FAKE] * 4
+        p[i] = None
+        assert _split(d, ptrs=p) == -1
+    assert _split(d, splits=4, ws_bytes=need - 1) == -6
+    assert _split(d, splits=4, ws=None) == -6
+    assert _split(d, splits=4, ws=FAKE + 64, ws_bytes=need) == -5
+    assert _split(_dims(d_vh=mha.lib().mha_max_head_dim() + 1)) == -7
+    assert _split(_dims(scale=float("inf"))) == -9
+    assert _split(_dims(n_q=3, n_k=4), MhaMask(flags=mha.MHA_MASK_CAUSAL)) == -4
+    # partition rows beyond 32-bit indexing
+    big = _dims(B=1, h=1, n_q=1 << 16, n_k=1 << 22)
+    assert mha.attn_split_workspace_bytes(big, 1 << 16) == 0
+    assert _split(big, splits=1 << 16) == -2

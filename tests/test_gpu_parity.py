@@ -500,3 +500,124 @@ def test_attn_core_f16_ragged_blocks(dims, causal):
     for r in range(h):
         np.testing.assert_array_equal(Zc[2, :, r * d_vh:(r + 1) * d_vh],
                                       np.broadcast_to(Vh16[2, r, 0], (n, d_vh)))
+
+
+# ---------------------------------------------------------------------------
+# key-split form (partitions of the key axis merged afterwards)
+# ---------------------------------------------------------------------------
+
+def _heads_dev(Qh, Kh, Vh, dt):
+    if dt == "f16":
+        to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(torch.float16)
+        t = [to(Qh), to(Kh), to(Vh)]
+        return t, [x.float().cpu().numpy() for x in t]
+    t = [_to_dev(Qh, dt), _to_dev(Kh, dt), _to_dev(Vh, dt)]
+    return t, [Qh, Kh, Vh]
+
+
+SPLIT_TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 1e-2}
+
+SPLIT_CASES = [
+    # dtype, B, h, n_q, n_k, d_h, d_vh, key_len, splits
+    ("bf16", 2, 4, 1, 5000, 64, 64, (5000, 777), 0),
+    ("bf16", 4, 2, 3, 4100, 128, 128, (4100, 1, 65, 3000), 7),
+    ("f16", 3, 2, 1, 2049, 64, 96, (2049, 64, 2000), 0),
+    ("f32", 2, 3, 5, 1500, 40, 24, (1500, 200), 4),
+    ("f32", 1, 2, 2, 300, 64, 64, None, 100),
+    ("bf16", 2, 2, 1, 640, 32, 32, None, 1),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_split_decode_matches_oracle(case):
+    """Few query rows against many (padded) keys, partitions of whole 64-key
+    blocks: some partitions of a padded item hold no allowed key (empty
+    state), and key_len 1 leaves one allowed key in the first partition."""
+    dt, B, h, n_q, n_k, d_h, d_vh, kl, splits = case
+    _say(f"[split decode] {case}")
+    Qh, Kh, Vh = make_heads(B, h, n_q, n_k, d_h, d_vh, "f32" if dt == "f16" else dt,
+                            seed=31 * n_k + n_q)
+    dev, host = _heads_dev(Qh, Kh, Vh, dt)
+    key_len = None if kl is None else np.array(kl[:B], dtype=np.int32)
+    c = 1.0 / math.sqrt(d_h)
+    ref = attn_core_ref(*host, c, allowed_set(B, n_q, n_k, key_len=key_len))
+    rm = torch.empty((B, h, n_q), device=DEV)
+    rl = torch.empty_like(rm)
+    Z = mha.attn_core_split(*dev, splits=splits, scale=c,
+                            key_len=None if key_len is None else torch.from_numpy(key_len).to(DEV),
+                            row_m=rm, row_l=rl)
+    torch.cuda.synchronize()
+    err = _rel_err(Z.cpu().numpy(), ref["Z"])
+    _say(f"  Z err {err:.3e}")
+    assert err <= SPLIT_TOL[dt]
+    np.testing.assert_allclose(rm.cpu().numpy(), ref["m"], rtol=0, atol=2e-3)
+    np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-5 if dt == "f32" else 4e-3)
+    if key_len is not None and 1 in kl[:B]:
+        b = list(kl[:B]).index(1)
+        Zc = Z.cpu().numpy()
+        for r in range(h):   # one allowed key: weight 1, the value itself
+            np.testing.assert_array_equal(Zc[b, :, r * d_vh:(r + 1) * d_vh],
+                                          np.broadcast_to(host[2][b, r, 0], (n_q, d_vh)))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_split_causal_and_bool_mask(dt):
+    """Causal square problem cut into 64-key partitions: for early rows every
+    later partition is empty; plus a general boolean mask."""
+    B, h, n = 2, 2, 300
+    _say(f"[split causal] {dt}")
+    Qh, Kh, Vh = make_heads(B, h, n, n, 64, 64, dt, seed=41)
+    c = 0.125
+    allow = allowed_set(B, n, n, causal=True)
+    ref = attn_core_ref(Qh, Kh, Vh, c, allow)
+    rm = torch.empty((B, h, n), device=DEV)
+    rl = torch.empty_like(rm)
+    dev = [_to_dev(Qh, dt), _to_dev(Kh, dt), _to_dev(Vh, dt)]
+    Z = mha.attn_core_split(*dev, splits=5, scale=c, causal=True, row_m=rm, row_l=rl)
+    torch.cuda.synchronize()
+    assert _rel_err(Z.cpu().numpy(), ref["Z"]) <= TOL[dt]
+    np.testing.assert_allclose(rm.cpu().numpy(), ref["m"], rtol=0, atol=1e-5)
+    np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-5 if dt == "f32" else 4e-3)
+    G = np.random.default_rng(42).random((B, n, n)) < 0.2
+    G[:, :, 299] = True
+    ref = attn_core_ref(Qh, Kh, Vh, c, allowed_set(B, n, n, allowed=G))["Z"]
+    Z = mha.attn_core_split(*dev, splits=3, scale=c, allowed=torch.from_numpy(G).to(DEV))
+    torch.cuda.synchronize()
+    assert _rel_err(Z.cpu().numpy(), ref) <= TOL[dt]
+
+
+def test_split_empty_row_and_agreement_with_unsplit():
+    """key_len = 0: NaN row, row_m = -inf, row_l = 0 (every partition empty).
+    Otherwise the split and unsplit forms agree to fp32 rounding."""
+    B, h, n_q, n_k = 2, 2, 4, 1000
+    Qh, Kh, Vh = make_heads(B, h, n_q, n_k, 64, 64, "f32", seed=43)
+    dev = [_to_dev(Qh, "f32"), _to_dev(Kh, "f32"), _to_dev(Vh, "f32")]
+    kl = torch.tensor([0, 999], dtype=torch.int32, device=DEV)
+    rm = torch.empty((B, h, n_q), device=DEV)
+    rl = torch.empty_like(rm)
+    Z = mha.attn_core_split(*dev, splits=6, key_len=kl, row_m=rm, row_l=rl)
+    Z1 = mha.attn_core(*dev, key_len=kl)
+    torch.cuda.synchronize()
+    Z, Z1 = Z.cpu().numpy(), Z1.cpu().numpy()
+    assert np.all(np.isnan(Z[0]))
+    assert np.all(rm.cpu().numpy()[0] == -np.inf) and np.all(rl.cpu().numpy()[0] == 0)
+    assert _rel_err(Z[1], Z1[1]) <= 1e-5
+
+
+def test_split_decode_full_size_sampled():
+    """A decode step at serving size: one query row per (item, head) against
+    32768 cached keys with ragged lengths, automatic partitioning, bf16 heads;
+    every row checked against the oracle (the oracle's cost is linear here)."""
+    B, h, n_k, d = 8, 16, 32768, 64
+    _say(f"[split full size] B={B} h={h} n_q=1 n_k={n_k} d={d}")
+    Qh, Kh, Vh = make_heads(B, h, 1, n_k, d, d, "bf16", seed=44)
+    key_len = np.random.default_rng(45).integers(1, n_k, size=B, endpoint=True).astype(np.int32)
+    key_len[0] = n_k
+    c = 1.0 / math.sqrt(d)
+    ref = attn_core_ref(Qh, Kh, Vh, c, allowed_set(B, 1, n_k, key_len=key_len))["Z"]
+    Z = mha.attn_core_split(_to_dev(Qh, "bf16"), _to_dev(Kh, "bf16"), _to_dev(Vh, "bf16"),
+                            scale=c, key_len=torch.from_numpy(key_len).to(DEV))
+    torch.cuda.synchronize()
+    err = _rel_err(Z.cpu().numpy(), ref)
+    _say(f"  Z err {err:.3e}")
+    assert err <= TOL["bf16"]

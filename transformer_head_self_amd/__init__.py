@@ -9,6 +9,9 @@ fallback, and every call raises if the library is missing or returns an error.
 Entry points (same names as the C ABI):
 * ``mha_forward``  projections, fused attention, concatenation, W^O.
 * ``attn_core``    fused attention on already projected heads.
+* ``attn_core_split``  the same with the key axis cut into partitions whose
+  summaries are merged afterwards (few query rows, many keys).
+* ``attn_split_workspace_bytes``.
 * ``mha_workspace_bytes``, ``mha_status_string``.
 """
 
@@ -19,7 +22,8 @@ import math
 import os
 
 __all__ = [
-    "MhaError", "MhaDims", "MhaMask", "lib", "mha_forward", "attn_core",
+    "MhaError", "MhaDims", "MhaMask", "lib", "mha_forward", "attn_core", "attn_core_split",
+    "attn_split_workspace_bytes",
     "mha_workspace_bytes", "mha_status_string", "MHA_F32", "MHA_BF16", "MHA_F16",
     "MHA_MASK_CAUSAL", "MHA_MASK_KEY_PADDING", "MHA_MASK_BOOL",
 ]
@@ -68,6 +72,11 @@ def lib():
         L.mha_forward.restype = ctypes.c_int
         L.attn_core.argtypes = [P(MhaDims), P(MhaMask), vp, vp, vp, vp, vp, vp, vp]
         L.attn_core.restype = ctypes.c_int
+        L.attn_split_workspace_bytes.argtypes = [P(MhaDims), ctypes.c_int32]
+        L.attn_split_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_core_split.argtypes = [P(MhaDims), P(MhaMask), vp, vp, vp, vp, vp, vp,
+                                      ctypes.c_int32, vp, ctypes.c_size_t, vp]
+        L.attn_core_split.restype = ctypes.c_int
         L.mha_status_string.argtypes = [ctypes.c_int]
         L.mha_status_string.restype = ctypes.c_char_p
         L.mha_max_head_dim.argtypes = []
@@ -185,20 +194,25 @@ def mha_forward(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, *, scale=None, causal
     return Y
 
 
-def attn_core(Qh, Kh, Vh, *, scale=None, causal=False, key_len=None, allowed=None,
-              out_dtype=None, Z=None, row_m=None, row_l=None, stream=None):
-    """Z [B, n_q, h*d_vh] from heads Qh [B,h,n_q,d_h], Kh [B,h,n_k,d_h], Vh [B,h,n_k,d_vh]."""
-    torch = _torch()
+def _core_dims(Qh, Kh, Vh, scale, out_dtype):
     B, h, n_q, d_h = Qh.shape
     n_k = Kh.shape[2]
     d_vh = Vh.shape[3]
     if Kh.dtype != Qh.dtype or Vh.dtype != Qh.dtype:
         raise TypeError("Qh, Kh and Vh must share one element type")
-    out_dtype = torch.float32 if out_dtype is None else out_dtype
-    dims = MhaDims(B=B, h=h, n_q=n_q, n_k=n_k, d_q=1, d_k=1, d_v=1, d_h=d_h, d_vh=d_vh, d_o=1,
+    return MhaDims(B=B, h=h, n_q=n_q, n_k=n_k, d_q=1, d_k=1, d_v=1, d_h=d_h, d_vh=d_vh, d_o=1,
                    scale=(1.0 / math.sqrt(d_h)) if scale is None else float(scale),
                    in_dtype=_dtype_code(Qh.dtype), out_dtype=_dtype_code(out_dtype),
                    work_dtype=_dtype_code(Qh.dtype))
+
+
+def attn_core(Qh, Kh, Vh, *, scale=None, causal=False, key_len=None, allowed=None,
+              out_dtype=None, Z=None, row_m=None, row_l=None, stream=None):
+    """Z [B, n_q, h*d_vh] from heads Qh [B,h,n_q,d_h], Kh [B,h,n_k,d_h], Vh [B,h,n_k,d_vh]."""
+    torch = _torch()
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    dims = _core_dims(Qh, Kh, Vh, scale, out_dtype)
+    B, h, n_q, n_k, d_vh = dims.B, dims.h, dims.n_q, dims.n_k, dims.d_vh
     m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Qh.device)
     if Z is None:
         Z = torch.empty((B, n_q, h * d_vh), dtype=out_dtype, device=Qh.device)
@@ -207,4 +221,33 @@ def attn_core(Qh, Kh, Vh, *, scale=None, causal=False, key_len=None, allowed=Non
     del keep
     if st != 0:
         raise MhaError(st, "attn_core")
+    return Z
+
+
+def attn_split_workspace_bytes(dims: MhaDims, splits=0):
+    return lib().attn_split_workspace_bytes(ctypes.byref(dims) if dims is not None else None,
+                                            int(splits))
+
+
+def attn_core_split(Qh, Kh, Vh, *, splits=0, scale=None, causal=False, key_len=None,
+                    allowed=None, out_dtype=None, Z=None, row_m=None, row_l=None,
+                    workspace=None, stream=None):
+    """attn_core with the key axis cut into partitions merged afterwards
+    (``splits`` partitions requested, 0 = library's choice)."""
+    torch = _torch()
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    dims = _core_dims(Qh, Kh, Vh, scale, out_dtype)
+    B, h, n_q, n_k, d_vh = dims.B, dims.h, dims.n_q, dims.n_k, dims.d_vh
+    m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Qh.device)
+    if Z is None:
+        Z = torch.empty((B, n_q, h * d_vh), dtype=out_dtype, device=Qh.device)
+    if workspace is None:
+        nbytes = attn_split_workspace_bytes(dims, splits)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=Qh.device)
+    st = lib().attn_core_split(ctypes.byref(dims), ctypes.byref(m), _ptr(Qh), _ptr(Kh),
+                               _ptr(Vh), _ptr(Z), _ptr(row_m), _ptr(row_l), int(splits),
+                               _ptr(workspace), workspace.numel(), _stream(stream))
+    del keep
+    if st != 0:
+        raise MhaError(st, "attn_core_split")
     return Z

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libmha.so")
 
-SOURCES = ["api.hip", "gemm.hip", "attn_bf16.hip", "attn_f16.hip", "attn_f32.hip"]
+SOURCES = ["api.hip", "gemm.hip", "attn_bf16.hip", "attn_f16.hip", "attn_f32.hip", "attn_merge.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -7,6 +7,8 @@
 // by W^O.  Review page "Multi-Head Attention", "The Complete Multi-Head
 // Operation": project, attend per head, concatenate, project once more.
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 #include <string.h>
 
@@ -18,6 +20,11 @@ hipError_t launch_attention_bf16(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attention_f16(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream);
 
+hipError_t launch_attention_split_bf16(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attention_split_f16(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attention_split_f32(const AttnParams& p, hipStream_t stream);
+hipError_t launch_split_merge(const AttnParams& p, hipStream_t stream);
+
 hipError_t launch_attention(const AttnParams& p, int elem_dtype, hipStream_t stream) {
   switch (elem_dtype) {
     case kBF16: return launch_attention_bf16(p, stream);
@@ -25,6 +32,18 @@ hipError_t launch_attention(const AttnParams& p, int elem_dtype, hipStream_t str
     case kF32: return launch_attention_f32(p, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_attention_split(const AttnParams& p, int elem_dtype, hipStream_t stream) {
+  hipError_t e;
+  switch (elem_dtype) {
+    case kBF16: e = launch_attention_split_bf16(p, stream); break;
+    case kF16: e = launch_attention_split_f16(p, stream); break;
+    case kF32: e = launch_attention_split_f32(p, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  return launch_split_merge(p, stream);
 }
 }  // namespace mha
 
@@ -98,6 +117,45 @@ void fill_mask(mha::AttnParams& p, const mha_mask* m) {
 struct Workspace {
   size_t q, k, v, z, total;
 };
+
+// Key partitions of the split form: `requested` > 0 asks for that many
+// (fewer if the keys run out: partitions are whole 64-key blocks); 0 lets the
+// library choose enough partitions for about 1024 workgroups (four per CU)
+// with at least 256 keys each.
+struct SplitPlan {
+  int splits, split_keys;
+  size_t m, l, z, total;   // workspace regions (bytes), 256-byte aligned
+};
+constexpr int kMaxSplits = 65536;
+
+SplitPlan split_plan(const mha_dims* d, int requested) {
+  SplitPlan sp;
+  const int64_t n_k = d->n_k;
+  int64_t want = requested;
+  if (want <= 0) {
+    const int64_t base = (int64_t)d->B * d->h * ((d->n_q + 127) / 128);
+    want = (1024 + base - 1) / base;
+    want = std::min<int64_t>(want, (n_k + 255) / 256);
+    if (want < 1) want = 1;
+  }
+  want = std::min<int64_t>(want, kMaxSplits);
+  int64_t keys = (n_k + want - 1) / want;
+  keys = (keys + 63) / 64 * 64;
+  sp.split_keys = (int)keys;
+  sp.splits = (int)((n_k + keys - 1) / keys);
+  const size_t rows = (size_t)d->B * d->h * d->n_q;
+  sp.m = 0;
+  sp.l = round256(sp.splits * rows * 4);
+  sp.z = sp.l + round256(sp.splits * rows * 4);
+  sp.total = sp.z + round256(sp.splits * rows * (size_t)d->d_vh * 4);
+  return sp;
+}
+
+// Partition rows (and so workgroups, at most one per partition row) index
+// with 32-bit integers.
+bool split_plan_fits(const mha_dims* d, const SplitPlan& sp) {
+  return (int64_t)sp.splits * d->B * d->h * d->n_q <= kIntMax;
+}
 
 Workspace carve(const mha_dims* d) {
   const size_t es = esize(d->work_dtype);
@@ -182,6 +240,44 @@ mha_status attn_core(const mha_dims* d, const mha_mask* m, const void* Qh, const
   attn_params(p, d, d->in_dtype, Qh, Kh, Vh, Z, d->out_dtype, row_m, row_l);
   fill_mask(p, m);
   if (mha::launch_attention(p, d->in_dtype, (hipStream_t)stream) != hipSuccess)
+    return MHA_ERR_LAUNCH;
+  return MHA_OK;
+}
+
+size_t attn_split_workspace_bytes(const mha_dims* d, int32_t splits) {
+  if (check_core_dims(d) != MHA_OK || splits < 0) return 0;
+  const SplitPlan sp = split_plan(d, splits);
+  if (!split_plan_fits(d, sp)) return 0;
+  return sp.total;
+}
+
+mha_status attn_core_split(const mha_dims* d, const mha_mask* m, const void* Qh, const void* Kh,
+                           const void* Vh, void* Z, float* row_m, float* row_l, int32_t splits,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  mha_status s = check_core_dims(d);
+  if (s != MHA_OK) return s;
+  if ((s = check_mask(d, m)) != MHA_OK) return s;
+  if (splits < 0) return MHA_ERR_DIM;
+  if (!Qh || !Kh || !Vh || !Z) return MHA_ERR_NULL;
+  const size_t ei = esize(d->in_dtype), eo = esize(d->out_dtype);
+  if (!aligned(Qh, ei) || !aligned(Kh, ei) || !aligned(Vh, ei) || !aligned(Z, eo) ||
+      !aligned(row_m, 4) || !aligned(row_l, 4))
+    return MHA_ERR_ALIGN;
+  const SplitPlan sp = split_plan(d, splits);
+  if (!split_plan_fits(d, sp)) return MHA_ERR_DIM;
+  if (!workspace || workspace_bytes < sp.total) return MHA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MHA_ERR_ALIGN;
+  mha::AttnParams p;
+  memset(&p, 0, sizeof(p));
+  attn_params(p, d, d->in_dtype, Qh, Kh, Vh, Z, d->out_dtype, row_m, row_l);
+  fill_mask(p, m);
+  char* ws = static_cast<char*>(workspace);
+  p.splits = sp.splits;
+  p.split_keys = sp.split_keys;
+  p.part_m = reinterpret_cast<float*>(ws + sp.m);
+  p.part_l = reinterpret_cast<float*>(ws + sp.l);
+  p.part_z = reinterpret_cast<float*>(ws + sp.z);
+  if (mha::launch_attention_split(p, d->in_dtype, (hipStream_t)stream) != hipSuccess)
     return MHA_ERR_LAUNCH;
   return MHA_OK;
 }

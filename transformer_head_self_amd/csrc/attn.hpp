@@ -150,10 +150,14 @@ static_assert(kLazyLimit == (float)(1 << (int)kLazyTau), "limit = 2^tau");
 // OCC: minimum waves per SIMD the register allocation must allow.
 // STATS: the caller wants the final (m, l) per row (deferred-shift variant:
 // the exact running maximum is tracked only then).
+// SPLIT: one key partition per workgroup; partial summaries are written
+// (p.part_m / part_l / part_z) instead of Z.  Uses the exact-shift merge: a
+// partition may hold no allowed key for some rows (empty state).
 template <typename T, int DH, int DV, int WAVES, int BN_, bool FAST, bool LAZY = false, int OCC = 1,
-          bool STATS = true>
+          bool STATS = true, bool SPLIT = false>
 __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p) {
   typedef AttnCfg<T, DH, DV, WAVES, BN_> C;
+  static_assert(!(SPLIT && LAZY), "a key partition may hold no allowed key for a row");
   static_assert(STATS || (LAZY && C::TR), "the block-sum trigger is for 2-byte elements");
   constexpr int NKB = C::NKB;
   typedef typename Elem<T>::vec vec;
@@ -181,7 +185,8 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   // on the same XCD when B*h is a multiple of 8, so its K/V stay in that
   // XCD's L2.  Causal: longest tiles (most keys) first.
   const int BH = p.B * p.h;
-  const int id = blockIdx.x;
+  const int sp = SPLIT ? (int)(blockIdx.x % (unsigned)p.splits) : 0;   // key partition
+  const int id = SPLIT ? (int)(blockIdx.x / (unsigned)p.splits) : (int)blockIdx.x;
   const int qt_rank = id / BH;
   const int bh = id - qt_rank * BH;
   const int qt = p.causal ? (p.num_q_tiles - 1 - qt_rank) : qt_rank;
@@ -196,7 +201,16 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   if (p.key_len) kvalid = min(kvalid, p.key_len[b]);
   int kend = kvalid;
   if (p.causal) kend = min(kend, q0 + C::QT);
-  const int nblk = kend > 0 ? (kend + BN - 1) / BN : 0;
+  // Key blocks [blk0, nblk) (absolute indices): all of [0, kend), or this
+  // workgroup's partition of it.
+  int blk0 = 0;
+  if constexpr (SPLIT) {
+    const int kbeg = sp * p.split_keys;
+    kend = min(kend, kbeg + p.split_keys);
+    blk0 = kbeg / BN;
+    if (kend < kbeg) kend = kbeg;
+  }
+  const int nblk = kend > blk0 * BN ? (kend + BN - 1) / BN : blk0;
 
   const T* Qb = reinterpret_cast<const T*>(p.Q) + (size_t)bh * p.n_q * p.ldq;
   const T* Kb = reinterpret_cast<const T*>(p.K) + (size_t)bh * p.n_k * p.ldk;
@@ -404,18 +418,18 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   }
 
   if constexpr (DMA) {
-    if (nblk > 0) issue_kv(0);
-    if (nblk > 1) issue_kv(1);
+    if (nblk > blk0) issue_kv(blk0);
+    if (nblk > blk0 + 1) issue_kv(blk0 + 1);
   } else {
-    if (nblk > 0) {
-      load_kv(0);
+    if (nblk > blk0) {
+      load_kv(blk0);
       store_kv(0);
     }
     __syncthreads();
-    if (nblk > 1) load_kv(1);
+    if (nblk > blk0 + 1) load_kv(blk0 + 1);
   }
 
-  for (int blk = 0; blk < nblk; ++blk) {
+  for (int blk = blk0; blk < nblk; ++blk) {
     if constexpr (DMA) {
       // block blk has landed once only block blk+1's loads are outstanding;
       // after the barrier no wave reads block blk-1, whose stage is refilled
@@ -425,7 +439,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       compiler_fence();
       if (blk + 2 < nblk) issue_kv(blk + 2);
     }
-    const int cur = blk & 1;
+    const int cur = (blk - blk0) & 1;   // register staging: buffer of this block
     const T* ks = Ks + cur * C::KBUF;
     const T* vs = Vs + cur * C::VBUF;
     const char* stage = smem + (blk % C::NS) * C::STAGE;   // DMA
@@ -669,6 +683,26 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
 
   // ---- finalise: z / l, store into the concatenation --------------------------
   float l_tot = half_sum(l_run);
+  if constexpr (SPLIT) {
+    // this partition's summary of each row: (m, l, z) at shift m, base 2
+    if (qi < p.n_q) {
+      const size_t pr = ((size_t)sp * BH + bh) * p.n_q + qi;
+      #pragma unroll
+      for (int d = 0; d < C::NDV; ++d) {
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int e0 = d * 32 + 8 * a + 4 * g;
+          store4(p.part_z, kF32, pr * p.d_vh + e0, (p.d_vh % 4) == 0, dvh - e0, o[d][4 * a],
+                 o[d][4 * a + 1], o[d][4 * a + 2], o[d][4 * a + 3]);
+        }
+      }
+      if (g == 0) {
+        p.part_m[pr] = m_run;
+        p.part_l[pr] = l_tot;
+      }
+    }
+    return;
+  }
   const float inv = 1.0f / l_tot;
   if constexpr (LAZY && STATS) {
     // l at the exact maximum: l* e^(mu - m)   (z / l is unchanged)

@@ -5,4 +5,7 @@ namespace mha {
 hipError_t launch_attention_bf16(const AttnParams& p, hipStream_t stream) {
   return launch_attn_typed<bf16>(p, stream);
 }
+hipError_t launch_attention_split_bf16(const AttnParams& p, hipStream_t stream) {
+  return launch_attn_split_typed<bf16>(p, stream);
+}
 }  // namespace mha

@@ -88,4 +88,43 @@ hipError_t launch_attn_typed(const AttnParams& p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+// Key-split form: one workgroup per (query tile, batch*head, key partition),
+// writing partial summaries (the merge launch follows in launch_attention_split).
+template <typename T, int DH, int DV>
+hipError_t launch_attn_split_fixed(AttnParams p, hipStream_t stream) {
+  constexpr int WAVES = MHA_ATTN_WAVES;
+  constexpr int BN = 64;
+  typedef AttnCfg<T, DH, DV, WAVES, BN> C;
+  p.num_q_tiles = (p.n_q + C::QT - 1) / C::QT;
+  const long long grid = (long long)p.num_q_tiles * p.B * p.h * p.splits;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 2147483647LL) return hipErrorInvalidValue;
+  const bool fast = p.d_h == DH && p.d_vh == DV && p.vec_q && p.vec_k && p.vec_v &&
+                    p.allowed == nullptr;
+  if (fast)
+    hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, false, 1, true, true>),
+                       dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, false, false, 1, true, true>),
+                       dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int DH>
+hipError_t launch_attn_split_dv(const AttnParams& p, hipStream_t stream) {
+  if (p.d_vh <= 32) return launch_attn_split_fixed<T, DH, 32>(p, stream);
+  if (p.d_vh <= 64) return launch_attn_split_fixed<T, DH, 64>(p, stream);
+  if (p.d_vh <= 96) return launch_attn_split_fixed<T, DH, 96>(p, stream);
+  if (p.d_vh <= 128) return launch_attn_split_fixed<T, DH, 128>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_attn_split_typed(const AttnParams& p, hipStream_t stream) {
+  if (p.d_h <= 32) return launch_attn_split_dv<T, 32>(p, stream);
+  if (p.d_h <= 64) return launch_attn_split_dv<T, 64>(p, stream);
+  if (p.d_h <= 128) return launch_attn_split_dv<T, 128>(p, stream);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace mha

@@ -64,11 +64,27 @@ struct AttnParams {
   int out_dtype;
   int vec_q, vec_k, vec_v, vec_z;
   int num_q_tiles;   // filled by the launcher
+  // Key-axis partitions (split launch only): partition sp covers keys
+  // [sp * split_keys, (sp + 1) * split_keys) and writes its rows' partial
+  // summaries instead of Z: part_m (maximum, base-2 units), part_l (the
+  // normaliser at that shift) [splits, B, h, n_q] and part_z (the weighted
+  // value sum at that shift) [splits, B, h, n_q, d_vh], all fp32; a row with
+  // no allowed key in a partition gets the empty state (-inf, 0, 0).
+  int splits;
+  int split_keys;    // a multiple of 64
+  float* part_m;
+  float* part_l;
+  float* part_z;
 };
 
 // elem_dtype: element type of Q, K, V (and of the softmax weights fed to
 // the value product).
 hipError_t launch_attention(const AttnParams& p, int elem_dtype, hipStream_t stream);
+
+// The key-split form: the partial-summary launch (p.splits partitions of
+// p.split_keys keys) followed by the merge launch that combines the
+// partitions' summaries and writes Z (and row_m / row_l).
+hipError_t launch_attention_split(const AttnParams& p, int elem_dtype, hipStream_t stream);
 
 // Largest head widths with an instantiated kernel.
 constexpr int kMaxHeadDim = 128;

@@ -22,8 +22,18 @@ What it computes, and from which passage
 * Page "Stable summary of an attention key block", Definition: allowed key
   sets are nonempty; the row maximum is the stabilising shift.
 
+* The same review page, "Parameter and Work Conventions" and "Audit Order":
+  projection biases are a convention to be stated; without them the layer
+  is the products above.  With them (here: optional vectors b_Q [h*d_h],
+  b_K [h*d_h], b_V [h*d_vh], b_O [d_o]) each product X W becomes X W + b,
+  the bias broadcast over rows, head r's block in entries r*d .. r*d+d-1.
+
 Readings of points the pages leave open (each is listed in the design doc):
 * masks are allowed sets (additive M in {0, -inf}); combined rules AND;
+* an additive score bias M may also be a general real matrix [B or 1, n_q,
+  n_k], added to the scaled scores c q.k (the review page's
+  softmax(Q K^T / sqrt(d_k) + M): M is not multiplied by the scale); its
+  -inf entries are forbidden keys, +inf and NaN are invalid;
 * key padding masks keys only, never whole query rows;
 * causal requires n_q == n_k and allows j <= i (0-based);
 * a row whose allowed set is empty violates the definition: EmptyRowError;
@@ -72,14 +82,15 @@ def allowed_set(B, n_q, n_k, causal=False, key_len=None, allowed=None):
     return A
 
 
-def project_separate(X, W, h, d):
-    """Per-head products X W^(r), r = 0..h-1, stacked as [B, h, n, d].
+def project_separate(X, W, h, d, bias=None):
+    """Per-head products X W^(r) (+ b^(r)), r = 0..h-1, stacked as [B, h, n, d].
 
     Page "Multi-head attention and self-attention", Definition: each head
     has its own projection matrix.  The combined matrix W [d_in, h*d] holds
     head r in columns r*d .. r*d+d-1 (review page, "Separate and Combined
     Projections"); here each head's block is sliced out and multiplied
-    on its own.
+    on its own.  An optional bias [h*d] is sliced the same way and added to
+    every row of the head's product.
     """
     X = _f64(X)
     W = _f64(W)
@@ -89,11 +100,13 @@ def project_separate(X, W, h, d):
         Wr = W[:, r * d:(r + 1) * d]
         for b in range(B):
             out[b, r] = X[b] @ Wr
+            if bias is not None:
+                out[b, r] += _f64(bias)[r * d:(r + 1) * d]
     return out
 
 
-def project_combined(X, W, h, d):
-    """One wide product, then reshape and transpose to [B, h, n, d].
+def project_combined(X, W, h, d, bias=None):
+    """One wide product (+ bias [h*d]), then reshape and transpose to [B, h, n, d].
 
     Review page "Multi-Head Attention", "Separate and Combined Projections":
     (B, T, h d) -> (B, T, h, d) -> (B, h, T, d).
@@ -102,6 +115,8 @@ def project_combined(X, W, h, d):
     W = _f64(W)
     B, n, _ = X.shape
     wide = X @ W                       # (B, n, h*d)
+    if bias is not None:
+        wide = wide + _f64(bias)[None, None, :]
     split = wide.reshape(B, n, h, d)   # reshape splits the feature axis
     return split.transpose(0, 2, 1, 3).copy()  # transpose swaps head and position
 
@@ -128,11 +143,23 @@ def masked_softmax_rows(S, allow):
     return A, m, l
 
 
-def attn_core_ref(Qh, Kh, Vh, scale, allow, keep_A=False):
+def _additive(add, B, n_q, n_k):
+    """The additive score bias as [B, n_q, n_k] float64 (None: all zeros)."""
+    if add is None:
+        return None
+    M = np.broadcast_to(_f64(add), (B, n_q, n_k))
+    if np.isnan(M).any() or np.isposinf(M).any():
+        raise ValueError("an additive score bias must be finite or -inf")
+    return M
+
+
+def attn_core_ref(Qh, Kh, Vh, scale, allow, keep_A=False, add=None):
     """Attention on projected heads; output in concatenated layout.
 
     Qh [B,h,n_q,d_h], Kh [B,h,n_k,d_h], Vh [B,h,n_k,d_vh];
-    allow [B,n_q,n_k] (one mask for every head).
+    allow [B,n_q,n_k] (one mask for every head); add: optional additive
+    score bias M [B or 1, n_q, n_k] (one for every head), added to the
+    scaled scores; its -inf entries are forbidden keys.
     Returns dict with Z [B, n_q, h*d_vh] (head r in columns r*d_vh..),
     m, l [B, h, n_q] (natural-log units), and A [B,h,n_q,n_k] if keep_A.
     """
@@ -144,10 +171,16 @@ def attn_core_ref(Qh, Kh, Vh, scale, allow, keep_A=False):
     m = np.empty((B, h, n_q))
     l = np.empty((B, h, n_q))
     A_all = np.empty((B, h, n_q, n_k)) if keep_A else None
+    M = _additive(add, B, n_q, n_k)
     for b in range(B):
+        allow_b = np.asarray(allow[b], dtype=bool)
+        if M is not None:
+            allow_b = allow_b & (M[b] > -np.inf)
         for r in range(h):
             S = scale * (Qh[b, r] @ Kh[b, r].T)          # scores, materialised
-            A, m[b, r], l[b, r] = masked_softmax_rows(S, allow[b])
+            if M is not None:
+                S = S + np.where(allow_b, M[b], 0.0)      # + M on the allowed entries
+            A, m[b, r], l[b, r] = masked_softmax_rows(S, allow_b)
             Z[b, :, r * d_vh:(r + 1) * d_vh] = A @ Vh[b, r]   # concat in head order
             if keep_A:
                 A_all[b, r] = A
@@ -158,24 +191,30 @@ def attn_core_ref(Qh, Kh, Vh, scale, allow, keep_A=False):
 
 
 def mha_ref(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, scale, allow,
-            projection="combined", keep_A=False):
+            projection="combined", keep_A=False, add=None, biases=None):
     """Full multi-head attention forward in float64.
 
     Q [B,n_q,d_q], K [B,n_k,d_k], V [B,n_k,d_v]; W_Q [d_q,h*d_h],
-    W_K [d_k,h*d_h], W_V [d_v,h*d_vh], W_O [h*d_vh,d_o]; no biases.
+    W_K [d_k,h*d_h], W_V [d_v,h*d_vh], W_O [h*d_vh,d_o].  ``biases``: None
+    (no biases) or a dict with any of b_Q [h*d_h], b_K [h*d_h], b_V [h*d_vh],
+    b_O [d_o].  ``add``: optional additive score bias M [B or 1, n_q, n_k].
     ``projection`` picks one of two independent projection code paths.
     Returns dict with Y [B,n_q,d_o], Z, m, l (and A if keep_A).
     """
+    bs = biases or {}
     proj = {"combined": project_combined, "separate": project_separate}[projection]
-    Qh = proj(Q, W_Q, h, d_h)
-    Kh = proj(K, W_K, h, d_h)
-    Vh = proj(V, W_V, h, d_vh)
-    out = attn_core_ref(Qh, Kh, Vh, scale, allow, keep_A=keep_A)
+    Qh = proj(Q, W_Q, h, d_h, bs.get("b_Q"))
+    Kh = proj(K, W_K, h, d_h, bs.get("b_K"))
+    Vh = proj(V, W_V, h, d_vh, bs.get("b_V"))
+    out = attn_core_ref(Qh, Kh, Vh, scale, allow, keep_A=keep_A, add=add)
     out["Y"] = out["Z"] @ _f64(W_O)                 # output projection
+    if bs.get("b_O") is not None:
+        out["Y"] = out["Y"] + _f64(bs["b_O"])[None, None, :]
     return out
 
 
-def mha_ref_rows(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, scale, allow, b, rows):
+def mha_ref_rows(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, scale, allow, b, rows,
+                 add=None, biases=None):
     """The same computation restricted to query rows ``rows`` of item ``b``.
 
     Keys and values of item b are projected in full; only the selected
@@ -184,13 +223,20 @@ def mha_ref_rows(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, scale, allow, b, row
     Z_rows [len(rows), h*d_vh], m_rows [h, len(rows)], l_rows [h, len(rows)]).
     """
     rows = np.asarray(rows)
+    bs = biases or {}
     Qb = _f64(Q[b])[rows][None]                        # (1, R, d_q)
     Kb = _f64(K[b])[None]
     Vb = _f64(V[b])[None]
-    Qh = project_combined(Qb, W_Q, h, d_h)
-    Kh = project_combined(Kb, W_K, h, d_h)
-    Vh = project_combined(Vb, W_V, h, d_vh)
+    Qh = project_combined(Qb, W_Q, h, d_h, bs.get("b_Q"))
+    Kh = project_combined(Kb, W_K, h, d_h, bs.get("b_K"))
+    Vh = project_combined(Vb, W_V, h, d_vh, bs.get("b_V"))
     sub_allow = np.asarray(allow[b])[rows][None]
-    out = attn_core_ref(Qh, Kh, Vh, scale, sub_allow)
+    sub_add = None
+    if add is not None:
+        A = _f64(add)
+        sub_add = (A[0] if A.shape[0] == 1 else A[b])[rows][None]
+    out = attn_core_ref(Qh, Kh, Vh, scale, sub_allow, add=sub_add)
     Y = out["Z"][0] @ _f64(W_O)
+    if bs.get("b_O") is not None:
+        Y = Y + _f64(bs["b_O"])[None, :]
     return Y, out["Z"][0], out["m"][0], out["l"][0]

@@ -14,7 +14,11 @@ Each pin comes from the pages or from mathematics the pages fix:
 * the merge identity of page "Stable summary of an attention key block",
   checked by brute force over every partition and bracketing of tiny key sets,
   in float64 and in 50-digit arithmetic;
-* an independent 50-digit scalar-loop implementation (oracle/bruteforce.py).
+* an independent 50-digit scalar-loop implementation (oracle/bruteforce.py);
+* for the additive score bias M and the projection biases (review page
+  "Multi-Head Attention": softmax(Q K^T / sqrt(d_k) + M); the bias
+  convention): the worked example driven by M or by b_Q, closed forms with
+  zero scale, the exact shift a key bias causes in the row maximum.
 """
 
 import itertools
@@ -507,7 +511,7 @@ def test_oracle_matches_50_digit_bruteforce(case):
 # the pins have teeth: plausible mistakes planted in the oracle are caught
 # --------------------------------------------------------------------------
 
-def _mut_reshape_without_transpose(X, W, h, d):
+def _mut_reshape_without_transpose(X, W, h, d, bias=None):
     X = np.asarray(X, np.float64)
     B, n, _ = X.shape
     return (X @ W).reshape(B, h, n, d)          # reshape where a transpose belongs
@@ -565,6 +569,211 @@ def test_planted_mistakes_fail_the_bruteforce_pin(monkeypatch, name, mutant):
                 out = mha_oracle.mha_ref(Q, K, V, W_Q, W_K, W_V, W_O, case["h"],
                                          case["d_h"], case["d_vh"], scale, allow)
                 bad = not (_rel(out["Y"], to_float(Yb)) < 1e-13)
+            except Exception:
+                bad = True
+        caught = caught or bad
+    assert caught, f"mutant {mutant.__name__} slipped past the brute-force pin"
+
+
+# --------------------------------------------------------------------------
+# additive score bias M and projection biases
+# --------------------------------------------------------------------------
+
+def test_additive_bias_levels_the_worked_example():
+    """Worked example: scaled scores (sqrt2, 0).  M = (0, sqrt2) is added
+    after the scale, so both scores become sqrt2: weights 1/2 each, output
+    (1/2, 1/2), row maximum sqrt2, l = 2.  Scaling M, or subtracting it,
+    would give other weights."""
+    g = _worked()["inputs"]
+    q = np.array(g["q1"])
+    Kh = np.array(g["k"])
+    Vh = np.array(g["v"])
+    M = np.array([[[0.0, math.sqrt(2.0)]]])
+    out = attn_core_ref(q[None, None, None, :], Kh[None, None], Vh[None, None],
+                        1.0 / math.sqrt(2.0), np.ones((1, 1, 2), bool), keep_A=True, add=M)
+    np.testing.assert_allclose(out["A"][0, 0, 0], [0.5, 0.5], atol=1e-15)
+    np.testing.assert_allclose(out["Z"][0, 0], [0.5, 0.5], atol=1e-15)
+    assert out["m"][0, 0, 0] == pytest.approx(math.sqrt(2.0), abs=1e-15)
+    assert out["l"][0, 0, 0] == pytest.approx(2.0, abs=1e-15)
+
+
+def test_additive_bias_zero_scale_gives_weighted_mean():
+    """c = 0 and M_ij = log w_ij: the weights are w_ij / sum_j w_ij."""
+    rng = _rng(60)
+    B, h, n_q, n_k, d = 2, 3, 5, 7, 4
+    Qh, Kh, Vh = (rng.normal(size=s) for s in ((B, h, n_q, d), (B, h, n_k, d), (B, h, n_k, d)))
+    Wt = rng.uniform(0.1, 3.0, size=(B, n_q, n_k))
+    out = attn_core_ref(Qh, Kh, Vh, 0.0, np.ones((B, n_q, n_k), bool), add=np.log(Wt))
+    for b in range(B):
+        for r in range(h):
+            ref = (Wt[b] @ Vh[b, r]) / Wt[b].sum(axis=1)[:, None]
+            np.testing.assert_allclose(out["Z"][b, :, r * d:(r + 1) * d], ref, rtol=1e-13)
+
+
+def test_additive_minus_inf_equals_boolean_mask_and_row_constant_shifts_m():
+    rng = _rng(61)
+    B, h, n, d = 2, 2, 6, 3
+    Qh, Kh, Vh = (rng.normal(size=(B, h, n, d)) for _ in range(3))
+    G = rng.random((B, n, n)) < 0.5
+    G[:, :, 2] = True
+    M = np.where(G, 0.0, -np.inf)
+    a = attn_core_ref(Qh, Kh, Vh, 0.4, allowed_set(B, n, n, allowed=G))
+    b = attn_core_ref(Qh, Kh, Vh, 0.4, np.ones((B, n, n), bool), add=M)
+    for k in ("Z", "m", "l"):
+        np.testing.assert_array_equal(a[k], b[k])
+    # a per-row constant: same output, the maximum moves by the constant
+    cst = rng.normal(size=(B, n))
+    c2 = attn_core_ref(Qh, Kh, Vh, 0.4, np.ones((B, n, n), bool),
+                       add=np.broadcast_to(cst[:, :, None], (B, n, n)))
+    c0 = attn_core_ref(Qh, Kh, Vh, 0.4, np.ones((B, n, n), bool))
+    np.testing.assert_allclose(c2["Z"], c0["Z"], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(c2["m"], c0["m"] + cst[:, None, :], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(c2["l"], c0["l"], rtol=1e-14)
+
+
+def test_additive_bias_rejects_nan_and_plus_inf():
+    Qh = np.zeros((1, 1, 2, 2))
+    for bad in (np.nan, np.inf):
+        with pytest.raises(ValueError):
+            attn_core_ref(Qh, Qh, Qh, 1.0, np.ones((1, 2, 2), bool),
+                          add=np.array([[[0.0, bad], [0.0, 0.0]]]))
+
+
+def test_query_bias_alone_drives_the_worked_example():
+    """W_Q = 0 and b_Q = the page's query: every row attends like q1, so
+    every output row is the printed (0.80, 0.20) pair; b_O then adds."""
+    g = _worked()
+    inp, pr = g["inputs"], g["printed"]
+    K = np.array([inp["k"]])
+    V = np.array([inp["v"]])
+    Q = _rng(62).normal(size=(1, 3, 2))
+    I = np.eye(2)
+    out = mha_ref(Q, K, V, np.zeros((2, 2)), I, I, I, 1, 2, 2, 1.0 / math.sqrt(2.0),
+                  np.ones((1, 3, 2), bool), biases={"b_Q": np.array(inp["q1"])})
+    for i in range(3):
+        assert np.all(np.abs(out["Y"][0, i] - pr["output"]["value"]) <= pr["output"]["abs_tol"])
+    b_O = np.array([10.0, -20.0])
+    out2 = mha_ref(Q, K, V, np.zeros((2, 2)), I, I, I, 1, 2, 2, 1.0 / math.sqrt(2.0),
+                   np.ones((1, 3, 2), bool), biases={"b_Q": np.array(inp["q1"]), "b_O": b_O})
+    np.testing.assert_allclose(out2["Y"], out["Y"] + b_O, rtol=0, atol=1e-13)
+
+
+def test_key_bias_moves_only_the_row_maximum():
+    """k_j + b_K adds c q_i . b_K to every score of row i: weights, output and
+    l are unchanged, m moves by exactly that amount."""
+    rng = _rng(63)
+    B, n, d_in, h, d = 2, 5, 4, 2, 3
+    Q, K, V = (rng.normal(size=(B, n, d_in)) for _ in range(3))
+    W_Q, W_K, W_V = (rng.normal(size=(d_in, h * d)) for _ in range(3))
+    W_O = rng.normal(size=(h * d, 4))
+    b_K = rng.normal(size=h * d)
+    allow = allowed_set(B, n, n, causal=True)
+    a = mha_ref(Q, K, V, W_Q, W_K, W_V, W_O, h, d, d, 0.6, allow)
+    b = mha_ref(Q, K, V, W_Q, W_K, W_V, W_O, h, d, d, 0.6, allow, biases={"b_K": b_K})
+    np.testing.assert_allclose(b["Y"], a["Y"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(b["l"], a["l"], rtol=1e-12)
+    Qh = project_separate(Q, W_Q, h, d)
+    shift = 0.6 * np.einsum("brid,rd->bri", Qh, b_K.reshape(h, d))
+    np.testing.assert_allclose(b["m"], a["m"] + shift, rtol=0, atol=1e-12)
+
+
+def test_value_and_output_bias_closed_form():
+    """W_Q = W_K = 0: every allowed weight is equal, so causal row i returns
+    (mean of x_0..x_i) W_V + b_V, then Y = Z W_O + b_O."""
+    rng = _rng(64)
+    B, n, d_in, h, d_vh, d_o = 2, 6, 3, 2, 2, 5
+    X = rng.normal(size=(B, n, d_in))
+    W_V = rng.normal(size=(d_in, h * d_vh))
+    W_O = rng.normal(size=(h * d_vh, d_o))
+    b_V = rng.normal(size=h * d_vh)
+    b_O = rng.normal(size=d_o)
+    Z0 = np.zeros((d_in, h * 2))
+    out = mha_ref(X, X, X, Z0, Z0, W_V, W_O, h, 2, d_vh, 0.5, allowed_set(B, n, n, causal=True),
+                  biases={"b_Q": rng.normal(size=h * 2), "b_K": rng.normal(size=h * 2),
+                          "b_V": b_V, "b_O": b_O})
+    prefix = np.cumsum(X, axis=1) / np.arange(1, n + 1)[None, :, None]
+    Z = prefix @ W_V + b_V
+    np.testing.assert_allclose(out["Y"], Z @ W_O + b_O, rtol=1e-12, atol=1e-13)
+
+
+BIAS_CASES = [
+    dict(seed=70, B=2, n=4, d_in=3, h=2, d_h=2, d_vh=3, d_o=2, causal=True, m_batch=1),
+    dict(seed=71, B=2, n=5, d_in=2, h=1, d_h=3, d_vh=2, d_o=3, causal=False, m_batch=2),
+]
+
+
+def _bias_inputs(c):
+    rng = _rng(c["seed"])
+    B, n, d_in, h = c["B"], c["n"], c["d_in"], c["h"]
+    X = rng.normal(size=(B, n, d_in))
+    W_Q = rng.normal(size=(d_in, h * c["d_h"]))
+    W_K = rng.normal(size=(d_in, h * c["d_h"]))
+    W_V = rng.normal(size=(d_in, h * c["d_vh"]))
+    W_O = rng.normal(size=(h * c["d_vh"], c["d_o"]))
+    bs = {"b_Q": rng.normal(size=h * c["d_h"]), "b_K": rng.normal(size=h * c["d_h"]),
+          "b_V": rng.normal(size=h * c["d_vh"]), "b_O": rng.normal(size=c["d_o"])}
+    M = rng.normal(size=(c["m_batch"], n, n)) * 2.0
+    M[..., 1, 0] = -np.inf
+    return X, W_Q, W_K, W_V, W_O, bs, M
+
+
+def _bias_brute(c, X, W_Q, W_K, W_V, W_O, bs, M):
+    Yb, Zb = mha_bruteforce(X.tolist(), X.tolist(), X.tolist(), W_Q.tolist(), W_K.tolist(),
+                            W_V.tolist(), W_O.tolist(), c["h"], c["d_h"], c["d_vh"], 0.7,
+                            causal=c["causal"], add=M.tolist(),
+                            biases={k: v.tolist() for k, v in bs.items()})
+    return to_float(Yb), to_float(Zb)
+
+
+@pytest.mark.parametrize("case", BIAS_CASES, ids=lambda c: f"seed{c['seed']}")
+def test_biases_match_50_digit_bruteforce(case):
+    X, W_Q, W_K, W_V, W_O, bs, M = _bias_inputs(case)
+    Yb, Zb = _bias_brute(case, X, W_Q, W_K, W_V, W_O, bs, M)
+    allow = allowed_set(case["B"], case["n"], case["n"], causal=case["causal"])
+    for proj in ("combined", "separate"):
+        out = mha_ref(X, X, X, W_Q, W_K, W_V, W_O, case["h"], case["d_h"], case["d_vh"], 0.7,
+                      allow, projection=proj, add=M, biases=bs)
+        assert _rel(out["Y"], Yb) < 1e-13
+        assert _rel(out["Z"], Zb) < 1e-13
+    Y1, Z1, _, _ = mha_ref_rows(X, X, X, W_Q, W_K, W_V, W_O, case["h"], case["d_h"],
+                                case["d_vh"], 0.7, allow, 1, [0, 2, 3], add=M, biases=bs)
+    np.testing.assert_allclose(Y1, np.array(Yb)[1][[0, 2, 3]], rtol=1e-12, atol=1e-13)
+
+
+def _mut_additive_subtracted(add, B, n_q, n_k):
+    return None if add is None else -np.broadcast_to(np.asarray(add, np.float64), (B, n_q, n_k))
+
+
+def _mut_combined_drops_bias(X, W, h, d, bias=None):
+    return project_combined(X, W, h, d)
+
+
+def _mut_combined_bias_head_reversed(X, W, h, d, bias=None):
+    if bias is not None:
+        bias = np.asarray(bias).reshape(h, d)[::-1].reshape(-1)
+    return project_combined(X, W, h, d, bias)
+
+
+BIAS_MUTANTS = [
+    ("_additive", _mut_additive_subtracted),
+    ("project_combined", _mut_combined_drops_bias),
+    ("project_combined", _mut_combined_bias_head_reversed),
+]
+
+
+@pytest.mark.parametrize("name,mutant", BIAS_MUTANTS, ids=[m[1].__name__ for m in BIAS_MUTANTS])
+def test_planted_bias_mistakes_fail_the_bruteforce_pin(monkeypatch, name, mutant):
+    caught = False
+    for case in BIAS_CASES:
+        X, W_Q, W_K, W_V, W_O, bs, M = _bias_inputs(case)
+        Yb, _ = _bias_brute(case, X, W_Q, W_K, W_V, W_O, bs, M)
+        allow = allowed_set(case["B"], case["n"], case["n"], causal=case["causal"])
+        with monkeypatch.context() as mp:
+            mp.setattr(mha_oracle, name, mutant)
+            try:
+                out = mha_oracle.mha_ref(X, X, X, W_Q, W_K, W_V, W_O, case["h"], case["d_h"],
+                                         case["d_vh"], 0.7, allow, add=M, biases=bs)
+                bad = not (_rel(out["Y"], Yb) < 1e-13)
             except Exception:
                 bad = True
         caught = caught or bad

@@ -77,13 +77,38 @@ typedef enum { MHA_F32 = 0, MHA_BF16 = 1, MHA_F16 = 2 } mha_dtype;
 #define MHA_MASK_CAUSAL 1u      /* key j allowed for query i only if j <= i (needs n_q == n_k) */
 #define MHA_MASK_KEY_PADDING 2u /* key j allowed only if j < key_len[b]                      */
 #define MHA_MASK_BOOL 4u        /* key j allowed only if allowed[b][i][j] != 0               */
+/* Additive score bias: review page "Multi-Head Attention", "The Complete
+ * Multi-Head Operation", softmax(Q K^T / sqrt(d_k) + M).  M is added to the
+ * scaled scores c q_i.k_j (it is not multiplied by c), one M for every head
+ * (page "Multi-head attention and self-attention", Definition: one chosen
+ * mask for every head).  Entries of -inf forbid the key
+ * (as a rule above would); +inf and NaN entries are not allowed (not
+ * checked: a device read).  A row whose allowed set ends up empty behaves
+ * as described under the device-side preconditions above. */
+#define MHA_MASK_ADDITIVE 8u    /* score_ij += add[b][i][j] (fp32)                          */
 
 typedef struct mha_mask {
   uint32_t flags;               /* OR of MHA_MASK_* (unknown bits: MHA_ERR_MASK)            */
   const int32_t* key_len;       /* [B] valid keys per batch item (KEY_PADDING), device      */
   const uint8_t* allowed;       /* [Bm][n_q][n_k], 1 = allowed (BOOL), device               */
   int64_t allowed_batch_stride; /* elements between items; 0 = one mask for the batch       */
+  const float* add;             /* [Ba][n_q][n_k] fp32 (ADDITIVE), device, 4-byte aligned   */
+  int64_t add_batch_stride;     /* elements between items; 0 = one bias for the batch       */
 } mha_mask;
+
+/* Projection biases (review page "Multi-Head Attention", "Parameter and
+ * Work Conventions" and "Audit Order": the bias convention is stated, not
+ * assumed).  Each pointer may be NULL (no bias for that product); a bias is
+ * added to every row of its product in fp32, before the product is rounded:
+ * Q W_Q + b_Q, K W_K + b_K, V W_V + b_V, Z W_O + b_O.  Element type
+ * in_dtype, device memory, head r's part of b_Q / b_K / b_V in entries
+ * r*d .. r*d+d-1 (the combined layout of the weights). */
+typedef struct mha_bias {
+  const void* b_Q;  /* [h*d_h]  */
+  const void* b_K;  /* [h*d_h]  */
+  const void* b_V;  /* [h*d_vh] */
+  const void* b_O;  /* [d_o]    */
+} mha_bias;
 
 /* Dimensions use the general definition's names (page "Multi-head attention
  * and self-attention", Definition). */
@@ -114,10 +139,11 @@ size_t mha_workspace_bytes(const mha_dims* d);
 
 /* Full forward pass.  Page "Multi-head attention and self-attention",
  * Definition; review page "Multi-Head Attention", "The Complete Multi-Head
- * Operation" (no biases).
+ * Operation".
  *   Q   [B, n_q, d_q]   K [B, n_k, d_k]   V [B, n_k, d_v]        (in_dtype)
  *   W_Q [d_q, h*d_h]    W_K [d_k, h*d_h]  W_V [d_v, h*d_vh]      (in_dtype)
  *   W_O [h*d_vh, d_o]                                            (in_dtype)
+ *   bias  optional projection biases (NULL: none; see mha_bias)
  *   Y   [B, n_q, d_o]                                            (out_dtype, written)
  *   row_m, row_l  optional [B, h, n_q] fp32 (may be NULL): the final row
  *        maximum of the scaled scores (natural-log units) and the shifted
@@ -127,7 +153,8 @@ size_t mha_workspace_bytes(const mha_dims* d);
 mha_status mha_forward(const mha_dims* d, const mha_mask* m,
                        const void* Q, const void* K, const void* V,
                        const void* W_Q, const void* W_K, const void* W_V,
-                       const void* W_O, void* Y, float* row_m, float* row_l,
+                       const void* W_O, const mha_bias* bias, void* Y,
+                       float* row_m, float* row_l,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Attention on projected heads, written in the concatenated layout.

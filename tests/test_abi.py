@@ -54,9 +54,11 @@ def test_struct_layout_matches_header():
     #include <stddef.h>
     #include "mha.h"
     int main(void) {
-      printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(mha_dims), offsetof(mha_dims, scale),
-             offsetof(mha_dims, out_dtype), offsetof(mha_dims, work_dtype), sizeof(mha_mask),
-             offsetof(mha_mask, key_len), offsetof(mha_mask, allowed_batch_stride));
+      printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(mha_dims),
+             offsetof(mha_dims, scale), offsetof(mha_dims, out_dtype),
+             offsetof(mha_dims, work_dtype), sizeof(mha_mask), offsetof(mha_mask, key_len),
+             offsetof(mha_mask, allowed_batch_stride), offsetof(mha_mask, add),
+             offsetof(mha_mask, add_batch_stride), sizeof(mha_bias), offsetof(mha_bias, b_O));
       return 0;
     }
     """
@@ -70,7 +72,9 @@ def test_struct_layout_matches_header():
                                                check=True).stdout.split()]
     assert vals == [ctypes.sizeof(MhaDims), MhaDims.scale.offset, MhaDims.out_dtype.offset,
                     MhaDims.work_dtype.offset, ctypes.sizeof(MhaMask), MhaMask.key_len.offset,
-                    MhaMask.allowed_batch_stride.offset]
+                    MhaMask.allowed_batch_stride.offset, MhaMask.add.offset,
+                    MhaMask.add_batch_stride.offset, ctypes.sizeof(mha.MhaBias),
+                    mha.MhaBias.b_O.offset]
 
 
 def _dims(**kw):
@@ -80,12 +84,13 @@ def _dims(**kw):
     return MhaDims(**base)
 
 
-def _fwd(d, m=None, ptrs=None, ws_bytes=1 << 30, ws=FAKE):
+def _fwd(d, m=None, ptrs=None, ws_bytes=1 << 30, ws=FAKE, bias=None):
     L = mha.lib()
     p = [FAKE] * 8 if ptrs is None else ptrs
     mp = ctypes.byref(m) if m is not None else None
-    return L.mha_forward(ctypes.byref(d) if d is not None else None, mp, *p, None, None, ws,
-                         ws_bytes, None)
+    bp = ctypes.byref(bias) if bias is not None else None
+    return L.mha_forward(ctypes.byref(d) if d is not None else None, mp, *p[:7], bp, p[7], None,
+                         None, ws, ws_bytes, None)
 
 
 def _core(d, m=None, ptrs=None):
@@ -162,6 +167,14 @@ def test_mask_descriptor_errors():
     assert _core(_dims(), m) == -4               # stride shorter than one mask plane
     m = MhaMask(flags=mha.MHA_MASK_KEY_PADDING, key_len=FAKE + 2)
     assert _core(_dims(), m) == -5               # int32 array misaligned
+    m = MhaMask(flags=mha.MHA_MASK_ADDITIVE)     # no additive bias
+    assert _core(_dims(), m) == -4
+    m = MhaMask(flags=mha.MHA_MASK_ADDITIVE, add=FAKE, add_batch_stride=64 * 64 - 1)
+    assert _fwd(_dims(), m) == -4                # stride shorter than one plane
+    m = MhaMask(flags=mha.MHA_MASK_ADDITIVE, add=FAKE + 2)
+    assert _core(_dims(), m) == -5               # fp32 array misaligned
+    m = MhaMask(flags=mha.MHA_MASK_ADDITIVE | 16, add=FAKE)
+    assert _core(_dims(), m) == -4               # unknown flag bit
 
 
 def test_misaligned_pointers():
@@ -175,6 +188,18 @@ def test_misaligned_pointers():
     q = [FAKE] * 4
     q[3] = FAKE + 1
     assert _core(_dims(), ptrs=q) == -5
+
+
+def test_projection_bias_alignment():
+    ok = mha.MhaBias(b_Q=FAKE, b_K=FAKE, b_V=FAKE, b_O=FAKE)
+    # every check passes except the missing workspace: the biases were accepted
+    assert _fwd(_dims(), bias=ok, ws=None) == -6
+    for f in ("b_Q", "b_K", "b_V", "b_O"):
+        b = mha.MhaBias(b_Q=FAKE, b_K=FAKE, b_V=FAKE, b_O=FAKE)
+        setattr(b, f, FAKE + 2)                  # fp32 bias must be 4-byte aligned
+        assert _fwd(_dims(), bias=b) == -5
+    b = mha.MhaBias(b_O=FAKE + 2)                # bf16 biases need 2-byte alignment only
+    assert _fwd(_dims(in_dtype=mha.MHA_BF16, work_dtype=mha.MHA_F16), bias=b, ws=None) == -6
 
 
 def test_workspace_checks():

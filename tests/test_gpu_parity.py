@@ -19,6 +19,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import transformer_head_self_amd as mha  # noqa: E402
+from transformer_head_self_amd.inputs import _cast  # noqa: E402
 from transformer_head_self_amd.inputs import (  # noqa: E402
     WORKLOADS, custom_workload, make_heads, make_inputs)
 from oracle import allowed_set, attn_core_ref, mha_ref, mha_ref_rows  # noqa: E402
@@ -621,3 +622,142 @@ def test_split_decode_full_size_sampled():
     err = _rel_err(Z.cpu().numpy(), ref)
     _say(f"  Z err {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# additive score bias M and projection biases
+# ---------------------------------------------------------------------------
+
+def _additive(rng, Bm, n_q, n_k, frac_forbidden=0.1):
+    M = rng.normal(size=(Bm, n_q, n_k)) * 2.0
+    M[rng.random(M.shape) < frac_forbidden] = -np.inf
+    M[:, :, 0] = rng.normal(size=(Bm, n_q))  # key 0 stays allowed in every row
+    return M.astype(np.float32)
+
+
+ADD_CASES = [
+    # dtype, B, h, n_q, n_k, d_h, d_vh, causal, key_len, batch-shared M
+    ("f32", 2, 3, 100, 333, 40, 24, False, None, False),
+    ("f32", 2, 2, 130, 130, 64, 64, True, (130, 7), True),
+    ("bf16", 2, 3, 130, 257, 64, 96, False, (257, 1), False),
+    ("bf16", 1, 2, 300, 300, 128, 128, True, None, True),
+    ("f16", 3, 2, 65, 200, 64, 64, False, (200, 64, 3), False),
+]
+
+
+@pytest.mark.parametrize("case", ADD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_additive_bias_core_matches_oracle(case):
+    dt, B, h, n_q, n_k, d_h, d_vh, causal, kl, shared = case
+    _say(f"[additive core] {case}")
+    Qh, Kh, Vh = make_heads(B, h, n_q, n_k, d_h, d_vh, "f32" if dt == "f16" else dt,
+                            seed=50 + n_q)
+    dev, host = _heads_dev(Qh, Kh, Vh, dt)
+    rng = np.random.default_rng(51 + n_k)
+    M = _additive(rng, 1 if shared else B, n_q, n_k)
+    key_len = None if kl is None else np.array(kl[:B], dtype=np.int32)
+    c = 1.0 / math.sqrt(d_h)
+    allow = allowed_set(B, n_q, n_k, causal=causal, key_len=key_len)
+    ref = attn_core_ref(*host, c, allow, add=M)
+    rm = torch.empty((B, h, n_q), device=DEV)
+    rl = torch.empty_like(rm)
+    kl_dev = None if key_len is None else torch.from_numpy(key_len).to(DEV)
+    Z = mha.attn_core(*dev, scale=c, causal=causal, key_len=kl_dev,
+                      add=torch.from_numpy(M).to(DEV), row_m=rm, row_l=rl)
+    torch.cuda.synchronize()
+    err = _rel_err(Z.cpu().numpy(), ref["Z"])
+    _say(f"  Z err {err:.3e}")
+    assert err <= SPLIT_TOL[dt]
+    np.testing.assert_allclose(rm.cpu().numpy(), ref["m"], rtol=0, atol=1e-4)
+    np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-5 if dt == "f32" else 4e-3)
+    # the key-split form takes the same bias
+    Zs = mha.attn_core_split(*dev, splits=3, scale=c, causal=causal, key_len=kl_dev,
+                             add=torch.from_numpy(M).to(DEV))
+    torch.cuda.synchronize()
+    assert _rel_err(Zs.cpu().numpy(), ref["Z"]) <= SPLIT_TOL[dt]
+
+
+def test_additive_bias_single_finite_entry_returns_that_value_exactly():
+    """M = -inf everywhere except key j(i) = 3 i mod n_k: row i returns v_j(i)."""
+    B, h, n = 2, 2, 96
+    for dt in ("f32", "bf16"):
+        Qh, Kh, Vh = make_heads(B, h, n, n, 64, 64, dt, seed=52)
+        M = np.full((1, n, n), -np.inf, np.float32)
+        j = (3 * np.arange(n)) % n
+        M[0, np.arange(n), j] = 1.5
+        Z = mha.attn_core(_to_dev(Qh, dt), _to_dev(Kh, dt), _to_dev(Vh, dt),
+                          add=torch.from_numpy(M).to(DEV))
+        torch.cuda.synchronize()
+        Z = Z.cpu().numpy()
+        for r in range(h):
+            np.testing.assert_array_equal(Z[:, :, r * 64:(r + 1) * 64],
+                                          Vh[:, r][:, j].astype(np.float32))
+
+
+FWD_BIAS_CASES = [
+    # workload kind, dtype, B, n_q, n_k, d_q, d_k, d_v, h, d_h, d_vh, d_o, causal, with M
+    ("self", "f32", 2, 96, 96, 64, 64, 64, 4, 16, 16, 64, True, True),
+    ("cross", "f32", 2, 70, 150, 48, 40, 56, 3, 24, 40, 72, False, False),
+    ("cross", "bf16", 2, 128, 320, 256, 192, 128, 4, 64, 96, 256, False, True),
+    ("self", "bf16", 1, 512, 512, 512, 512, 512, 8, 64, 64, 512, True, False),
+]
+
+
+@pytest.mark.parametrize("case", FWD_BIAS_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_forward_with_projection_biases(case):
+    kind, dt, B, n_q, n_k, d_q, d_k, d_v, h, d_h, d_vh, d_o, causal, with_add = case
+    _say(f"[forward biases] {case}")
+    rng = np.random.default_rng(53 + n_q)
+
+    Q = _cast(rng.standard_normal((B, n_q, d_q)), dt)
+    if kind == "self":
+        K = V = Q
+    else:
+        K = _cast(rng.standard_normal((B, n_k, d_k)), dt)
+        V = _cast(rng.standard_normal((B, n_k, d_v)), dt)
+    W = {k: _cast(rng.standard_normal(s) / math.sqrt(s[0]), dt) for k, s in
+         (("W_Q", (d_q, h * d_h)), ("W_K", (d_k, h * d_h)), ("W_V", (d_v, h * d_vh)),
+          ("W_O", (h * d_vh, d_o)))}
+    bs = {k: _cast(rng.standard_normal(n) * 0.5, dt) for k, n in
+          (("b_Q", h * d_h), ("b_K", h * d_h), ("b_V", h * d_vh), ("b_O", d_o))}
+    M = _additive(rng, B, n_q, n_k) if with_add else None
+    allow = allowed_set(B, n_q, n_k, causal=causal)
+    ref = mha_ref(Q, K, V, W["W_Q"], W["W_K"], W["W_V"], W["W_O"], h, d_h, d_vh,
+                  1.0 / math.sqrt(d_h), allow, add=M, biases=bs)
+    tQ = _to_dev(Q, dt)
+    tK, tV = (tQ, tQ) if kind == "self" else (_to_dev(K, dt), _to_dev(V, dt))
+    Y = mha.mha_forward(tQ, tK, tV, *(_to_dev(W[k], dt) for k in ("W_Q", "W_K", "W_V", "W_O")),
+                        h, d_h, d_vh, causal=causal,
+                        add=None if M is None else torch.from_numpy(M).to(DEV),
+                        **{k: _to_dev(v, dt) for k, v in bs.items()})
+    torch.cuda.synchronize()
+    err = _rel_err(Y.cpu().numpy(), ref["Y"])
+    _say(f"  Y err {err:.3e}")
+    assert err <= TOL[dt]
+    # without biases the result moves by far more than the tolerance
+    assert _rel_err(ref["Y"], mha_ref(Q, K, V, W["W_Q"], W["W_K"], W["W_V"], W["W_O"], h, d_h,
+                                      d_vh, 1.0 / math.sqrt(d_h), allow, add=M)["Y"]) > 10 * TOL[dt]
+
+
+def test_forward_biases_at_headline_size_sampled():
+    """Projection biases on the 4 x 4096-token causal bf16 workload (fast
+    attention path, 256x256 GEMM tiles), checked on sampled query rows."""
+    w = WORKLOADS["self-bf16-B4-T4096-dm1024-h16-dh64-causal"]
+    _say("[forward biases, full size] " + w.name)
+    x = make_inputs(w)
+    rng = np.random.default_rng(54)
+
+    bs = {k: _cast(rng.standard_normal(n) * 0.5, "bf16") for k, n in
+          (("b_Q", w.h * w.d_h), ("b_K", w.h * w.d_h), ("b_V", w.h * w.d_vh), ("b_O", w.d_o))}
+    Q = _to_dev(x["Q"], "bf16")
+    Wd = {k: _to_dev(x[k], "bf16") for k in ("W_Q", "W_K", "W_V", "W_O")}
+    Y = mha.mha_forward(Q, Q, Q, Wd["W_Q"], Wd["W_K"], Wd["W_V"], Wd["W_O"], w.h, w.d_h, w.d_vh,
+                        causal=True, **{k: _to_dev(v, "bf16") for k, v in bs.items()})
+    torch.cuda.synchronize()
+    Y = Y.cpu().numpy()
+    allow = _allow(w, x)
+    for b, rows in ((0, [0, 1, 777, 4095]), (3, [63, 64, 2048, 4000])):
+        Yr, _, _, _ = mha_ref_rows(x["Q"], x["Q"], x["Q"], x["W_Q"], x["W_K"], x["W_V"], x["W_O"],
+                                   w.h, w.d_h, w.d_vh, w.scale, allow, b, rows, biases=bs)
+        err = _rel_err(Y[b, rows], Yr)
+        _say(f"  item {b} rows {rows}: err {err:.3e}")
+        assert err <= TOL["bf16"]

@@ -22,16 +22,16 @@ import math
 import os
 
 __all__ = [
-    "MhaError", "MhaDims", "MhaMask", "lib", "mha_forward", "attn_core", "attn_core_split",
+    "MhaError", "MhaDims", "MhaMask", "MhaBias", "lib", "mha_forward", "attn_core", "attn_core_split",
     "attn_split_workspace_bytes",
     "mha_workspace_bytes", "mha_status_string", "MHA_F32", "MHA_BF16", "MHA_F16",
-    "MHA_MASK_CAUSAL", "MHA_MASK_KEY_PADDING", "MHA_MASK_BOOL",
+    "MHA_MASK_CAUSAL", "MHA_MASK_KEY_PADDING", "MHA_MASK_BOOL", "MHA_MASK_ADDITIVE",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmha.so")
 
 MHA_F32, MHA_BF16, MHA_F16 = 0, 1, 2
-MHA_MASK_CAUSAL, MHA_MASK_KEY_PADDING, MHA_MASK_BOOL = 1, 2, 4
+MHA_MASK_CAUSAL, MHA_MASK_KEY_PADDING, MHA_MASK_BOOL, MHA_MASK_ADDITIVE = 1, 2, 4, 8
 
 
 class MhaError(RuntimeError):
@@ -49,7 +49,13 @@ class MhaDims(ctypes.Structure):
 
 class MhaMask(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_uint32), ("key_len", ctypes.c_void_p),
-                ("allowed", ctypes.c_void_p), ("allowed_batch_stride", ctypes.c_int64)]
+                ("allowed", ctypes.c_void_p), ("allowed_batch_stride", ctypes.c_int64),
+                ("add", ctypes.c_void_p), ("add_batch_stride", ctypes.c_int64)]
+
+
+class MhaBias(ctypes.Structure):
+    _fields_ = [("b_Q", ctypes.c_void_p), ("b_K", ctypes.c_void_p), ("b_V", ctypes.c_void_p),
+                ("b_O", ctypes.c_void_p)]
 
 
 _LIB = None
@@ -67,8 +73,8 @@ def lib():
         vp, P = ctypes.c_void_p, ctypes.POINTER
         L.mha_workspace_bytes.argtypes = [P(MhaDims)]
         L.mha_workspace_bytes.restype = ctypes.c_size_t
-        L.mha_forward.argtypes = [P(MhaDims), P(MhaMask)] + [vp] * 8 + [vp, vp, vp,
-                                                                          ctypes.c_size_t, vp]
+        L.mha_forward.argtypes = ([P(MhaDims), P(MhaMask)] + [vp] * 7 + [P(MhaBias)] +
+                                  [vp] * 4 + [ctypes.c_size_t, vp])
         L.mha_forward.restype = ctypes.c_int
         L.attn_core.argtypes = [P(MhaDims), P(MhaMask), vp, vp, vp, vp, vp, vp, vp]
         L.attn_core.restype = ctypes.c_int
@@ -119,7 +125,7 @@ def _ptr(t):
     return t.data_ptr()
 
 
-def _mask(B, n_q, n_k, causal, key_len, allowed, device):
+def _mask(B, n_q, n_k, causal, key_len, allowed, device, add=None):
     torch = _torch()
     m = MhaMask()
     m.flags = 0
@@ -139,6 +145,14 @@ def _mask(B, n_q, n_k, causal, key_len, allowed, device):
         m.flags |= MHA_MASK_BOOL
         m.allowed = G.data_ptr()
         m.allowed_batch_stride = 0 if G.shape[0] == 1 else n_q * n_k
+    if add is not None:
+        M = torch.as_tensor(add, device=device).to(torch.float32).contiguous()
+        if M.dim() != 3 or M.shape[1:] != (n_q, n_k) or M.shape[0] not in (1, B):
+            raise ValueError("add must have shape [B or 1, n_q, n_k]")
+        keep.append(M)
+        m.flags |= MHA_MASK_ADDITIVE
+        m.add = M.data_ptr()
+        m.add_batch_stride = 0 if M.shape[0] == 1 else n_q * n_k
     return m, keep
 
 
@@ -155,13 +169,17 @@ def default_work_dtype(in_dtype):
 
 
 def mha_forward(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, *, scale=None, causal=False,
-                key_len=None, allowed=None, out_dtype=None, work_dtype=None, Y=None,
-                row_m=None, row_l=None, workspace=None, stream=None):
+                key_len=None, allowed=None, add=None, b_Q=None, b_K=None, b_V=None, b_O=None,
+                out_dtype=None, work_dtype=None, Y=None, row_m=None, row_l=None,
+                workspace=None, stream=None):
     """Y [B, n_q, d_o] = MHA(Q, K, V) for Q [B,n_q,d_q], K [B,n_k,d_k], V [B,n_k,d_v].
 
     Weights are combined (head r in column block r): W_Q [d_q, h*d_h],
-    W_K [d_k, h*d_h], W_V [d_v, h*d_vh], W_O [h*d_vh, d_o].  ``scale``
-    defaults to 1/sqrt(d_h); ``out_dtype`` to float32; ``work_dtype`` (the
+    W_K [d_k, h*d_h], W_V [d_v, h*d_vh], W_O [h*d_vh, d_o]; optional
+    projection biases b_Q [h*d_h], b_K [h*d_h], b_V [h*d_vh], b_O [d_o] in
+    the weights' element type; optional additive score bias ``add``
+    [B or 1, n_q, n_k] (float32, -inf forbids a key).  ``scale`` defaults
+    to 1/sqrt(d_h); ``out_dtype`` to float32; ``work_dtype`` (the
     intermediates' element type) to float16 for 2-byte inputs, else float32.
     """
     torch = _torch()
@@ -170,23 +188,28 @@ def mha_forward(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, *, scale=None, causal
     d_v = V.shape[2]
     d_o = W_O.shape[1]
     in_code = _dtype_code(Q.dtype)
-    for t in (K, V, W_Q, W_K, W_V, W_O):
-        if t.dtype != Q.dtype:
-            raise TypeError("Q, K, V and the weights must share one element type")
+    for t in (K, V, W_Q, W_K, W_V, W_O, b_Q, b_K, b_V, b_O):
+        if t is not None and t.dtype != Q.dtype:
+            raise TypeError("Q, K, V, the weights and the biases must share one element type")
+    for t, n in ((b_Q, h * d_h), (b_K, h * d_h), (b_V, h * d_vh), (b_O, d_o)):
+        if t is not None and t.numel() != n:
+            raise ValueError("a projection bias has the wrong length")
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     work_dtype = default_work_dtype(Q.dtype) if work_dtype is None else work_dtype
     dims = MhaDims(B=B, h=h, n_q=n_q, n_k=n_k, d_q=d_q, d_k=d_k, d_v=d_v, d_h=d_h, d_vh=d_vh,
                    d_o=d_o, scale=(1.0 / math.sqrt(d_h)) if scale is None else float(scale),
                    in_dtype=in_code, out_dtype=_dtype_code(out_dtype),
                    work_dtype=_dtype_code(work_dtype))
-    m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Q.device)
+    m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Q.device, add)
+    bias = MhaBias(b_Q=_ptr(b_Q), b_K=_ptr(b_K), b_V=_ptr(b_V), b_O=_ptr(b_O))
     if Y is None:
         Y = torch.empty((B, n_q, d_o), dtype=out_dtype, device=Q.device)
     need = mha_workspace_bytes(dims)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
     st = lib().mha_forward(ctypes.byref(dims), ctypes.byref(m), _ptr(Q), _ptr(K), _ptr(V),
-                           _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_O), _ptr(Y), _ptr(row_m),
+                           _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_O), ctypes.byref(bias),
+                           _ptr(Y), _ptr(row_m),
                            _ptr(row_l), _ptr(workspace), workspace.numel(), _stream(stream))
     del keep
     if st != 0:
@@ -207,13 +230,13 @@ def _core_dims(Qh, Kh, Vh, scale, out_dtype):
 
 
 def attn_core(Qh, Kh, Vh, *, scale=None, causal=False, key_len=None, allowed=None,
-              out_dtype=None, Z=None, row_m=None, row_l=None, stream=None):
+              add=None, out_dtype=None, Z=None, row_m=None, row_l=None, stream=None):
     """Z [B, n_q, h*d_vh] from heads Qh [B,h,n_q,d_h], Kh [B,h,n_k,d_h], Vh [B,h,n_k,d_vh]."""
     torch = _torch()
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     dims = _core_dims(Qh, Kh, Vh, scale, out_dtype)
     B, h, n_q, n_k, d_vh = dims.B, dims.h, dims.n_q, dims.n_k, dims.d_vh
-    m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Qh.device)
+    m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Qh.device, add)
     if Z is None:
         Z = torch.empty((B, n_q, h * d_vh), dtype=out_dtype, device=Qh.device)
     st = lib().attn_core(ctypes.byref(dims), ctypes.byref(m), _ptr(Qh), _ptr(Kh), _ptr(Vh),
@@ -230,7 +253,7 @@ def attn_split_workspace_bytes(dims: MhaDims, splits=0):
 
 
 def attn_core_split(Qh, Kh, Vh, *, splits=0, scale=None, causal=False, key_len=None,
-                    allowed=None, out_dtype=None, Z=None, row_m=None, row_l=None,
+                    allowed=None, add=None, out_dtype=None, Z=None, row_m=None, row_l=None,
                     workspace=None, stream=None):
     """attn_core with the key axis cut into partitions merged afterwards
     (``splits`` partitions requested, 0 = library's choice)."""
@@ -238,7 +261,7 @@ def attn_core_split(Qh, Kh, Vh, *, splits=0, scale=None, causal=False, key_len=N
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     dims = _core_dims(Qh, Kh, Vh, scale, out_dtype)
     B, h, n_q, n_k, d_vh = dims.B, dims.h, dims.n_q, dims.n_k, dims.d_vh
-    m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Qh.device)
+    m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Qh.device, add)
     if Z is None:
         Z = torch.empty((B, n_q, h * d_vh), dtype=out_dtype, device=Qh.device)
     if workspace is None:

@@ -87,7 +87,8 @@ mha_status check_full_dims(const mha_dims* d) {
 
 mha_status check_mask(const mha_dims* d, const mha_mask* m) {
   if (!m) return MHA_OK;
-  const uint32_t known = MHA_MASK_CAUSAL | MHA_MASK_KEY_PADDING | MHA_MASK_BOOL;
+  const uint32_t known =
+      MHA_MASK_CAUSAL | MHA_MASK_KEY_PADDING | MHA_MASK_BOOL | MHA_MASK_ADDITIVE;
   if (m->flags & ~known) return MHA_ERR_MASK;
   if ((m->flags & MHA_MASK_CAUSAL) && d->n_q != d->n_k) return MHA_ERR_MASK;
   if ((m->flags & MHA_MASK_KEY_PADDING) && !m->key_len) return MHA_ERR_MASK;
@@ -96,7 +97,13 @@ mha_status check_mask(const mha_dims* d, const mha_mask* m) {
     const int64_t plane = (int64_t)d->n_q * d->n_k;
     if (m->allowed_batch_stride != 0 && m->allowed_batch_stride < plane) return MHA_ERR_MASK;
   }
+  if (m->flags & MHA_MASK_ADDITIVE) {
+    if (!m->add) return MHA_ERR_MASK;
+    const int64_t plane = (int64_t)d->n_q * d->n_k;
+    if (m->add_batch_stride != 0 && m->add_batch_stride < plane) return MHA_ERR_MASK;
+  }
   if ((m->flags & MHA_MASK_KEY_PADDING) && !aligned(m->key_len, 4)) return MHA_ERR_ALIGN;
+  if ((m->flags & MHA_MASK_ADDITIVE) && !aligned(m->add, 4)) return MHA_ERR_ALIGN;
   return MHA_OK;
 }
 
@@ -105,12 +112,18 @@ void fill_mask(mha::AttnParams& p, const mha_mask* m) {
   p.key_len = nullptr;
   p.allowed = nullptr;
   p.allowed_batch_stride = 0;
+  p.add = nullptr;
+  p.add_batch_stride = 0;
   if (!m) return;
   p.causal = (m->flags & MHA_MASK_CAUSAL) ? 1 : 0;
   if (m->flags & MHA_MASK_KEY_PADDING) p.key_len = m->key_len;
   if (m->flags & MHA_MASK_BOOL) {
     p.allowed = m->allowed;
     p.allowed_batch_stride = m->allowed_batch_stride;
+  }
+  if (m->flags & MHA_MASK_ADDITIVE) {
+    p.add = m->add;
+    p.add_batch_stride = m->add_batch_stride;
   }
 }
 
@@ -284,8 +297,8 @@ mha_status attn_core_split(const mha_dims* d, const mha_mask* m, const void* Qh,
 
 mha_status mha_forward(const mha_dims* d, const mha_mask* m, const void* Q, const void* K,
                        const void* V, const void* W_Q, const void* W_K, const void* W_V,
-                       const void* W_O, void* Y, float* row_m, float* row_l, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       const void* W_O, const mha_bias* bias, void* Y, float* row_m,
+                       float* row_l, void* workspace, size_t workspace_bytes, void* stream) {
   mha_status s = check_full_dims(d);
   if (s != MHA_OK) return s;
   if ((s = check_mask(d, m)) != MHA_OK) return s;
@@ -294,6 +307,11 @@ mha_status mha_forward(const mha_dims* d, const mha_mask* m, const void* Q, cons
   if (!aligned(Q, ei) || !aligned(K, ei) || !aligned(V, ei) || !aligned(W_Q, ei) ||
       !aligned(W_K, ei) || !aligned(W_V, ei) || !aligned(W_O, ei) || !aligned(Y, eo) ||
       !aligned(row_m, 4) || !aligned(row_l, 4))
+    return MHA_ERR_ALIGN;
+  const mha_bias nb = {nullptr, nullptr, nullptr, nullptr};
+  const mha_bias& bs = bias ? *bias : nb;
+  if (!aligned(bs.b_Q, ei) || !aligned(bs.b_K, ei) || !aligned(bs.b_V, ei) ||
+      !aligned(bs.b_O, ei))
     return MHA_ERR_ALIGN;
   const Workspace w = carve(d);
   if (!workspace || workspace_bytes < w.total) return MHA_ERR_WORKSPACE;
@@ -314,6 +332,7 @@ mha_status mha_forward(const mha_dims* d, const mha_mask* m, const void* Q, cons
   gb.count = 3;
   const void* srcs[3] = {Q, K, V};
   const void* ws3[3] = {W_Q, W_K, W_V};
+  const void* b3[3] = {bs.b_Q, bs.b_K, bs.b_V};
   void* dst[3] = {Qh, Kh, Vh};
   const int Ms[3] = {d->B * d->n_q, d->B * d->n_k, d->B * d->n_k};
   const int Ks[3] = {d->d_q, d->d_k, d->d_v};
@@ -335,6 +354,7 @@ mha_status mha_forward(const mha_dims* d, const mha_mask* m, const void* Q, cons
     p.vec_a = aligned(p.A, 16) && (p.K % vin == 0);
     p.vec_w = aligned(p.W, 16) && (p.N % vin == 0);
     p.vec_c = 1;
+    p.bias = b3[i];
   }
   if (mha::launch_gemm(gb, d->in_dtype, d->in_dtype, st) != hipSuccess) return MHA_ERR_LAUNCH;
 
@@ -358,6 +378,7 @@ mha_status mha_forward(const mha_dims* d, const mha_mask* m, const void* Q, cons
   o.K = d->h * d->d_vh;
   o.epilogue = mha::kRowMajor;
   o.out_dtype = d->out_dtype;
+  o.bias = bs.b_O;
   o.vec_a = (o.K % vwork == 0);
   o.vec_w = aligned(W_O, 16) && (o.N % vin == 0);
   o.vec_c = aligned(Y, 16);

@@ -217,6 +217,8 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   const T* Vb = reinterpret_cast<const T*>(p.V) + (size_t)bh * p.n_k * p.ldv;
   const uint8_t* Gb =
       (!FAST && p.allowed) ? p.allowed + (size_t)b * p.allowed_batch_stride : nullptr;
+  // additive score bias M (general path only): added to the scaled score
+  const float* Ab = (!FAST && p.add) ? p.add + (size_t)b * p.add_batch_stride : nullptr;
   const bool vq = FAST || p.vec_q, vk = FAST || p.vec_k, vv = FAST || p.vec_v;
   const int dh = FAST ? DH : p.d_h;
   const int dvh = FAST ? DV : p.d_vh;
@@ -231,8 +233,12 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   // The deferred-shift variant also scales 2-byte queries once (one extra
   // rounding of q c log2(e) to T), so that the score MFMA alone forms
   // c' s - mu.
+  // With an additive bias the mask step forms the scaled score c' s + M log2(e)
+  // itself (cs0 = the scale still to apply to the raw product), and later
+  // steps see scaled scores (cs = 1).
   constexpr bool PRESCALE = sizeof(T) == 4 || LAZY;
-  const float cs = PRESCALE ? 1.0f : fabsf(p.scale_log2);
+  const float cs0 = PRESCALE ? 1.0f : fabsf(p.scale_log2);
+  const float cs = (Ab != nullptr) ? 1.0f : cs0;
 
   // This lane's query row as the B operand of S^T = K Q^T (registers, whole
   // kernel).
@@ -481,8 +487,8 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       // Score slot (kb, i) of this lane is key k0 + off(kb, i) + 4 g with
       // off = 32 kb + 8 (i / 4) + i % 4.  Causal and key padding allow exactly
       // the keys j <= lim = min(qi, kvalid - 1): one compare per score.
-      const bool need_mask =
-          (k0 + BN > kvalid) || (p.causal && k0 + BN - 1 > qw) || (!FAST && Gb != nullptr);
+      const bool need_mask = (k0 + BN > kvalid) || (p.causal && k0 + BN - 1 > qw) ||
+                             (!FAST && (Gb != nullptr || Ab != nullptr));
       auto apply_mask = [&]() {
         const int lim = p.causal ? min(qi, kvalid - 1) : kvalid - 1;
         const int t = lim - k0 - 4 * g;
@@ -494,7 +500,14 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
             bool ok = off <= t;
             if (!FAST && Gb != nullptr && ok)
               ok = qi < p.n_q && Gb[(size_t)qi * p.n_k + k0 + off + 4 * g] != 0;
-            s[kb][i] = ok ? s[kb][i] : -INFINITY;
+            if (!FAST && Ab != nullptr) {
+              // an allowed key has index <= lim < n_k, and qi < n_q is checked
+              const float mb =
+                  (ok && qi < p.n_q) ? Ab[(size_t)qi * p.n_k + k0 + off + 4 * g] : 0.f;
+              s[kb][i] = ok ? fmaf(s[kb][i], cs0, mb * kLog2e) : -INFINITY;
+            } else {
+              s[kb][i] = ok ? s[kb][i] : -INFINITY;
+            }
           }
       };
       if (need_mask) apply_mask();

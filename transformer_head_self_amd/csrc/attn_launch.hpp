@@ -32,7 +32,7 @@ hipError_t launch_attn_fixed(AttnParams p, hipStream_t stream) {
   const long long grid = (long long)p.num_q_tiles * p.B * p.h;
   if (grid <= 0) return hipSuccess;
   const bool fast = p.d_h == DH && p.d_vh == DV && p.vec_q && p.vec_k && p.vec_v &&
-                    p.allowed == nullptr;
+                    p.allowed == nullptr && p.add == nullptr;
   // The deferred-shift variant is used for the fast path (causal / key
   // padding masks only, where every row's first block holds an allowed key)
   // except for bf16, whose extra rounding of the scaled query would cost
@@ -100,7 +100,7 @@ hipError_t launch_attn_split_fixed(AttnParams p, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   if (grid > 2147483647LL) return hipErrorInvalidValue;
   const bool fast = p.d_h == DH && p.d_vh == DV && p.vec_q && p.vec_k && p.vec_v &&
-                    p.allowed == nullptr;
+                    p.allowed == nullptr && p.add == nullptr;
   if (fast)
     hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, false, 1, true, true>),
                        dim3((unsigned)grid), dim3(C::NT), 0, stream, p);

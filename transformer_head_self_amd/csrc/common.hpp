@@ -21,6 +21,7 @@ typedef float floatx8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2e = 1.4426950408889634f;
 
 // Element codes shared with the C ABI (mha_dtype).
 enum DType : int { kF32 = 0, kBF16 = 1, kF16 = 2 };

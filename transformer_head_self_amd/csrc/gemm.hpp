@@ -17,6 +17,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "gemm_store.hpp"
 #include "internal.hpp"
 
 namespace mha {
@@ -160,6 +161,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmBatch batch) {
   }
 
   // ---- epilogue ------------------------------------------------------------
+  add_column_bias<TW>(P, acc, n0 + wn * C::WN, g);
   #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int m = m0 + wm * C::WM + i * 32 + l32;

@@ -188,6 +188,7 @@ void gemm_dma_wide_kernel(GemmBatch batch) {
   // keep the compiler from computing it before the loop).
   int m0w = m0 + wm * 128, n0w = n0 + wn * 64, lane_e = lane;
   asm volatile("" : "+s"(m0w), "+s"(n0w), "+v"(lane_e));
+  add_column_bias<TW>(P, acc, n0w, lane_e >> 5);
   // every wave has finished reading the stage buffers before they are reused
   // for the staged stores (18 KB per wave)
   __syncthreads();

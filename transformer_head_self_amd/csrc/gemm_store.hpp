@@ -19,6 +19,29 @@
 
 namespace mha {
 
+// Projection bias (the bias convention of review page "Multi-Head
+// Attention", "Parameter and Work Conventions"): C[m, n] += bias[n], in fp32
+// before the store rounds.  acc[j][i] holds columns n0w + 32 j + 8 a + 4 g +
+// (0..3) in registers 4a..4a+3 for every i.  TW: the bias's element type
+// (that of W).  Columns past N add nothing (they are never stored).
+template <typename TW, int NI>
+__device__ __forceinline__ void add_column_bias(const GemmProblem& P, floatx16 (&acc)[2][NI],
+                                                int n0w, int g) {
+  if (P.bias == nullptr) return;
+  const TW* bias = reinterpret_cast<const TW*>(P.bias);
+  #pragma unroll
+  for (int j = 0; j < 2; ++j)
+    #pragma unroll
+    for (int a = 0; a < 4; ++a)
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = n0w + 32 * j + 8 * a + 4 * g + e;
+        const float bv = n < P.N ? (float)bias[n] : 0.f;
+        #pragma unroll
+        for (int i = 0; i < NI; ++i) acc[j][i][4 * a + e] += bv;
+      }
+}
+
 template <int DT, bool HEADS>
 __device__ __forceinline__ void store_wave_block(const GemmProblem& P, const floatx16 (&acc)[2][4],
                                                  int m0w, int n0w, int g, int l32) {

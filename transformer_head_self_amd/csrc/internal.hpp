@@ -32,6 +32,7 @@ struct GemmProblem {
   int tiles_m, tiles_n, tile_begin;  // filled by the launcher
   int vec_a, vec_w;  // 16-byte vector loads allowed for A / W rows
   int vec_c;         // vector stores allowed for C (kRowMajor)
+  const void* bias;  // optional [N], element type of W: C[m, n] += bias[n] before rounding
   FastDiv dh_div, ntok_div;  // filled by the launcher
 };
 
@@ -57,6 +58,8 @@ struct AttnParams {
   const int32_t* key_len;   // optional [B]
   const uint8_t* allowed;   // optional [Bm, n_q, n_k]
   long long allowed_batch_stride;
+  const float* add;         // optional additive score bias [Ba, n_q, n_k] (natural-log units)
+  long long add_batch_stride;
   int B, h, n_q, n_k, d_h, d_vh;
   int ldq, ldk, ldv, ldz;
   float scale_log2;  // c * log2(e)

@@ -9,7 +9,8 @@ Modules
 -------
 mha_oracle   dense float64 reference: projections (two independent forms),
              materialised score matrix, mask, stable row softmax, weighted
-             value sum, head concatenation, output projection.
+             value sum, head concatenation, output projection; and the
+             analytic gradients of the attention core.
 summary      the stable key-block summary (m, l, z), its empty state and its
              merge rule, written out literally for checking identities.
 bruteforce   pure-Python scalar loops in 50-digit mpmath arithmetic for tiny
@@ -26,6 +27,7 @@ from .mha_oracle import (  # noqa: F401
     project_combined,
     masked_softmax_rows,
     attn_core_ref,
+    attn_core_grad_ref,
     mha_ref,
     mha_ref_rows,
 )

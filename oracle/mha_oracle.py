@@ -240,3 +240,44 @@ def mha_ref_rows(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, scale, allow, b, row
     if bs.get("b_O") is not None:
         Y = Y + _f64(bs["b_O"])[None, :]
     return Y, out["Z"][0], out["m"][0], out["l"][0]
+
+
+def attn_core_grad_ref(Qh, Kh, Vh, scale, allow, dZ, add=None):
+    """Gradients of the attention core for an upstream gradient dZ.
+
+    Same arguments as ``attn_core_ref`` plus dZ [B, n_q, h*d_vh] (the
+    gradient of a scalar loss with respect to the concatenated output Z).
+    Returns dict with dQh, dKh, dVh (shapes of Qh, Kh, Vh).
+
+    Derivation (calculus on the definitions the forward follows; the pages
+    give no backward pass): for one head, with scores S = c Q K^T (+ M) and
+    A = masked row softmax of S, Z_r = A V:
+      dV = A^T dZ_r                          (Z_r is linear in V);
+      dA = dZ_r V^T;
+      dS_ij = A_ij (dA_ij - sum_k A_ik dA_ik)   (softmax Jacobian per row;
+                                                forbidden entries have
+                                                A_ij = 0, so dS_ij = 0);
+      dQ = c dS K,  dK = c dS^T Q.
+    The row term sum_k A_ik dA_ik equals sum_e dZ_ie Z_ie.
+    """
+    Qh, Kh, Vh = _f64(Qh), _f64(Kh), _f64(Vh)
+    dZ = _f64(dZ)
+    B, h, n_q, _ = Qh.shape
+    n_k = Kh.shape[2]
+    d_vh = Vh.shape[3]
+    out = attn_core_ref(Qh, Kh, Vh, scale, allow, keep_A=True, add=add)
+    A_all = out["A"]
+    dQ = np.zeros_like(Qh)
+    dK = np.zeros_like(Kh)
+    dV = np.zeros_like(Vh)
+    for b in range(B):
+        for r in range(h):
+            A = A_all[b, r]                                   # [n_q, n_k]
+            dZr = dZ[b, :, r * d_vh:(r + 1) * d_vh]           # [n_q, d_vh]
+            dV[b, r] = A.T @ dZr
+            dA = dZr @ Vh[b, r].T
+            rowdot = np.sum(A * dA, axis=1, keepdims=True)
+            dS = A * (dA - rowdot)
+            dQ[b, r] = scale * (dS @ Kh[b, r])
+            dK[b, r] = scale * (dS.T @ Qh[b, r])
+    return {"dQh": dQ, "dKh": dK, "dVh": dV}

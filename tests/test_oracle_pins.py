@@ -31,7 +31,7 @@ import numpy as np
 import pytest
 
 from oracle import (
-    BOTTOM, EmptyRowError, allowed_set, attn_core_ref, finalize, fold, merge,
+    BOTTOM, EmptyRowError, allowed_set, attn_core_grad_ref, attn_core_ref, finalize, fold, merge,
     mha_ref, mha_ref_rows, project_combined, project_separate, summary,
 )
 from oracle import mha_oracle
@@ -778,3 +778,115 @@ def test_planted_bias_mistakes_fail_the_bruteforce_pin(monkeypatch, name, mutant
                 bad = True
         caught = caught or bad
     assert caught, f"mutant {mutant.__name__} slipped past the brute-force pin"
+
+
+# --------------------------------------------------------------------------
+# gradients of the attention core
+# --------------------------------------------------------------------------
+
+def _grad_case(seed, B=2, h=2, n_q=5, n_k=6, d_h=3, d_vh=4):
+    rng = _rng(seed)
+    Qh = rng.normal(size=(B, h, n_q, d_h))
+    Kh = rng.normal(size=(B, h, n_k, d_h))
+    Vh = rng.normal(size=(B, h, n_k, d_vh))
+    dZ = rng.normal(size=(B, n_q, h * d_vh))
+    return Qh, Kh, Vh, dZ
+
+
+GRAD_MASKS = [
+    dict(causal=False, key_len=None, bool_mask=False, add=False),
+    dict(causal=True, key_len=None, bool_mask=False, add=False),
+    dict(causal=False, key_len=[6, 2], bool_mask=True, add=False),
+    dict(causal=True, key_len=[4, 6], bool_mask=False, add=True),
+]
+
+
+def _grad_allow(mask, B, n_q, n_k, rng):
+    G = None
+    if mask["bool_mask"]:
+        G = rng.random((B, n_q, n_k)) < 0.6
+        G[:, :, 0] = True
+    kl = None if mask["key_len"] is None else np.array(mask["key_len"])
+    allow = allowed_set(B, n_q, n_k, causal=mask["causal"], key_len=kl, allowed=G)
+    M = None
+    if mask["add"]:
+        M = rng.normal(size=(B, n_q, n_k))
+        M[:, 2, 1] = -np.inf
+    return allow, M
+
+
+@pytest.mark.parametrize("mask", GRAD_MASKS, ids=lambda m: "-".join(f"{k}{v}" for k, v in m.items()))
+def test_core_gradient_matches_central_differences(mask):
+    """Loss L = sum(Z * dZ): every partial derivative of the oracle's gradient
+    equals the central difference of the forward oracle (step 1e-5, error
+    O(h^2) ~ 1e-10)."""
+    n = 6
+    Qh, Kh, Vh, dZ = _grad_case(80, n_q=n, n_k=n)
+    allow, M = _grad_allow(mask, 2, n, n, _rng(81))
+    c = 0.7
+    g = attn_core_grad_ref(Qh, Kh, Vh, c, allow, dZ, add=M)
+
+    def loss(Q, K, V):
+        return float(np.sum(attn_core_ref(Q, K, V, c, allow, add=M)["Z"] * dZ))
+
+    eps = 1e-5
+    for name, X, key in (("Q", Qh, "dQh"), ("K", Kh, "dKh"), ("V", Vh, "dVh")):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            Xp = X.copy(); Xp[idx] += eps
+            Xm = X.copy(); Xm[idx] -= eps
+            args = {"Q": Qh, "K": Kh, "V": Vh}
+            args[name] = Xp
+            lp = loss(args["Q"], args["K"], args["V"])
+            args[name] = Xm
+            lm = loss(args["Q"], args["K"], args["V"])
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g[key], num, rtol=1e-6, atol=1e-8)
+
+
+def test_core_gradient_invariants():
+    """Adding one vector to every key leaves each row's softmax unchanged, so
+    the key gradients of a (batch, head) sum to zero over the allowed keys;
+    with c = 0 the weights do not depend on Q or K (dQ = dK = 0) and
+    dV = A^T dZ with A the uniform weights; a row with one allowed key
+    has dQ = 0."""
+    Qh, Kh, Vh, dZ = _grad_case(82, n_q=7, n_k=7)
+    allow = allowed_set(2, 7, 7, causal=True)
+    g = attn_core_grad_ref(Qh, Kh, Vh, 0.9, allow, dZ)
+    np.testing.assert_allclose(g["dKh"].sum(axis=2), 0.0, atol=1e-12)
+    np.testing.assert_allclose(g["dQh"][:, :, 0], 0.0, atol=1e-15)   # row 0 sees key 0 only
+    g0 = attn_core_grad_ref(Qh, Kh, Vh, 0.0, allow, dZ)
+    assert np.all(g0["dQh"] == 0) and np.all(g0["dKh"] == 0)
+    A = np.tril(np.ones((7, 7))) / np.arange(1, 8)[:, None]
+    for b in range(2):
+        for r in range(2):
+            np.testing.assert_allclose(g0["dVh"][b, r], A.T @ dZ[b, :, r * 4:(r + 1) * 4],
+                                       rtol=1e-13)
+
+
+def _mut_grad_no_row_term(Qh, Kh, Vh, scale, allow, dZ, add=None):
+    out = attn_core_ref(Qh, Kh, Vh, scale, allow, keep_A=True, add=add)
+    B, h = Qh.shape[:2]
+    d_vh = Vh.shape[3]
+    res = {"dQh": np.zeros(Qh.shape), "dKh": np.zeros(Kh.shape), "dVh": np.zeros(Vh.shape)}
+    for b in range(B):
+        for r in range(h):
+            A = out["A"][b, r]
+            dZr = np.asarray(dZ)[b, :, r * d_vh:(r + 1) * d_vh]
+            dS = A * (dZr @ np.asarray(Vh)[b, r].T)           # the row term is missing
+            res["dVh"][b, r] = A.T @ dZr
+            res["dQh"][b, r] = scale * dS @ np.asarray(Kh)[b, r]
+            res["dKh"][b, r] = scale * dS.T @ np.asarray(Qh)[b, r]
+    return res
+
+
+def test_planted_gradient_mistake_fails_central_differences():
+    Qh, Kh, Vh, dZ = _grad_case(83, B=1, h=1, n_q=3, n_k=4, d_h=2, d_vh=2)
+    allow = np.ones((1, 3, 4), bool)
+    g = _mut_grad_no_row_term(Qh, Kh, Vh, 0.8, allow, dZ)
+    eps = 1e-5
+    Qp = Qh.copy(); Qp[0, 0, 0, 0] += eps
+    Qm = Qh.copy(); Qm[0, 0, 0, 0] -= eps
+    num = (np.sum(attn_core_ref(Qp, Kh, Vh, 0.8, allow)["Z"] * dZ) -
+           np.sum(attn_core_ref(Qm, Kh, Vh, 0.8, allow)["Z"] * dZ)) / (2 * eps)
+    assert abs(g["dQh"][0, 0, 0, 0] - num) > 1e-4

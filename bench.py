@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--decode", action="store_true",
                     help="time the key-split attention core on a decode step instead "
                          "(one query row per item and head against 32768 cached keys)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the attention-core backward pass on the headline shape instead")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters (optional)")
     return ap.parse_args()
@@ -165,6 +167,71 @@ def decode_bench(args, torch):
     }), flush=True)
 
 
+def backward_bench(args, torch):
+    """Attention-core backward on the headline shape (B=4, T=4096, h=16,
+    d=64, causal), fp16 heads and fp16 Z/dZ/gradients (the forward's
+    intermediate type).  FLOPs counted as 2.5 x the forward's (five products
+    of n_q x n_k x d instead of two: the recomputed scores, dZ V^T, A^T dZ,
+    dS K and dS^T Q), halved for causal."""
+    import transformer_head_self_amd as mha
+    from transformer_head_self_amd.inputs import make_heads
+    B, h, T, d = 4, 16, 4096, 64
+    dev = torch.device("cuda:0")
+    Qh, Kh, Vh = (torch.from_numpy(a).to(dev).to(torch.float16)
+                  for a in make_heads(B, h, T, T, d, d, "f32", seed=70))
+    gen = torch.Generator(device="cpu").manual_seed(71)
+    dZ = torch.randn(B, T, h * d, generator=gen).to(dev).half()
+    Z = torch.empty((B, T, h * d), dtype=torch.float16, device=dev)
+    rm = torch.empty((B, h, T), device=dev)
+    rl = torch.empty_like(rm)
+    stream = torch.cuda.current_stream()
+    scale = 1 / math.sqrt(d)
+    dims = mha.MhaDims(B=B, h=h, n_q=T, n_k=T, d_q=1, d_k=1, d_v=1, d_h=d, d_vh=d, d_o=1,
+                       scale=scale, in_dtype=2, out_dtype=2, work_dtype=2)
+    ws = torch.empty(mha.attn_backward_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    grads = [torch.empty_like(Qh), torch.empty_like(Kh), torch.empty_like(Vh)]
+
+    def fwd():
+        mha.attn_core(Qh, Kh, Vh, scale=scale, causal=True, out_dtype=torch.float16, Z=Z,
+                      row_m=rm, row_l=rl, stream=stream)
+
+    def bwd():
+        mha.attn_core_backward(Qh, Kh, Vh, Z, dZ, rm, rl, scale=scale, causal=True,
+                               dQh=grads[0], dKh=grads[1], dVh=grads[2], workspace=ws,
+                               stream=stream)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_fwd = timed(fwd)
+    ms_bwd = timed(bwd)
+    fwd_flops = 2.0 * B * h * T * T * (d + d) / 2
+    bwd_flops = 2.5 * fwd_flops
+    peak = PEAK_TFLOPS["bf16"]
+    tf = bwd_flops / (ms_bwd * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "attention-core backward TFLOP/s (T=4096, h=16, d=64, causal)",
+        "value": round(tf, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_bwd, 5), "higher_is_better": True,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "attn-backward-f16-B4-T4096-h16-d64-causal",
+                   "flops_per_step": bwd_flops},
+        "roofline": {"bound": "mfma", "kernel": "attn_bwd_kv_kernel + attn_bwd_q_kernel",
+                     "achieved": round(tf, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tf / peak, 4)},
+        "forward_ms": round(ms_fwd, 5),
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -190,6 +257,9 @@ def main():
 
     if args.decode:
         decode_bench(args, torch)
+        return
+    if args.backward:
+        backward_bench(args, torch)
         return
 
     import transformer_head_self_amd as mha

@@ -190,6 +190,36 @@ mha_status attn_core_split(const mha_dims* d, const mha_mask* m,
                            float* row_m, float* row_l, int32_t splits,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward pass of attn_core: gradients of a scalar loss with respect to
+ * Qh, Kh and Vh, given dZ, its gradient with respect to Z.  The pages define
+ * the forward pass; the gradients follow from it by calculus (for one head,
+ * A = softmax of S = c Qh Kh^T (+ M), Z = A Vh):
+ *   dVh = A^T dZ,  dS = A o (dZ Vh^T - D),  D_i = sum_e dZ_ie Z_ie,
+ *   dQh = c dS Kh, dKh = c dS^T Qh.
+ * A is recomputed block by block from the forward's row statistics (page
+ * "Stable summary of an attention key block", Definition: the weights are
+ * e^(s - m) / l for the final (m, l) of each row); nothing of size n_q x n_k
+ * is stored.  Same dims and mask as the forward call (an additive bias M is
+ * applied; no gradient with respect to M is formed).
+ *   in_dtype   BF16 or F16 (Qh, Kh, Vh); F32 gives MHA_ERR_DTYPE.
+ *   out_dtype  element type of Z, dZ and of the gradients written.
+ *   Qh, Kh, Vh as for attn_core; Z [B, n_q, h*d_vh] the forward's output,
+ *   dZ of the same shape; row_m, row_l [B, h, n_q] fp32 from the same
+ *   forward call (required).
+ *   dQh [B, h, n_q, d_h], dKh [B, h, n_k, d_h], dVh [B, h, n_k, d_vh]
+ *   (written; keys no query may use get 0).
+ *   workspace  device scratch of attn_backward_workspace_bytes(d) bytes,
+ *   256-byte aligned (two fp32 values per row and head).
+ * Three launches on `stream`: row terms, dKh and dVh, dQh.  The result is
+ * deterministic (no atomics). */
+size_t attn_backward_workspace_bytes(const mha_dims* d);
+mha_status attn_core_backward(const mha_dims* d, const mha_mask* m,
+                              const void* Qh, const void* Kh, const void* Vh,
+                              const void* Z, const void* dZ,
+                              const float* row_m, const float* row_l,
+                              void* dQh, void* dKh, void* dVh,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code (host memory, never freed). */
 const char* mha_status_string(int status);
 

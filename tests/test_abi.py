@@ -296,3 +296,33 @@ def test_split_argument_errors():
     big = _dims(B=1, h=1, n_q=1 << 16, n_k=1 << 22)
     assert mha.attn_split_workspace_bytes(big, 1 << 16) == 0
     assert _split(big, splits=1 << 16) == -2
+
+
+# ---- backward of the attention core -----------------------------------------
+
+def _bwd(d, m=None, ptrs=None, ws=FAKE, ws_bytes=1 << 30):
+    p = [FAKE] * 10 if ptrs is None else ptrs
+    return mha.lib().attn_core_backward(
+        ctypes.byref(d) if d is not None else None, ctypes.byref(m) if m is not None else None,
+        *p, ws, ws_bytes, None)
+
+
+def test_backward_workspace_and_errors():
+    d = _dims(in_dtype=mha.MHA_BF16, out_dtype=mha.MHA_BF16, B=3, h=5, n_q=37)
+    need = mha.attn_backward_workspace_bytes(d)
+    assert need == 2 * ((3 * 5 * 37 * 4 + 255) // 256 * 256)
+    assert mha.attn_backward_workspace_bytes(None) == 0
+    assert _bwd(None) == -1
+    assert _bwd(_dims()) == -3                       # fp32 heads: no backward kernels
+    for i in range(10):
+        p = [FAKE] * 10
+        p[i] = None
+        assert _bwd(d, ptrs=p) == -1                 # row_m and row_l are required
+    p = [FAKE] * 10
+    p[4] = FAKE + 1                                  # dZ misaligned for bf16
+    assert _bwd(d, ptrs=p) == -5
+    assert _bwd(d, ws_bytes=need - 1) == -6
+    assert _bwd(d, ws=None) == -6
+    assert _bwd(d, ws=FAKE + 128, ws_bytes=need) == -5
+    assert _bwd(d, MhaMask(flags=mha.MHA_MASK_CAUSAL)) == -4   # n_q != n_k
+    assert _bwd(_dims(in_dtype=mha.MHA_F16, out_dtype=mha.MHA_F32, d_h=200)) == -7

@@ -761,3 +761,128 @@ def test_forward_biases_at_headline_size_sampled():
         err = _rel_err(Y[b, rows], Yr)
         _say(f"  item {b} rows {rows}: err {err:.3e}")
         assert err <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# backward of the attention core (gradients from the saved row statistics)
+# ---------------------------------------------------------------------------
+
+from oracle import attn_core_grad_ref  # noqa: E402
+
+# Gradient bars (normwise ||out - ref|| / ||ref||, and max|out - ref| /
+# max|ref|): the kernels round A, dS and dZ once to the element type
+# (u = 2^-9 for bf16, 2^-11 for fp16) before fp32 sums; a CPU emulation of
+# exactly those roundings on these cases gives normwise 2.4e-3 (bf16) and
+# 3e-4 (fp16), max-normalised at most 3.7e-3 and 6.2e-4.  The bars are about
+# twice that.  (max|err| / RMS, the forward's metric, is dominated by the
+# heavy tail of the gradients: a few keys with large weights.)
+BWD_TOL = {"bf16": (5e-3, 1e-2), "f16": (1e-3, 2e-3)}
+
+
+def _grad_err(out, ref):
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = out - ref
+    return (float(np.linalg.norm(d) / np.linalg.norm(ref)),
+            float(np.abs(d).max() / np.abs(ref).max()))
+
+
+def _bwd_run(dt, zdt, Qh, Kh, Vh, dZ, c, causal=False, key_len=None, allowed=None, add=None):
+    """GPU forward (for Z, row_m, row_l) then backward; returns numpy grads,
+    the exact values the GPU consumed (heads and dZ), and Z."""
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+    zt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[zdt]
+    dev = [torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(tdt) for a in (Qh, Kh, Vh)]
+    B, h, n_q, _ = Qh.shape
+    kl = None if key_len is None else torch.from_numpy(np.asarray(key_len, np.int32)).to(DEV)
+    G = None if allowed is None else torch.from_numpy(allowed).to(DEV)
+    M = None if add is None else torch.from_numpy(add).to(DEV)
+    rm = torch.empty((B, h, n_q), device=DEV)
+    rl = torch.empty_like(rm)
+    Z = mha.attn_core(*dev, scale=c, causal=causal, key_len=kl, allowed=G, add=M, out_dtype=zt,
+                      row_m=rm, row_l=rl)
+    dZt = torch.from_numpy(np.ascontiguousarray(dZ)).to(DEV).to(zt)
+    grads = mha.attn_core_backward(*dev, Z, dZt, rm, rl, scale=c, causal=causal, key_len=kl,
+                                   allowed=G, add=M)
+    torch.cuda.synchronize()
+    host = [t.float().cpu().numpy().astype(np.float64) for t in dev]
+    return ([g.float().cpu().numpy() for g in grads], host,
+            dZt.float().cpu().numpy().astype(np.float64))
+
+
+BWD_CASES = [
+    # dtype, grad dtype, B, h, n_q, n_k, d_h, d_vh, causal, key_len, bool, additive
+    ("bf16", "f32", 2, 3, 100, 333, 64, 64, False, None, False, False),
+    ("f16", "f32", 2, 2, 200, 200, 64, 64, True, None, False, False),
+    ("bf16", "bf16", 2, 2, 130, 257, 64, 96, False, (257, 100), False, False),
+    ("f16", "f32", 1, 2, 300, 300, 128, 128, True, (300,), False, False),
+    ("f16", "f16", 3, 2, 65, 65, 40, 24, True, (65, 10, 1), False, False),
+    ("bf16", "f32", 2, 2, 96, 160, 32, 32, False, None, True, False),
+    ("f16", "f32", 2, 2, 150, 150, 64, 64, True, None, False, True),
+    ("f16", "f32", 2, 2, 1, 700, 64, 64, False, (700, 300), False, False),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_backward_matches_oracle(case):
+    dt, zdt, B, h, n_q, n_k, d_h, d_vh, causal, kl, use_bool, use_add = case
+    _say(f"[backward] {case}")
+    Qh, Kh, Vh = make_heads(B, h, n_q, n_k, d_h, d_vh, "f32", seed=60 + n_q + n_k)
+    rng = np.random.default_rng(61 + n_k)
+    dZ = rng.standard_normal((B, n_q, h * d_vh)).astype(np.float32)
+    key_len = None if kl is None else np.array(kl[:B], dtype=np.int32)
+    G = None
+    if use_bool:
+        G = rng.random((B, n_q, n_k)) < 0.5
+        G[:, :, 0] = True
+    M = _additive(rng, B, n_q, n_k) if use_add else None
+    c = 1.0 / math.sqrt(d_h)
+    grads, host, dZh = _bwd_run(dt, zdt, Qh, Kh, Vh, dZ, c, causal, key_len, G, M)
+    allow = allowed_set(B, n_q, n_k, causal=causal, key_len=key_len, allowed=G)
+    ref = attn_core_grad_ref(*host, c, allow, dZh, add=M)
+    for name, got in zip(("dQh", "dKh", "dVh"), grads):
+        fro, mx = _grad_err(got, ref[name])
+        _say(f"  {name} normwise {fro:.3e} max {mx:.3e}")
+        assert fro <= BWD_TOL[dt][0] and mx <= BWD_TOL[dt][1], name
+    # keys that no query may use get exactly zero gradient
+    if key_len is not None:
+        for b in range(B):
+            assert np.all(grads[1][b, :, key_len[b]:] == 0)
+            assert np.all(grads[2][b, :, key_len[b]:] == 0)
+
+
+def test_backward_zero_scale_and_determinism():
+    """c = 0: weights do not depend on Q or K, so dQh = dKh = 0 exactly, and
+    dVh is the uniform-weight closed form; two runs agree bit for bit."""
+    B, h, n, d = 2, 2, 200, 64
+    Qh, Kh, Vh = make_heads(B, h, n, n, d, d, "f32", seed=62)
+    dZ = np.random.default_rng(63).standard_normal((B, n, h * d)).astype(np.float32)
+    g1, host, dZh = _bwd_run("f16", "f32", Qh, Kh, Vh, dZ, 0.0, causal=True)
+    g2, _, _ = _bwd_run("f16", "f32", Qh, Kh, Vh, dZ, 0.0, causal=True)
+    assert np.all(g1[0] == 0) and np.all(g1[1] == 0)
+    A = np.tril(np.ones((n, n))) / np.arange(1, n + 1)[:, None]
+    for b in range(B):
+        for r in range(h):
+            ref = A.T @ dZh[b, :, r * d:(r + 1) * d]
+            fro, mx = _grad_err(g1[2][b, r], ref)
+            assert fro <= BWD_TOL["f16"][0] and mx <= BWD_TOL["f16"][1]
+    for a, b in zip(g1, g2):
+        assert np.array_equal(a, b)
+
+
+def test_backward_full_size_two_heads():
+    """The 4 x 4096-token causal shape with 16 heads of 64 (fp16 heads, fp32
+    gradients); two (item, head) pairs checked in full against the oracle."""
+    B, h, T, d = 4, 16, 4096, 64
+    _say(f"[backward full size] B={B} h={h} T={T} d={d} causal")
+    Qh, Kh, Vh = make_heads(B, h, T, T, d, d, "f32", seed=64)
+    dZ = np.random.default_rng(65).standard_normal((B, T, h * d)).astype(np.float32)
+    grads, host, dZh = _bwd_run("f16", "f32", Qh, Kh, Vh, dZ, 0.125, causal=True)
+    allow = allowed_set(1, T, T, causal=True)
+    for b, r in ((0, 0), (3, 11)):
+        sub = [x[b:b + 1, r:r + 1] for x in host]
+        ref = attn_core_grad_ref(*sub, 0.125, allow, dZh[b:b + 1, :, r * d:(r + 1) * d])
+        for k, (name, got) in enumerate(zip(("dQh", "dKh", "dVh"), grads)):
+            fro, mx = _grad_err(got[b, r], ref[name][0, 0])
+            _say(f"  item {b} head {r} {name} normwise {fro:.3e} max {mx:.3e}")
+            assert fro <= BWD_TOL["f16"][0] and mx <= BWD_TOL["f16"][1]

@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
 * ``attn_core_split``  the same with the key axis cut into partitions whose
   summaries are merged afterwards (few query rows, many keys).
 * ``attn_split_workspace_bytes``.
+* ``attn_core_backward``  gradients of the attention core from the forward's
+  row statistics; ``attn_backward_workspace_bytes``.
 * ``mha_workspace_bytes``, ``mha_status_string``.
 """
 
@@ -23,7 +25,7 @@ import os
 
 __all__ = [
     "MhaError", "MhaDims", "MhaMask", "MhaBias", "lib", "mha_forward", "attn_core", "attn_core_split",
-    "attn_split_workspace_bytes",
+    "attn_split_workspace_bytes", "attn_core_backward", "attn_backward_workspace_bytes",
     "mha_workspace_bytes", "mha_status_string", "MHA_F32", "MHA_BF16", "MHA_F16",
     "MHA_MASK_CAUSAL", "MHA_MASK_KEY_PADDING", "MHA_MASK_BOOL", "MHA_MASK_ADDITIVE",
 ]
@@ -83,6 +85,11 @@ def lib():
         L.attn_core_split.argtypes = [P(MhaDims), P(MhaMask), vp, vp, vp, vp, vp, vp,
                                       ctypes.c_int32, vp, ctypes.c_size_t, vp]
         L.attn_core_split.restype = ctypes.c_int
+        L.attn_backward_workspace_bytes.argtypes = [P(MhaDims)]
+        L.attn_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_core_backward.argtypes = [P(MhaDims), P(MhaMask)] + [vp] * 11 + [ctypes.c_size_t,
+                                                                                vp]
+        L.attn_core_backward.restype = ctypes.c_int
         L.mha_status_string.argtypes = [ctypes.c_int]
         L.mha_status_string.restype = ctypes.c_char_p
         L.mha_max_head_dim.argtypes = []
@@ -274,3 +281,39 @@ def attn_core_split(Qh, Kh, Vh, *, splits=0, scale=None, causal=False, key_len=N
     if st != 0:
         raise MhaError(st, "attn_core_split")
     return Z
+
+
+def attn_backward_workspace_bytes(dims: MhaDims):
+    return int(lib().attn_backward_workspace_bytes(ctypes.byref(dims) if dims is not None
+                                                   else None))
+
+
+def attn_core_backward(Qh, Kh, Vh, Z, dZ, row_m, row_l, *, scale=None, causal=False,
+                       key_len=None, allowed=None, add=None, dQh=None, dKh=None, dVh=None,
+                       workspace=None, stream=None):
+    """Gradients (dQh, dKh, dVh) of a loss with upstream gradient dZ for the
+    attention core; Z, row_m and row_l come from the same forward call (same
+    masks and scale).  Gradients have the element type of Z and dZ."""
+    torch = _torch()
+    if dZ.dtype != Z.dtype:
+        raise TypeError("Z and dZ must share one element type")
+    dims = _core_dims(Qh, Kh, Vh, scale, Z.dtype)
+    B, h, n_q, n_k, d_h, d_vh = dims.B, dims.h, dims.n_q, dims.n_k, dims.d_h, dims.d_vh
+    m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Qh.device, add)
+    if dQh is None:
+        dQh = torch.empty((B, h, n_q, d_h), dtype=Z.dtype, device=Qh.device)
+    if dKh is None:
+        dKh = torch.empty((B, h, n_k, d_h), dtype=Z.dtype, device=Qh.device)
+    if dVh is None:
+        dVh = torch.empty((B, h, n_k, d_vh), dtype=Z.dtype, device=Qh.device)
+    if workspace is None:
+        workspace = torch.empty(max(attn_backward_workspace_bytes(dims), 1), dtype=torch.uint8,
+                                device=Qh.device)
+    st = lib().attn_core_backward(ctypes.byref(dims), ctypes.byref(m), _ptr(Qh), _ptr(Kh),
+                                  _ptr(Vh), _ptr(Z), _ptr(dZ), _ptr(row_m), _ptr(row_l),
+                                  _ptr(dQh), _ptr(dKh), _ptr(dVh), _ptr(workspace),
+                                  workspace.numel(), _stream(stream))
+    del keep
+    if st != 0:
+        raise MhaError(st, "attn_core_backward")
+    return dQh, dKh, dVh

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libmha.so")
 
-SOURCES = ["api.hip", "gemm.hip", "attn_bf16.hip", "attn_f16.hip", "attn_f32.hip", "attn_merge.hip"]
+SOURCES = ["api.hip", "gemm.hip", "attn_bf16.hip", "attn_f16.hip", "attn_f32.hip", "attn_merge.hip",
+           "attn_bwd.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -33,7 +34,7 @@ FLAGS = [
 # register copies around the softmax arithmetic).  The GEMMs keep their
 # accumulators wherever the compiler prefers (accumulation registers).
 PER_SOURCE_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-                    for src in ("attn_bf16.hip", "attn_f16.hip", "attn_f32.hip")}
+                    for src in ("attn_bf16.hip", "attn_f16.hip", "attn_f32.hip", "attn_bwd.hip")}
 
 
 def _hipcc():

@@ -295,6 +295,81 @@ mha_status attn_core_split(const mha_dims* d, const mha_mask* m, const void* Qh,
   return MHA_OK;
 }
 
+size_t attn_backward_workspace_bytes(const mha_dims* d) {
+  if (check_core_dims(d) != MHA_OK) return 0;
+  return 2 * round256((size_t)d->B * d->h * d->n_q * 4);
+}
+
+mha_status attn_core_backward(const mha_dims* d, const mha_mask* m, const void* Qh,
+                              const void* Kh, const void* Vh, const void* Z, const void* dZ,
+                              const float* row_m, const float* row_l, void* dQh, void* dKh,
+                              void* dVh, void* workspace, size_t workspace_bytes, void* stream) {
+  mha_status s = check_core_dims(d);
+  if (s != MHA_OK) return s;
+  if (d->in_dtype == MHA_F32) return MHA_ERR_DTYPE;
+  if ((s = check_mask(d, m)) != MHA_OK) return s;
+  if (!Qh || !Kh || !Vh || !Z || !dZ || !row_m || !row_l || !dQh || !dKh || !dVh)
+    return MHA_ERR_NULL;
+  const size_t ei = esize(d->in_dtype), eo = esize(d->out_dtype);
+  if (!aligned(Qh, ei) || !aligned(Kh, ei) || !aligned(Vh, ei) || !aligned(Z, eo) ||
+      !aligned(dZ, eo) || !aligned(row_m, 4) || !aligned(row_l, 4) || !aligned(dQh, eo) ||
+      !aligned(dKh, eo) || !aligned(dVh, eo))
+    return MHA_ERR_ALIGN;
+  const size_t rows = (size_t)d->B * d->h * d->n_q;
+  if (!workspace || workspace_bytes < attn_backward_workspace_bytes(d)) return MHA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MHA_ERR_ALIGN;
+  mha::AttnBwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.Q = Qh;
+  p.K = Kh;
+  p.V = Vh;
+  p.Z = Z;
+  p.dZ = dZ;
+  p.row_m = row_m;
+  p.row_l = row_l;
+  p.dQ = dQh;
+  p.dK = dKh;
+  p.dV = dVh;
+  p.lse2 = static_cast<float*>(workspace);
+  p.dsum = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(rows * 4));
+  p.B = d->B;
+  p.h = d->h;
+  p.n_q = d->n_q;
+  p.n_k = d->n_k;
+  p.d_h = d->d_h;
+  p.d_vh = d->d_vh;
+  p.ldz = d->h * d->d_vh;
+  p.scale = d->scale;
+  p.scale_log2 = d->scale * 1.4426950408889634f;
+  p.elem_dtype = d->in_dtype;
+  p.z_dtype = d->out_dtype;
+  p.g_dtype = d->out_dtype;
+  if (m) {
+    p.causal = (m->flags & MHA_MASK_CAUSAL) ? 1 : 0;
+    if (m->flags & MHA_MASK_KEY_PADDING) p.key_len = m->key_len;
+    if (m->flags & MHA_MASK_BOOL) {
+      p.allowed = m->allowed;
+      p.allowed_batch_stride = m->allowed_batch_stride;
+    }
+    if (m->flags & MHA_MASK_ADDITIVE) {
+      p.add = m->add;
+      p.add_batch_stride = m->add_batch_stride;
+    }
+  }
+  const int vin = vec_elems(d->in_dtype), vz = vec_elems(d->out_dtype);
+  p.vec_q = aligned(Qh, 16) && d->d_h % vin == 0;
+  p.vec_k = aligned(Kh, 16) && d->d_h % vin == 0;
+  p.vec_v = aligned(Vh, 16) && d->d_vh % vin == 0;
+  p.vec_z = aligned(dZ, 16) && d->d_vh % vz == 0;
+  const size_t a4 = 4 * eo;   // four-element stores
+  p.vec_dq = aligned(dQh, a4) && d->d_h % 4 == 0;
+  p.vec_dk = aligned(dKh, a4) && d->d_h % 4 == 0;
+  p.vec_dv = aligned(dVh, a4) && d->d_vh % 4 == 0;
+  if (mha::launch_attention_backward(p, d->in_dtype, (hipStream_t)stream) != hipSuccess)
+    return MHA_ERR_LAUNCH;
+  return MHA_OK;
+}
+
 mha_status mha_forward(const mha_dims* d, const mha_mask* m, const void* Q, const void* K,
                        const void* V, const void* W_Q, const void* W_K, const void* W_V,
                        const void* W_O, const mha_bias* bias, void* Y, float* row_m,

@@ -1,0 +1,53 @@
+// Launches of the attention backward pass (bf16 and fp16 heads).
+#include "attn_bwd.hpp"
+
+namespace mha {
+
+template <typename T, int DH, int DV>
+static hipError_t launch_bwd_fixed(const AttnBwdParams& p, hipStream_t stream) {
+  const long long BH = (long long)p.B * p.h;
+  const long long gkv = (long long)((p.n_k + 127) / 128) * BH;
+  const long long gq = (long long)((p.n_q + 127) / 128) * BH;
+  if (gkv > 2147483647LL || gq > 2147483647LL) return hipErrorInvalidValue;
+  if (gkv > 0)
+    hipLaunchKernelGGL((attn_bwd_kv_kernel<T, DH, DV>), dim3((unsigned)gkv), dim3(256), 0, stream,
+                       p);
+  if (gq > 0)
+    hipLaunchKernelGGL((attn_bwd_q_kernel<T, DH, DV>), dim3((unsigned)gq), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int DH>
+static hipError_t launch_bwd_dv(const AttnBwdParams& p, hipStream_t stream) {
+  if (p.d_vh <= 32) return launch_bwd_fixed<T, DH, 32>(p, stream);
+  if (p.d_vh <= 64) return launch_bwd_fixed<T, DH, 64>(p, stream);
+  if (p.d_vh <= 96) return launch_bwd_fixed<T, DH, 96>(p, stream);
+  if (p.d_vh <= 128) return launch_bwd_fixed<T, DH, 128>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t launch_bwd_typed(const AttnBwdParams& p, hipStream_t stream) {
+  if (p.d_h <= 32) return launch_bwd_dv<T, 32>(p, stream);
+  if (p.d_h <= 64) return launch_bwd_dv<T, 64>(p, stream);
+  if (p.d_h <= 128) return launch_bwd_dv<T, 128>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attention_backward(const AttnBwdParams& p, int elem_dtype, hipStream_t stream) {
+  const size_t rows = (size_t)p.B * p.h * p.n_q;
+  if (rows > 0) {
+    const size_t blocks = (rows + 3) / 4;   // four (row, head) waves per workgroup
+    if (blocks > 2147483647ULL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  switch (elem_dtype) {
+    case kBF16: return launch_bwd_typed<bf16>(p, stream);
+    case kF16: return launch_bwd_typed<f16>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mha

@@ -1,0 +1,516 @@
+// Backward pass of the fused attention core for gfx950 (2-byte elements,
+// fp32 accumulation).
+//
+// The pages define the forward pass only; the gradients follow from it by
+// calculus.  For one head with scores S = c Q K^T (+ M), weights A = the
+// masked row softmax of S and output Z = A V, and an upstream gradient dZ:
+//   dV = A^T dZ,   dA = dZ V^T,   dS = A o (dA - D),  D_i = sum_e dZ_ie Z_ie,
+//   dQ = c dS K,   dK = c dS^T Q.
+// The weights are recomputed block by block from the forward's row
+// statistics: page "Stable summary of an attention key block", Definition,
+// gives A_ij = e^(s_ij - m_i) / l_i for the final (m, l) of row i, so no
+// n_q x n_k matrix is stored.  Here A_ij = 2^(s_ij c log2(e) - L_i) with
+// L_i = m_i log2(e) + log2(l_i) prepared once per row (attn_bwd_prep_kernel,
+// which also forms D_i).
+//
+// Mapping onto the matrix cores (ours), with the 32x32x16 MFMA whose result
+// acc[i] holds row 8 (i/4) + 4 g + (i%4), column l % 32:
+// * attn_bwd_kv_kernel: a wave owns 32 keys; query tiles of 64 rows of Q and
+//   dZ stream through LDS.  S = Q K^T and dA = dZ V^T put one key per lane
+//   (K and V rows are the B operands, held in registers), so A and dS come
+//   out in the B-operand layout of dV^T += dZ^T A and dK^T += Q^T dS, whose
+//   A operands (dZ^T, Q^T) are read from row-major LDS tiles with the
+//   transposing load, exactly as the forward reads V^T.
+// * attn_bwd_q_kernel: a wave owns 32 queries, key tiles stream through LDS
+//   (the forward's structure): S^T = K Q^T and dA^T = V dZ^T put one query
+//   per lane, and dQ^T += K^T dS^T reads K^T with the transposing load.
+// Two kernels instead of one with atomic dQ updates: the sums are formed in
+// a fixed order, so runs are deterministic.
+#pragma once
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace mha {
+
+template <int DH, int DV>
+struct BwdCfg {
+  static constexpr int WAVES = 4;
+  static constexpr int NT = 64 * WAVES;
+  static constexpr int VEC = 8;              // 2-byte elements per 16-byte chunk
+  static constexpr int BR = 64;              // rows of a streamed tile
+  static constexpr int KCH = DH / 16;        // MFMA k-chunks over d_h
+  static constexpr int VCH = DV / 16;        // MFMA k-chunks over d_vh
+  static constexpr int NDH = DH / 32;        // 32-row blocks of dK^T / dQ^T
+  static constexpr int NDV = DV / 32;        // 32-row blocks of dV^T
+  static constexpr int HROW = DH + 8;        // LDS row strides (elements): 16 bytes of
+  static constexpr int VROW = DV + 8;        // padding stagger the rows over the banks
+  static constexpr int HTILE = BR * HROW, VTILE = BR * VROW;
+  static constexpr int H_PER_T = (BR * DH / VEC + NT - 1) / NT;
+  static constexpr int V_PER_T = (BR * DV / VEC + NT - 1) / NT;
+  // waves per SIMD the dK/dV kernel's registers must allow: two (at most
+  // 256 VGPRs) unless its accumulators and operand rows need more
+  static constexpr int KV_OCC = (DH + DV <= 160) ? 2 : 1;
+  static_assert(DH % 32 == 0 && DV % 32 == 0, "head widths are multiples of 32");
+};
+
+// Eight consecutive elements of a row of element type `dtype` (fp32, bf16
+// or fp16) at `base + off`, columns col..col+7 of `ncols` valid ones (zero
+// past the end), rounded to T (nearest even).
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::vec load8_as(const void* base, int dtype, size_t off,
+                                                          int col, int ncols, bool vec_ok) {
+  typedef typename Elem<T>::vec V;
+  if (dtype == kF32) {
+    const float* row = reinterpret_cast<const float*>(base) + off;
+    floatx8 f;
+    if (vec_ok && col + 8 <= ncols) {
+      const floatx4 a = *reinterpret_cast<const floatx4*>(row + col);
+      const floatx4 b = *reinterpret_cast<const floatx4*>(row + col + 4);
+      f = floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    } else {
+      #pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = (col + e < ncols) ? row[col + e] : 0.f;
+    }
+    return __builtin_convertvector(f, V);
+  } else if (dtype == kBF16) {
+    return convert_chunk<T, bf16>(
+        load_chunk<bf16>(reinterpret_cast<const bf16*>(base) + off, col, ncols, vec_ok));
+  } else {
+    return convert_chunk<T, f16>(
+        load_chunk<f16>(reinterpret_cast<const f16*>(base) + off, col, ncols, vec_ok));
+  }
+}
+
+__device__ __forceinline__ float load1_as(const void* base, int dtype, size_t idx) {
+  if (dtype == kF32) return reinterpret_cast<const float*>(base)[idx];
+  if (dtype == kBF16) return (float)reinterpret_cast<const bf16*>(base)[idx];
+  return (float)reinterpret_cast<const f16*>(base)[idx];
+}
+
+// Per row and head: D = sum_e dZ Z, and L = m log2(e) + log2(l) (+inf for a
+// row without allowed keys, whose weights are then all 0).  One wave per
+// (query row, head): consecutive waves take consecutive heads of one row of
+// the concatenation, so a workgroup reads contiguous memory; lanes take
+// elements e and e + 64 and the wave sums its lanes.  dZ enters D rounded to
+// the element type, as it enters the products dA = dZ V^T: D then matches
+// the row sum sum_j A_ij dA_ij of the rounded dZ, and dA - D carries no
+// rounding mismatch into the cancellation between the two.
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(AttnBwdParams p) {
+  const int lane = threadIdx.x & 63;
+  const size_t pair = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (b*n_q + q)*h + r
+  const size_t npairs = (size_t)p.B * p.n_q * p.h;
+  if (pair >= npairs) return;                                        // whole wave
+  const size_t row = pair / p.h;                                     // b*n_q + q
+  const int r = (int)(pair - row * p.h);
+  const int b = (int)(row / p.n_q);
+  const int qi = (int)(row - (size_t)b * p.n_q);
+  const size_t off = row * p.ldz + (size_t)r * p.d_vh;
+  float acc = 0.f;
+  for (int e = lane; e < p.d_vh; e += 64) {
+    const float dz = load1_as(p.dZ, p.z_dtype, off + e);
+    const float dzr = p.elem_dtype == kBF16 ? (float)(bf16)dz : (float)(f16)dz;
+    acc = fmaf(dzr, load1_as(p.Z, p.z_dtype, off + e), acc);
+  }
+  #pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (lane == 0) {
+    const size_t idx = ((size_t)b * p.h + r) * p.n_q + qi;
+    p.dsum[idx] = acc;
+    const float m = p.row_m[idx], l = p.row_l[idx];
+    p.lse2[idx] = (l > 0.f && m != -INFINITY) ? fmaf(m, kLog2e, __log2f(l)) : INFINITY;
+  }
+}
+
+// Stage one 64-row tile of a row-major [rows x ncols] array (row stride ld,
+// element type dtype) into LDS rows of ROW elements, rounded to T; rows past
+// `nrows` and columns past `ncols` are zero.
+template <typename T, int D, int ROW, int PER_T, int NT>
+struct TileStager {
+  typedef typename Elem<T>::vec vec;
+  vec reg[PER_T];
+  __device__ __forceinline__ void load(const void* base, int dtype, size_t row0_off, size_t ld,
+                                       int r0, int nrows, int ncols, bool vec_ok, int tid) {
+    #pragma unroll
+    for (int t = 0; t < PER_T; ++t) {
+      const int ci = tid + t * NT;
+      if ((64 * D / 8) % NT != 0 && ci >= 64 * D / 8) continue;
+      const int row = ci / (D / 8), col = (ci - row * (D / 8)) * 8;
+      reg[t] = (r0 + row < nrows)
+                   ? load8_as<T>(base, dtype, row0_off + (size_t)(r0 + row) * ld, col, ncols, vec_ok)
+                   : zero_vec<vec>();
+    }
+  }
+  __device__ __forceinline__ void store(T* tile, int tid) const {
+    #pragma unroll
+    for (int t = 0; t < PER_T; ++t) {
+      const int ci = tid + t * NT;
+      if ((64 * D / 8) % NT != 0 && ci >= 64 * D / 8) continue;
+      const int row = ci / (D / 8), col = (ci - row * (D / 8)) * 8;
+      *reinterpret_cast<vec*>(&tile[row * ROW + col]) = reg[t];
+    }
+  }
+};
+
+// Is key `key` allowed for query `q` of item b (general rules; n_q, n_k and
+// key padding bounds included)?
+__device__ __forceinline__ bool bwd_allowed(const AttnBwdParams& p, const uint8_t* G, int q,
+                                            int key, int kvalid) {
+  if (q >= p.n_q || key >= kvalid) return false;
+  if (p.causal && key > q) return false;
+  if (G != nullptr && G[(size_t)q * p.n_k + key] == 0) return false;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (128 keys, b*h + r); a wave owns 32 keys.
+// ---------------------------------------------------------------------------
+template <typename T, int DH, int DV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BwdCfg<DH, DV>::KV_OCC, 2)))
+void attn_bwd_kv_kernel(AttnBwdParams p) {
+  typedef BwdCfg<DH, DV> C;
+  typedef typename Elem<T>::vec vec;
+  typedef typename Elem<T>::vec4 vec4;
+  __shared__ __attribute__((aligned(16))) T Qs[2][C::HTILE];
+  __shared__ __attribute__((aligned(16))) T Zs[2][C::VTILE];
+  __shared__ float Ls[2][C::BR], Ds[2][C::BR];
+  constexpr int tdt = __is_same(T, bf16) ? kBF16 : kF16;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int BH = p.B * p.h;
+  const int kt = blockIdx.x / BH;             // key tile (earliest keys first: most queries)
+  const int bh = blockIdx.x - kt * BH;
+  const int b = bh / p.h, r = bh - b * p.h;
+  const int k0 = kt * 128, k0w = k0 + 32 * wave;
+  const int key = k0w + l32;                  // this lane's key
+  int kvalid = p.n_k;
+  if (p.key_len) kvalid = min(kvalid, p.key_len[b]);
+
+  const T* Qb = reinterpret_cast<const T*>(p.Q) + (size_t)bh * p.n_q * p.d_h;
+  const T* Kb = reinterpret_cast<const T*>(p.K) + (size_t)bh * p.n_k * p.d_h;
+  const T* Vb = reinterpret_cast<const T*>(p.V) + (size_t)bh * p.n_k * p.d_vh;
+  const size_t zoff = (size_t)b * p.n_q * p.ldz + (size_t)r * p.d_vh;   // row 0 of this head
+  const uint8_t* G = p.allowed ? p.allowed + (size_t)b * p.allowed_batch_stride : nullptr;
+  const float* M = p.add ? p.add + (size_t)b * p.add_batch_stride : nullptr;
+  const float* lse = p.lse2 + (size_t)bh * p.n_q;
+  const float* dsm = p.dsum + (size_t)bh * p.n_q;
+
+  // this lane's key row of K and V as B operands (k-chunk c: elements
+  // 16 c + 8 g .. +7); keys past n_k read as zero
+  vec kf[C::KCH], vf[C::VCH];
+  #pragma unroll
+  for (int c = 0; c < C::KCH; ++c)
+    kf[c] = key < p.n_k ? load_chunk<T>(Kb + (size_t)key * p.d_h, 16 * c + 8 * g, p.d_h, p.vec_k)
+                        : zero_vec<vec>();
+  #pragma unroll
+  for (int c = 0; c < C::VCH; ++c)
+    vf[c] = key < p.n_k ? load_chunk<T>(Vb + (size_t)key * p.d_vh, 16 * c + 8 * g, p.d_vh, p.vec_v)
+                        : zero_vec<vec>();
+
+  floatx16 dk[C::NDH], dv[C::NDV];
+  #pragma unroll
+  for (int d = 0; d < C::NDH; ++d)
+    #pragma unroll
+    for (int i = 0; i < 16; ++i) dk[d][i] = 0.f;
+  #pragma unroll
+  for (int d = 0; d < C::NDV; ++d)
+    #pragma unroll
+    for (int i = 0; i < 16; ++i) dv[d][i] = 0.f;
+
+  // query tiles that can reach this key tile: causal needs q >= key
+  const int qb0 = (p.causal ? k0 : 0) / C::BR;
+  const int nqb = (k0 < kvalid) ? (p.n_q + C::BR - 1) / C::BR : qb0;   // padded keys only: none
+
+  TileStager<T, DH, C::HROW, C::H_PER_T, C::NT> qst;
+  TileStager<T, DV, C::VROW, C::V_PER_T, C::NT> zst;
+  float lreg = 0.f, dreg = 0.f;
+  auto load_tile = [&](int qb) {
+    const int q0 = qb * C::BR;
+    qst.load(Qb, tdt, 0, p.d_h, q0, p.n_q, p.d_h, p.vec_q, tid);
+    zst.load(p.dZ, p.z_dtype, zoff, p.ldz, q0, p.n_q, p.d_vh, p.vec_z, tid);
+    if (tid < C::BR) {
+      const int q = q0 + tid;
+      lreg = q < p.n_q ? lse[q] : INFINITY;
+      dreg = q < p.n_q ? dsm[q] : 0.f;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    qst.store(Qs[buf], tid);
+    zst.store(Zs[buf], tid);
+    if (tid < C::BR) {
+      Ls[buf][tid] = lreg;
+      Ds[buf][tid] = dreg;
+    }
+  };
+
+  if (nqb > qb0) {
+    load_tile(qb0);
+    store_tile(0);
+  }
+  __syncthreads();
+  if (nqb > qb0 + 1) load_tile(qb0 + 1);
+
+  const int srow = 4 * g + ((lane & 15) >> 2);
+  const int scol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const float cs = p.scale_log2;
+
+  for (int qb = qb0; qb < nqb; ++qb) {
+    const int cur = (qb - qb0) & 1;
+    const T* qs = Qs[cur];
+    const T* zs = Zs[cur];
+    const int q0 = qb * C::BR;
+    #pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int qs0 = q0 + 32 * sb;
+      // whole sub-block before this wave's first key (causal), or every key
+      // of the wave padded: nothing to add
+      if ((p.causal && qs0 + 31 < k0w) || k0w >= kvalid || qs0 >= p.n_q) continue;
+      floatx16 sacc, dpacc;
+      #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sacc[i] = 0.f;
+        dpacc[i] = 0.f;
+      }
+      // S = Q K^T (lane: key l32; registers: queries), dA = dZ V^T
+      #pragma unroll
+      for (int c = 0; c < C::KCH; ++c) {
+        const vec qa = *reinterpret_cast<const vec*>(&qs[(32 * sb + l32) * C::HROW + 16 * c + 8 * g]);
+        mfma_chunk(sacc, qa, kf[c]);
+      }
+      #pragma unroll
+      for (int c = 0; c < C::VCH; ++c) {
+        const vec za = *reinterpret_cast<const vec*>(&zs[(32 * sb + l32) * C::VROW + 16 * c + 8 * g]);
+        mfma_chunk(dpacc, za, vf[c]);
+      }
+      // A and dS; query of slot i: q0 + 32 sb + 8 (i/4) + 4 g + i%4
+      const bool need_mask = (p.causal && qs0 < k0w + 31) || (k0w + 31 >= kvalid) ||
+                             (qs0 + 31 >= p.n_q) || G != nullptr || M != nullptr;
+      #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int ql = 32 * sb + 8 * (i >> 2) + 4 * g + (i & 3);
+        const int q = q0 + ql;
+        float x = sacc[i] * cs;
+        bool ok = true;
+        if (need_mask) {
+          ok = bwd_allowed(p, G, q, key, kvalid);
+          if (M != nullptr && ok) x = fmaf(M[(size_t)q * p.n_k + key], kLog2e, x);
+        }
+        const float a = ok ? __builtin_amdgcn_exp2f(x - Ls[cur][ql]) : 0.f;
+        sacc[i] = a;
+        dpacc[i] = a * (dpacc[i] - Ds[cur][ql]);
+      }
+      // dV^T += dZ^T A and dK^T += Q^T dS; slot t of chunk st is query
+      // 16 st + 4 g + t (t < 4) or 16 st + 8 + 4 g + (t - 4), as in the
+      // transposing read below
+      #pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        floatx8 af, sf;
+        #pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          af[t] = sacc[8 * st + t];
+          sf[t] = dpacc[8 * st + t];
+        }
+        const vec ab = Cvt<T>::eight(af);
+        const vec sbv = Cvt<T>::eight(sf);
+        #pragma unroll
+        for (int d = 0; d < C::NDV; ++d) {
+          const T* v0 = &zs[(32 * sb + 16 * st + srow) * C::VROW + d * 32 + scol];
+          const vec4 lo = lds_read_tr4<T>(v0);
+          const vec4 hi = lds_read_tr4<T>(v0 + 8 * C::VROW);
+          const vec za = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          mfma_chunk(dv[d], za, ab);
+        }
+        #pragma unroll
+        for (int d = 0; d < C::NDH; ++d) {
+          const T* q0p = &qs[(32 * sb + 16 * st + srow) * C::HROW + d * 32 + scol];
+          const vec4 lo = lds_read_tr4<T>(q0p);
+          const vec4 hi = lds_read_tr4<T>(q0p + 8 * C::HROW);
+          const vec qa = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          mfma_chunk(dk[d], qa, sbv);
+        }
+      }
+    }
+    if (qb + 1 < nqb) store_tile(cur ^ 1);
+    __syncthreads();
+    if (qb + 2 < nqb) load_tile(qb + 2);
+  }
+
+  // dK = c (dK^T)^T, dV = (dV^T)^T: lane writes its key's row
+  if (key < p.n_k) {
+    const size_t kro = ((size_t)bh * p.n_k + key) * p.d_h;
+    const size_t vro = ((size_t)bh * p.n_k + key) * p.d_vh;
+    #pragma unroll
+    for (int d = 0; d < C::NDH; ++d)
+      #pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int e0 = d * 32 + 8 * a + 4 * g;
+        store4(p.dK, p.g_dtype, kro + e0, p.vec_dk, p.d_h - e0, dk[d][4 * a] * p.scale,
+               dk[d][4 * a + 1] * p.scale, dk[d][4 * a + 2] * p.scale, dk[d][4 * a + 3] * p.scale);
+      }
+    #pragma unroll
+    for (int d = 0; d < C::NDV; ++d)
+      #pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int e0 = d * 32 + 8 * a + 4 * g;
+        store4(p.dV, p.g_dtype, vro + e0, p.vec_dv, p.d_vh - e0, dv[d][4 * a], dv[d][4 * a + 1],
+               dv[d][4 * a + 2], dv[d][4 * a + 3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (128 queries, b*h + r); a wave owns 32 queries.
+// ---------------------------------------------------------------------------
+template <typename T, int DH, int DV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_q_kernel(AttnBwdParams p) {
+  typedef BwdCfg<DH, DV> C;
+  typedef typename Elem<T>::vec vec;
+  typedef typename Elem<T>::vec4 vec4;
+  __shared__ __attribute__((aligned(16))) T Ks[2][C::HTILE];
+  __shared__ __attribute__((aligned(16))) T Vs[2][C::VTILE];
+  constexpr int tdt = __is_same(T, bf16) ? kBF16 : kF16;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int BH = p.B * p.h;
+  const int nqt = (p.n_q + 127) / 128;
+  const int qt_rank = blockIdx.x / BH;
+  const int bh = blockIdx.x - qt_rank * BH;
+  const int qt = p.causal ? (nqt - 1 - qt_rank) : qt_rank;   // causal: most keys first
+  const int b = bh / p.h, r = bh - b * p.h;
+  const int q0 = qt * 128, q0w = q0 + 32 * wave;
+  const int qi = q0w + l32;                    // this lane's query
+  int kvalid = p.n_k;
+  if (p.key_len) kvalid = min(kvalid, p.key_len[b]);
+  int kend = kvalid;
+  if (p.causal) kend = min(kend, q0 + 128);
+  const int nkb = kend > 0 ? (kend + C::BR - 1) / C::BR : 0;
+
+  const T* Qb = reinterpret_cast<const T*>(p.Q) + (size_t)bh * p.n_q * p.d_h;
+  const T* Kb = reinterpret_cast<const T*>(p.K) + (size_t)bh * p.n_k * p.d_h;
+  const T* Vb = reinterpret_cast<const T*>(p.V) + (size_t)bh * p.n_k * p.d_vh;
+  const size_t zrow = ((size_t)b * p.n_q + qi) * p.ldz + (size_t)r * p.d_vh;
+  const uint8_t* G = p.allowed ? p.allowed + (size_t)b * p.allowed_batch_stride : nullptr;
+  const float* M = p.add ? p.add + (size_t)b * p.add_batch_stride : nullptr;
+
+  // this lane's query row of Q and dZ as B operands
+  vec qf[C::KCH], zf[C::VCH];
+  #pragma unroll
+  for (int c = 0; c < C::KCH; ++c)
+    qf[c] = qi < p.n_q ? load_chunk<T>(Qb + (size_t)qi * p.d_h, 16 * c + 8 * g, p.d_h, p.vec_q)
+                       : zero_vec<vec>();
+  #pragma unroll
+  for (int c = 0; c < C::VCH; ++c)
+    zf[c] = qi < p.n_q ? load8_as<T>(p.dZ, p.z_dtype, zrow, 16 * c + 8 * g, p.d_vh, p.vec_z)
+                       : zero_vec<vec>();
+  const float Lq = qi < p.n_q ? p.lse2[(size_t)bh * p.n_q + qi] : INFINITY;
+  const float Dq = qi < p.n_q ? p.dsum[(size_t)bh * p.n_q + qi] : 0.f;
+
+  floatx16 dq[C::NDH];
+  #pragma unroll
+  for (int d = 0; d < C::NDH; ++d)
+    #pragma unroll
+    for (int i = 0; i < 16; ++i) dq[d][i] = 0.f;
+
+  TileStager<T, DH, C::HROW, C::H_PER_T, C::NT> kst;
+  TileStager<T, DV, C::VROW, C::V_PER_T, C::NT> vst;
+  auto load_tile = [&](int kb) {
+    const int kk0 = kb * C::BR;
+    kst.load(Kb, tdt, 0, p.d_h, kk0, p.n_k, p.d_h, p.vec_k, tid);
+    vst.load(Vb, tdt, 0, p.d_vh, kk0, p.n_k, p.d_vh, p.vec_v, tid);
+  };
+  auto store_tile = [&](int buf) {
+    kst.store(Ks[buf], tid);
+    vst.store(Vs[buf], tid);
+  };
+  if (nkb > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  if (nkb > 1) load_tile(1);
+
+  const int srow = 4 * g + ((lane & 15) >> 2);
+  const int scol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const float cs = p.scale_log2;
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int cur = kb & 1;
+    const T* ks = Ks[cur];
+    const T* vs = Vs[cur];
+    const int kk0 = kb * C::BR;
+    #pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int ks0 = kk0 + 32 * sb;
+      if ((p.causal && ks0 > q0w + 31) || ks0 >= kvalid || q0w >= p.n_q) continue;
+      floatx16 sacc, dpacc;
+      #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sacc[i] = 0.f;
+        dpacc[i] = 0.f;
+      }
+      // S^T = K Q^T (lane: query l32; registers: keys), dA^T = V dZ^T
+      #pragma unroll
+      for (int c = 0; c < C::KCH; ++c) {
+        const vec ka = *reinterpret_cast<const vec*>(&ks[(32 * sb + l32) * C::HROW + 16 * c + 8 * g]);
+        mfma_chunk(sacc, ka, qf[c]);
+      }
+      #pragma unroll
+      for (int c = 0; c < C::VCH; ++c) {
+        const vec va = *reinterpret_cast<const vec*>(&vs[(32 * sb + l32) * C::VROW + 16 * c + 8 * g]);
+        mfma_chunk(dpacc, va, zf[c]);
+      }
+      const bool need_mask = (p.causal && ks0 + 31 > q0w) || (ks0 + 31 >= kvalid) ||
+                             (q0w + 31 >= p.n_q) || G != nullptr || M != nullptr;
+      #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = ks0 + 8 * (i >> 2) + 4 * g + (i & 3);
+        float x = sacc[i] * cs;
+        bool ok = true;
+        if (need_mask) {
+          ok = bwd_allowed(p, G, qi, key, kvalid);
+          if (M != nullptr && ok) x = fmaf(M[(size_t)qi * p.n_k + key], kLog2e, x);
+        }
+        const float a = ok ? __builtin_amdgcn_exp2f(x - Lq) : 0.f;
+        sacc[i] = a * (dpacc[i] - Dq);         // dS^T
+      }
+      // dQ^T += K^T dS^T (slot permutation as in the forward's value product)
+      #pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        floatx8 sf;
+        #pragma unroll
+        for (int t = 0; t < 8; ++t) sf[t] = sacc[8 * st + t];
+        const vec sbv = Cvt<T>::eight(sf);
+        #pragma unroll
+        for (int d = 0; d < C::NDH; ++d) {
+          const T* k0p = &ks[(32 * sb + 16 * st + srow) * C::HROW + d * 32 + scol];
+          const vec4 lo = lds_read_tr4<T>(k0p);
+          const vec4 hi = lds_read_tr4<T>(k0p + 8 * C::HROW);
+          const vec ka = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          mfma_chunk(dq[d], ka, sbv);
+        }
+      }
+    }
+    if (kb + 1 < nkb) store_tile(cur ^ 1);
+    __syncthreads();
+    if (kb + 2 < nkb) load_tile(kb + 2);
+  }
+
+  if (qi < p.n_q) {
+    const size_t qro = ((size_t)bh * p.n_q + qi) * p.d_h;
+    #pragma unroll
+    for (int d = 0; d < C::NDH; ++d)
+      #pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int e0 = d * 32 + 8 * a + 4 * g;
+        store4(p.dQ, p.g_dtype, qro + e0, p.vec_dq, p.d_h - e0, dq[d][4 * a] * p.scale,
+               dq[d][4 * a + 1] * p.scale, dq[d][4 * a + 2] * p.scale, dq[d][4 * a + 3] * p.scale);
+      }
+  }
+}
+
+}  // namespace mha

@@ -89,6 +89,43 @@ hipError_t launch_attention(const AttnParams& p, int elem_dtype, hipStream_t str
 // partitions' summaries and writes Z (and row_m / row_l).
 hipError_t launch_attention_split(const AttnParams& p, int elem_dtype, hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// Attention backward: gradients of a scalar loss with respect to Qh, Kh, Vh
+// given dZ (its gradient with respect to the concatenated output) and the
+// forward's row statistics (m, l).
+// ---------------------------------------------------------------------------
+struct AttnBwdParams {
+  const void* Q;     // [B, h, n_q, d_h]   (element type T)
+  const void* K;     // [B, h, n_k, d_h]
+  const void* V;     // [B, h, n_k, d_vh]
+  const void* Z;     // [B, n_q, ldz], head r at column r*d_vh   (z_dtype)
+  const void* dZ;    // same layout and type as Z
+  const float* row_m;  // [B, h, n_q] natural-log units
+  const float* row_l;  // [B, h, n_q]
+  void* dQ;          // [B, h, n_q, d_h]   (g_dtype)
+  void* dK;          // [B, h, n_k, d_h]
+  void* dV;          // [B, h, n_k, d_vh]
+  float* lse2;       // workspace [B, h, n_q]: m log2(e) + log2(l), +inf for an empty row
+  float* dsum;       // workspace [B, h, n_q]: sum_e dZ Z per row and head
+  const int32_t* key_len;
+  const uint8_t* allowed;
+  long long allowed_batch_stride;
+  const float* add;
+  long long add_batch_stride;
+  int B, h, n_q, n_k, d_h, d_vh;
+  int ldz;
+  float scale;       // c
+  float scale_log2;  // c log2(e)
+  int causal;
+  int elem_dtype;    // T: element type of Q, K, V and of the MFMA operands
+  int z_dtype, g_dtype;
+  int vec_q, vec_k, vec_v, vec_z;    // 16-byte loads allowed
+  int vec_dq, vec_dk, vec_dv;        // 4-element vector stores allowed
+};
+
+// The three launches of the backward pass on `stream` (2-byte elements).
+hipError_t launch_attention_backward(const AttnBwdParams& p, int elem_dtype, hipStream_t stream);
+
 // Largest head widths with an instantiated kernel.
 constexpr int kMaxHeadDim = 128;
 

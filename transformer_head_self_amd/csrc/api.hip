@@ -360,7 +360,7 @@ mha_status attn_core_backward(const mha_dims* d, const mha_mask* m, const void* 
   p.vec_q = aligned(Qh, 16) && d->d_h % vin == 0;
   p.vec_k = aligned(Kh, 16) && d->d_h % vin == 0;
   p.vec_v = aligned(Vh, 16) && d->d_vh % vin == 0;
-  p.vec_z = aligned(dZ, 16) && d->d_vh % vz == 0;
+  p.vec_z = aligned(dZ, 16) && aligned(Z, 16) && d->d_vh % vz == 0;
   const size_t a4 = 4 * eo;   // four-element stores
   p.vec_dq = aligned(dQh, a4) && d->d_h % 4 == 0;
   p.vec_dk = aligned(dKh, a4) && d->d_h % 4 == 0;

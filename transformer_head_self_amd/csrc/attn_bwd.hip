@@ -37,9 +37,30 @@ static hipError_t launch_bwd_typed(const AttnBwdParams& p, hipStream_t stream) {
 hipError_t launch_attention_backward(const AttnBwdParams& p, int elem_dtype, hipStream_t stream) {
   const size_t rows = (size_t)p.B * p.h * p.n_q;
   if (rows > 0) {
-    const size_t blocks = (rows + 3) / 4;   // four (row, head) waves per workgroup
-    if (blocks > 2147483647ULL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    const bool vec = p.z_dtype != kF32 && p.vec_z && p.ldz % 8 == 0 &&
+                     (p.d_vh == 32 || p.d_vh == 64 || p.d_vh == 128);
+    if (vec) {
+      // 16-byte chunks, one per thread; 64 % (d_vh / 8) == 0, so one head's
+      // chunks never straddle two waves
+      const size_t blocks = ((size_t)p.B * p.n_q * p.ldz / 8 + 255) / 256;
+      if (blocks > 2147483647ULL) return hipErrorInvalidValue;
+      const dim3 grid((unsigned)blocks);
+      const bool bf = p.z_dtype == kBF16;
+      if (p.d_vh == 32) {
+        if (bf) hipLaunchKernelGGL((attn_bwd_prep_vec_kernel<bf16, 4>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((attn_bwd_prep_vec_kernel<f16, 4>), grid, dim3(256), 0, stream, p);
+      } else if (p.d_vh == 64) {
+        if (bf) hipLaunchKernelGGL((attn_bwd_prep_vec_kernel<bf16, 8>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((attn_bwd_prep_vec_kernel<f16, 8>), grid, dim3(256), 0, stream, p);
+      } else {
+        if (bf) hipLaunchKernelGGL((attn_bwd_prep_vec_kernel<bf16, 16>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((attn_bwd_prep_vec_kernel<f16, 16>), grid, dim3(256), 0, stream, p);
+      }
+    } else {
+      const size_t blocks = (rows + 3) / 4;   // four (row, head) waves per workgroup
+      if (blocks > 2147483647ULL) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

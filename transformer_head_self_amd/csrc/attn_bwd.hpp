@@ -89,13 +89,24 @@ __device__ __forceinline__ float load1_as(const void* base, int dtype, size_t id
 }
 
 // Per row and head: D = sum_e dZ Z, and L = m log2(e) + log2(l) (+inf for a
-// row without allowed keys, whose weights are then all 0).  One wave per
-// (query row, head): consecutive waves take consecutive heads of one row of
-// the concatenation, so a workgroup reads contiguous memory; lanes take
-// elements e and e + 64 and the wave sums its lanes.  dZ enters D rounded to
-// the element type, as it enters the products dA = dZ V^T: D then matches
-// the row sum sum_j A_ij dA_ij of the rounded dZ, and dA - D carries no
-// rounding mismatch into the cancellation between the two.
+// row without allowed keys, whose weights are then all 0).  dZ enters D
+// rounded to the element type, as it enters the products dA = dZ V^T: D then
+// matches the row sum sum_j A_ij dA_ij of the rounded dZ, and dA - D carries
+// no rounding mismatch into the cancellation between the two.
+__device__ __forceinline__ void bwd_row_terms(const AttnBwdParams& p, int b, int r, int qi,
+                                              float dsum) {
+  const size_t idx = ((size_t)b * p.h + r) * p.n_q + qi;
+  p.dsum[idx] = dsum;
+  const float m = p.row_m[idx], l = p.row_l[idx];
+  p.lse2[idx] = (l > 0.f && m != -INFINITY) ? fmaf(m, kLog2e, __log2f(l)) : INFINITY;
+}
+
+__device__ __forceinline__ float round_as(float x, int elem_dtype) {
+  return elem_dtype == kBF16 ? (float)(bf16)x : (float)(f16)x;
+}
+
+// General form: one wave per (query row, head); lanes take elements e and
+// e + 64, and the wave sums its lanes.
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(AttnBwdParams p) {
   const int lane = threadIdx.x & 63;
   const size_t pair = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (b*n_q + q)*h + r
@@ -104,21 +115,43 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(AttnBwdParams p) {
   const size_t row = pair / p.h;                                     // b*n_q + q
   const int r = (int)(pair - row * p.h);
   const int b = (int)(row / p.n_q);
-  const int qi = (int)(row - (size_t)b * p.n_q);
   const size_t off = row * p.ldz + (size_t)r * p.d_vh;
   float acc = 0.f;
-  for (int e = lane; e < p.d_vh; e += 64) {
-    const float dz = load1_as(p.dZ, p.z_dtype, off + e);
-    const float dzr = p.elem_dtype == kBF16 ? (float)(bf16)dz : (float)(f16)dz;
-    acc = fmaf(dzr, load1_as(p.Z, p.z_dtype, off + e), acc);
-  }
+  for (int e = lane; e < p.d_vh; e += 64)
+    acc = fmaf(round_as(load1_as(p.dZ, p.z_dtype, off + e), p.elem_dtype),
+               load1_as(p.Z, p.z_dtype, off + e), acc);
   #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (lane == 0) {
-    const size_t idx = ((size_t)b * p.h + r) * p.n_q + qi;
-    p.dsum[idx] = acc;
-    const float m = p.row_m[idx], l = p.row_l[idx];
-    p.lse2[idx] = (l > 0.f && m != -INFINITY) ? fmaf(m, kLog2e, __log2f(l)) : INFINITY;
+  if (lane == 0) bwd_row_terms(p, b, r, (int)(row - (size_t)b * p.n_q), acc);
+}
+
+// Vector form (2-byte Z and dZ, d_vh in {32, 64, 128}, 16-byte aligned
+// rows): the rows of the concatenation [B*n_q, h*d_vh] are read as 16-byte
+// chunks by consecutive threads; the CPH = d_vh / 8 consecutive lanes that
+// hold one head's chunks of a row sum them with lane exchanges.
+template <typename TZ, int CPH>
+__global__ __launch_bounds__(256) void attn_bwd_prep_vec_kernel(AttnBwdParams p) {
+  typedef typename Elem<TZ>::vec vec;
+  const size_t chunks = (size_t)p.B * p.n_q * p.ldz / 8;
+  const size_t ci = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const bool live = ci < chunks;
+  float acc = 0.f;
+  size_t row = 0;
+  int cr = 0;
+  if (live) {
+    const vec dz = reinterpret_cast<const vec*>(p.dZ)[ci];
+    const vec z = reinterpret_cast<const vec*>(p.Z)[ci];
+    #pragma unroll
+    for (int t = 0; t < 8; ++t) acc = fmaf(round_as((float)dz[t], p.elem_dtype), (float)z[t], acc);
+    const size_t per_row = (size_t)p.ldz / 8;
+    row = ci / per_row;
+    cr = (int)(ci - row * per_row);
+  }
+  #pragma unroll
+  for (int m = CPH / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (live && cr % CPH == 0) {
+    const int b = (int)(row / p.n_q);
+    bwd_row_terms(p, b, cr / CPH, (int)(row - (size_t)b * p.n_q), acc);
   }
 }
 

@@ -159,7 +159,7 @@ def decode_bench(args, torch):
         "data": "synthetic",
         "config": {"workload": f"decode-f16-B{B}-h{h}-nq1-nk{n_k}-d{d}",
                    "splits": "auto", "workspace_bytes": int(ws.numel())},
-        "roofline": {"bound": "hbm", "kernel": "attn_fwd_kernel (split) + split_merge_kernel",
+        "roofline": {"bound": "hbm", "kernel": "attn_decode_kernel + split_merge_kernel",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": nbytes},
         "unsplit_ms": round(ms_plain, 5),

@@ -886,3 +886,38 @@ def test_backward_full_size_two_heads():
             fro, mx = _grad_err(got[b, r], ref[name][0, 0])
             _say(f"  item {b} head {r} {name} normwise {fro:.3e} max {mx:.3e}")
             assert fro <= BWD_TOL["f16"][0] and mx <= BWD_TOL["f16"][1]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_split_decode_kernel_masks(dt):
+    """The decode-shaped partition kernel (one to four query rows) with a
+    causal square, a boolean mask with whole partitions forbidden, and an
+    additive bias with -inf entries; head widths that need 4, 8 and 16
+    lanes per row."""
+    rng = np.random.default_rng(90)
+    for (B, h, n_q, n_k, d_h, d_vh) in ((2, 3, 4, 4, 32, 32), (2, 2, 3, 1500, 64, 64),
+                                         (1, 2, 2, 900, 128, 96), (2, 2, 1, 777, 40, 24)):
+        _say(f"[decode masks] {dt} B={B} h={h} n_q={n_q} n_k={n_k} d={d_h}/{d_vh}")
+        Qh, Kh, Vh = make_heads(B, h, n_q, n_k, d_h, d_vh, "f32" if dt == "f16" else dt,
+                                seed=91 + n_k)
+        dev, host = _heads_dev(Qh, Kh, Vh, dt)
+        causal = n_q == n_k
+        G = rng.random((B, n_q, n_k)) < 0.5
+        G[:, :, 256:512] = False                         # forbidden partitions
+        G[:, :, 0] = True
+        M = _additive(rng, B, n_q, n_k)
+        c = 1.0 / math.sqrt(d_h)
+        allow = allowed_set(B, n_q, n_k, causal=causal, allowed=G)
+        ref = attn_core_ref(*host, c, allow, add=M)
+        rm = torch.empty((B, h, n_q), device=DEV)
+        rl = torch.empty_like(rm)
+        Z = mha.attn_core_split(*dev, splits=0 if n_k > 4 else 1, scale=c, causal=causal,
+                                allowed=torch.from_numpy(G).to(DEV),
+                                add=torch.from_numpy(M).to(DEV), row_m=rm, row_l=rl)
+        torch.cuda.synchronize()
+        err = _rel_err(Z.cpu().numpy(), ref["Z"])
+        _say(f"  Z err {err:.3e}")
+        # the inputs are exact; weights and sums stay in fp32 here
+        assert err <= 1e-4
+        np.testing.assert_allclose(rm.cpu().numpy(), ref["m"], rtol=0, atol=1e-5)
+        np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-5)

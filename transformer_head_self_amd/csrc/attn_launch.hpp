@@ -2,6 +2,7 @@
 #pragma once
 
 #include "attn.hpp"
+#include "attn_decode.hpp"
 #include "attn_pipe.hpp"
 
 namespace mha {
@@ -119,8 +120,40 @@ hipError_t launch_attn_split_dv(const AttnParams& p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+// Decode-shaped partitions: one to four query rows, 2-byte rows of up to 128
+// elements in whole 16-byte chunks.
+template <typename T, int G, int NQ>
+hipError_t launch_attn_decode(const AttnParams& p, hipStream_t stream) {
+  const long long grid = (long long)p.B * p.h * p.splits;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 2147483647LL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_decode_kernel<T, G, NQ>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int G>
+hipError_t launch_attn_decode_nq(const AttnParams& p, hipStream_t stream) {
+  if (p.n_q == 1) return launch_attn_decode<T, G, 1>(p, stream);
+  if (p.n_q == 2) return launch_attn_decode<T, G, 2>(p, stream);
+  return launch_attn_decode<T, G, 4>(p, stream);
+}
+
+template <typename T>
+bool decode_applies(const AttnParams& p) {
+  return sizeof(T) == 2 && p.n_q <= 4 && p.d_h % 8 == 0 && p.d_vh % 8 == 0 && p.d_h <= 128 &&
+         p.d_vh <= 128 && p.vec_q && p.vec_k && p.vec_v;
+}
+
 template <typename T>
 hipError_t launch_attn_split_typed(const AttnParams& p, hipStream_t stream) {
+  if constexpr (sizeof(T) == 2) {
+    if (decode_applies<T>(p)) {
+      const int w = p.d_h > p.d_vh ? p.d_h : p.d_vh;
+      if (w <= 32) return launch_attn_decode_nq<T, 4>(p, stream);
+      if (w <= 64) return launch_attn_decode_nq<T, 8>(p, stream);
+      return launch_attn_decode_nq<T, 16>(p, stream);
+    }
+  }
   if (p.d_h <= 32) return launch_attn_split_dv<T, 32>(p, stream);
   if (p.d_h <= 64) return launch_attn_split_dv<T, 64>(p, stream);
   if (p.d_h <= 128) return launch_attn_split_dv<T, 128>(p, stream);

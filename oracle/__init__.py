@@ -30,5 +30,6 @@ from .mha_oracle import (  # noqa: F401
     attn_core_grad_ref,
     mha_ref,
     mha_ref_rows,
+    mha_grad_ref,
 )
 from .summary import BOTTOM, summary, merge, finalize, fold  # noqa: F401

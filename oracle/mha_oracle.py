@@ -281,3 +281,39 @@ def attn_core_grad_ref(Qh, Kh, Vh, scale, allow, dZ, add=None):
             dQ[b, r] = scale * (dS @ Kh[b, r])
             dK[b, r] = scale * (dS.T @ Qh[b, r])
     return {"dQh": dQ, "dKh": dK, "dVh": dV}
+
+
+def mha_grad_ref(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, scale, allow, dY, add=None,
+                 biases=None):
+    """Gradients of the full layer for an upstream gradient dY [B, n_q, d_o].
+
+    Returns dict with dQ, dK, dV (input gradients; for self-attention the
+    gradient with respect to X is their sum), dW_Q, dW_K, dW_V, dW_O and
+    db_Q, db_K, db_V, db_O (the bias gradients, whether or not the forward
+    used biases: a bias enters additively, so its gradient does not depend
+    on its value).  Calculus on the forward this module computes:
+      Y = Z W_O (+ b_O):       dZ = dY W_O^T,  dW_O = sum_b Z_b^T dY_b,  db_O = sum dY;
+      core:                    dQh, dKh, dVh from attn_core_grad_ref;
+      Qh = split(Q W_Q + b_Q): dQ_flat = merge(dQh) [B, n_q, h*d_h],
+                               dW_Q = sum_b Q_b^T dQ_flat_b, db_Q = sum dQ_flat,
+                               dQ = dQ_flat W_Q^T;  likewise for K and V.
+    """
+    bs = biases or {}
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    W_Q, W_K, W_V, W_O = _f64(W_Q), _f64(W_K), _f64(W_V), _f64(W_O)
+    dY = _f64(dY)
+    Qh = project_combined(Q, W_Q, h, d_h, bs.get("b_Q"))
+    Kh = project_combined(K, W_K, h, d_h, bs.get("b_K"))
+    Vh = project_combined(V, W_V, h, d_vh, bs.get("b_V"))
+    Z = attn_core_ref(Qh, Kh, Vh, scale, allow, add=add)["Z"]
+    dZ = dY @ W_O.T
+    out = {"dW_O": np.einsum("bnf,bno->fo", Z, dY), "db_O": dY.sum(axis=(0, 1))}
+    g = attn_core_grad_ref(Qh, Kh, Vh, scale, allow, dZ, add=add)
+    for name, X, W, gh in (("Q", Q, W_Q, g["dQh"]), ("K", K, W_K, g["dKh"]),
+                           ("V", V, W_V, g["dVh"])):
+        B, hh, n, d = gh.shape
+        flat = gh.transpose(0, 2, 1, 3).reshape(B, n, hh * d)   # merge the heads back
+        out["dW_" + name] = np.einsum("bni,bnj->ij", X, flat)
+        out["db_" + name] = flat.sum(axis=(0, 1))
+        out["d" + name] = flat @ W.T
+    return out

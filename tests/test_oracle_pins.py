@@ -890,3 +890,40 @@ def test_planted_gradient_mistake_fails_central_differences():
     num = (np.sum(attn_core_ref(Qp, Kh, Vh, 0.8, allow)["Z"] * dZ) -
            np.sum(attn_core_ref(Qm, Kh, Vh, 0.8, allow)["Z"] * dZ)) / (2 * eps)
     assert abs(g["dQh"][0, 0, 0, 0] - num) > 1e-4
+
+
+def test_layer_gradient_matches_central_differences():
+    """Every gradient of the full layer (inputs, weights, biases) against
+    central differences of the forward oracle, cross-attention with general
+    widths, key padding, an additive bias and all four projection biases."""
+    from oracle import mha_grad_ref
+    rng = _rng(95)
+    B, n_q, n_k, d_q, d_k, d_v, h, d_h, d_vh, d_o = 2, 3, 4, 3, 2, 3, 2, 2, 3, 2
+    P = {"Q": rng.normal(size=(B, n_q, d_q)), "K": rng.normal(size=(B, n_k, d_k)),
+         "V": rng.normal(size=(B, n_k, d_v)), "W_Q": rng.normal(size=(d_q, h * d_h)),
+         "W_K": rng.normal(size=(d_k, h * d_h)), "W_V": rng.normal(size=(d_v, h * d_vh)),
+         "W_O": rng.normal(size=(h * d_vh, d_o)), "b_Q": rng.normal(size=h * d_h),
+         "b_K": rng.normal(size=h * d_h), "b_V": rng.normal(size=h * d_vh),
+         "b_O": rng.normal(size=d_o)}
+    dY = rng.normal(size=(B, n_q, d_o))
+    allow = allowed_set(B, n_q, n_k, key_len=[4, 2])
+    M = rng.normal(size=(B, n_q, n_k))
+    c = 0.8
+
+    def loss(P):
+        bs = {k: P[k] for k in ("b_Q", "b_K", "b_V", "b_O")}
+        Y = mha_ref(P["Q"], P["K"], P["V"], P["W_Q"], P["W_K"], P["W_V"], P["W_O"], h, d_h,
+                    d_vh, c, allow, add=M, biases=bs)["Y"]
+        return float(np.sum(Y * dY))
+
+    g = mha_grad_ref(P["Q"], P["K"], P["V"], P["W_Q"], P["W_K"], P["W_V"], P["W_O"], h, d_h,
+                     d_vh, c, allow, dY, add=M,
+                     biases={k: P[k] for k in ("b_Q", "b_K", "b_V", "b_O")})
+    eps = 1e-6
+    for name in P:
+        num = np.zeros_like(P[name])
+        for idx in np.ndindex(P[name].shape):
+            Pp = dict(P); Pp[name] = P[name].copy(); Pp[name][idx] += eps
+            Pm = dict(P); Pm[name] = P[name].copy(); Pm[name][idx] -= eps
+            num[idx] = (loss(Pp) - loss(Pm)) / (2 * eps)
+        np.testing.assert_allclose(g["d" + name], num, rtol=1e-6, atol=1e-7, err_msg=name)

@@ -168,6 +168,7 @@ def decode_bench(args, torch):
 
 
 def backward_bench(args, torch):
+    import numpy as np
     """Attention-core backward on the headline shape (B=4, T=4096, h=16,
     d=64, causal), fp16 heads and fp16 Z/dZ/gradients (the forward's
     intermediate type).  FLOPs counted as 2.5 x the forward's (five products
@@ -214,6 +215,34 @@ def backward_bench(args, torch):
 
     ms_fwd = timed(fwd)
     ms_bwd = timed(bwd)
+
+    # the whole layer's backward on the headline workload (bf16 inputs and
+    # weights, fp16 intermediates, fp32 dY and gradients)
+    from transformer_head_self_amd.inputs import HEADLINE, WORKLOADS, make_inputs
+    w = WORKLOADS[HEADLINE]
+    x = make_inputs(w)
+    put = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
+    X = put(x["Q"])
+    Wt = {k: put(x[k]) for k in ("W_Q", "W_K", "W_V", "W_O")}
+    ldims = mha.MhaDims(B=w.B, h=w.h, n_q=w.n_q, n_k=w.n_k, d_q=w.d_q, d_k=w.d_k, d_v=w.d_v,
+                        d_h=w.d_h, d_vh=w.d_vh, d_o=w.d_o, scale=w.scale, in_dtype=1,
+                        out_dtype=0, work_dtype=2)
+    fws = torch.empty(mha.mha_workspace_bytes(ldims), dtype=torch.uint8, device=dev)
+    bws = torch.empty(mha.mha_backward_workspace_bytes(ldims), dtype=torch.uint8, device=dev)
+    lrm = torch.empty((w.B, w.h, w.n_q), device=dev)
+    lrl = torch.empty_like(lrm)
+    dY = torch.randn(w.B, w.n_q, w.d_o, generator=gen).to(dev)
+    mha.mha_forward(X, X, X, Wt["W_Q"], Wt["W_K"], Wt["W_V"], Wt["W_O"], w.h, w.d_h, w.d_vh,
+                    scale=w.scale, causal=True, row_m=lrm, row_l=lrl, workspace=fws,
+                    stream=stream)
+
+    def layer_bwd():
+        mha.mha_backward(X, X, X, Wt["W_Q"], Wt["W_K"], Wt["W_V"], Wt["W_O"], w.h, w.d_h,
+                         w.d_vh, dY, lrm, lrl, fws, scale=w.scale, causal=True, workspace=bws,
+                         stream=stream)
+
+    ms_layer = timed(layer_bwd)
+    layer_flops = 2.5 * w.core_flops_effective(None) + 2.0 * w.proj_flops()  # 2 products per GEMM
     fwd_flops = 2.0 * B * h * T * T * (d + d) / 2
     bwd_flops = 2.5 * fwd_flops
     peak = PEAK_TFLOPS["bf16"]
@@ -229,6 +258,9 @@ def backward_bench(args, torch):
                      "achieved": round(tf, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tf / peak, 4)},
         "forward_ms": round(ms_fwd, 5),
+        "layer_backward": {"workload": HEADLINE, "ms": round(ms_layer, 5),
+                           "tflops": round(layer_flops / (ms_layer * 1e-3) / 1e12, 3),
+                           "flops": layer_flops},
     }), flush=True)
 
 

@@ -220,6 +220,56 @@ mha_status attn_core_backward(const mha_dims* d, const mha_mask* m,
                               void* dQh, void* dKh, void* dVh,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Gradient outputs for the projection biases of mha_backward: each pointer
+ * may be NULL (not computed); element type out_dtype, device memory. */
+typedef struct mha_bias_grad {
+  void* db_Q;  /* [h*d_h]  */
+  void* db_K;  /* [h*d_h]  */
+  void* db_V;  /* [h*d_vh] */
+  void* db_O;  /* [d_o]    */
+} mha_bias_grad;
+
+/* Scratch mha_backward needs for these dims, 256-byte aligned regions:
+ * dZ, and the three heads' gradients in the concatenated layout (work_dtype),
+ * the backward's row terms, and the column-sum partials of the bias
+ * gradients.  Returns 0 if `d` is NULL or invalid. */
+size_t mha_backward_workspace_bytes(const mha_dims* d);
+
+/* Backward pass of mha_forward: gradients of a scalar loss with respect to
+ * the inputs, the weights and the biases, given dY, its gradient with
+ * respect to Y.  The pages define the forward pass; the gradients are
+ * calculus on it (page "Multi-head attention and self-attention",
+ * Definition: Y = Concat(Z_1..Z_h) W^O with Z_r the attention of
+ * (Q W_r^Q, K W_r^K, V W_r^V)):
+ *   dZ = dY (W^O)^T, dW^O = Z^T dY, db_O = column sums of dY;
+ *   per head, dQ_r, dK_r, dV_r from the core backward (attn_core_backward,
+ *   the weights recomputed from the saved row statistics);
+ *   dW^Q = Q^T dQ_cat, db_Q = column sums of dQ_cat, dQ = dQ_cat (W^Q)^T,
+ *   likewise for K and V (dQ_cat: the heads' gradients side by side).
+ * Arguments as for mha_forward (same dims and mask), plus:
+ *   dY [B, n_q, d_o] (out_dtype); row_m, row_l [B, h, n_q] from the forward
+ *   call (required); fwd_workspace: that call's workspace, still holding
+ *   its projected heads and concatenation (fwd_workspace_bytes >=
+ *   mha_workspace_bytes(d)).
+ *   Outputs (out_dtype; any may be NULL and is then not computed):
+ *   dQ [B, n_q, d_q], dK [B, n_k, d_k], dV [B, n_k, d_v] (written, not
+ *   accumulated: for self-attention the gradient of X is dQ + dK + dV),
+ *   dW_Q, dW_K, dW_V, dW_O (shapes of the weights), dbias (may be NULL).
+ *   workspace: mha_backward_workspace_bytes(d) bytes, 256-byte aligned.
+ * work_dtype must be BF16 or F16 (the core backward's element types); with
+ * F32 the call returns MHA_ERR_DTYPE.  All products accumulate in fp32;
+ * operands are rounded to work_dtype.  Deterministic. */
+mha_status mha_backward(const mha_dims* d, const mha_mask* m,
+                        const void* Q, const void* K, const void* V,
+                        const void* W_Q, const void* W_K, const void* W_V,
+                        const void* W_O, const void* dY,
+                        const float* row_m, const float* row_l,
+                        const void* fwd_workspace, size_t fwd_workspace_bytes,
+                        void* dQ, void* dK, void* dV,
+                        void* dW_Q, void* dW_K, void* dW_V, void* dW_O,
+                        const mha_bias_grad* dbias,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code (host memory, never freed). */
 const char* mha_status_string(int status);
 

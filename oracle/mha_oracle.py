@@ -288,10 +288,11 @@ def mha_grad_ref(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, scale, allow, dY, ad
     """Gradients of the full layer for an upstream gradient dY [B, n_q, d_o].
 
     Returns dict with dQ, dK, dV (input gradients; for self-attention the
-    gradient with respect to X is their sum), dW_Q, dW_K, dW_V, dW_O and
+    gradient with respect to X is their sum), dW_Q, dW_K, dW_V, dW_O,
     db_Q, db_K, db_V, db_O (the bias gradients, whether or not the forward
     used biases: a bias enters additively, so its gradient does not depend
-    on its value).  Calculus on the forward this module computes:
+    on its value) and dQ_cat, dK_cat, dV_cat (the heads' gradients side by
+    side, [B, n, h*d]).  Calculus on the forward this module computes:
       Y = Z W_O (+ b_O):       dZ = dY W_O^T,  dW_O = sum_b Z_b^T dY_b,  db_O = sum dY;
       core:                    dQh, dKh, dVh from attn_core_grad_ref;
       Qh = split(Q W_Q + b_Q): dQ_flat = merge(dQh) [B, n_q, h*d_h],
@@ -315,5 +316,6 @@ def mha_grad_ref(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, scale, allow, dY, ad
         flat = gh.transpose(0, 2, 1, 3).reshape(B, n, hh * d)   # merge the heads back
         out["dW_" + name] = np.einsum("bni,bnj->ij", X, flat)
         out["db_" + name] = flat.sum(axis=(0, 1))
+        out["d" + name + "_cat"] = flat
         out["d" + name] = flat @ W.T
     return out

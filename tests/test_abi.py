@@ -326,3 +326,27 @@ def test_backward_workspace_and_errors():
     assert _bwd(d, ws=FAKE + 128, ws_bytes=need) == -5
     assert _bwd(d, MhaMask(flags=mha.MHA_MASK_CAUSAL)) == -4   # n_q != n_k
     assert _bwd(_dims(in_dtype=mha.MHA_F16, out_dtype=mha.MHA_F32, d_h=200)) == -7
+
+
+def test_layer_backward_workspace_and_errors():
+    d = _dims(in_dtype=mha.MHA_BF16, work_dtype=mha.MHA_F16, out_dtype=mha.MHA_F32)
+    need = mha.mha_backward_workspace_bytes(d)
+    assert need > 0
+    assert mha.mha_backward_workspace_bytes(_dims(B=0)) == 0
+    L = mha.lib()
+    fwd = mha.mha_workspace_bytes(d)
+
+    def call(dd, ptrs=None, fws=FAKE, fwb=fwd, ws=FAKE, wsb=need):
+        p = [FAKE] * 10 if ptrs is None else ptrs
+        return L.mha_backward(ctypes.byref(dd) if dd is not None else None, None, *p, fws, fwb,
+                              *([FAKE] * 7), None, ws, wsb, None)
+    assert call(None) == -1
+    assert call(_dims()) == -3                         # fp32 intermediates: no core backward
+    for i in range(10):
+        p = [FAKE] * 10
+        p[i] = None
+        assert call(d, ptrs=p) == -1
+    assert call(d, fws=None) == -1
+    assert call(d, fwb=fwd - 1) == -6
+    assert call(d, wsb=need - 1) == -6
+    assert call(d, ws=FAKE + 16) == -5

@@ -921,3 +921,87 @@ def test_split_decode_kernel_masks(dt):
         assert err <= 1e-4
         np.testing.assert_allclose(rm.cpu().numpy(), ref["m"], rtol=0, atol=1e-5)
         np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# backward of the whole layer
+# ---------------------------------------------------------------------------
+
+from oracle import mha_grad_ref  # noqa: E402
+
+# Bars for the whole-layer gradients (fp16 intermediates): beyond the core
+# backward's roundings (normwise 3e-4 at fp16), dY, dZ, the heads' gradients
+# and the weights enter the gradient products rounded to fp16 and the
+# forward's heads and concatenation are fp16: each a 2^-11 relative rounding
+# of a factor, so the normwise error stays at a few units of 2^-11 (set from
+# the largest measured: normwise 7.8e-4, max-normalised 9.1e-4 on the cases
+# below).
+LAYER_TOL = (2e-3, 3e-3)
+
+LAYER_BWD_CASES = [
+    # kind, B, n_q, n_k, d_q, d_k, d_v, h, d_h, d_vh, d_o, causal, key_len, additive, biases
+    ("self", 2, 96, 96, 64, 64, 64, 4, 16, 16, 64, True, None, False, True),
+    ("cross", 2, 70, 150, 96, 80, 112, 3, 32, 48, 72, False, (150, 40), True, False),
+    ("self", 2, 512, 512, 512, 512, 512, 8, 64, 64, 512, True, None, False, True),
+]
+
+
+@pytest.mark.parametrize("case", LAYER_BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_layer_backward_matches_oracle(case):
+    """bf16 inputs and weights, fp16 intermediates, fp32 dY and gradients:
+    the forward through the library (its workspace and row statistics kept),
+    then mha_backward, against the float64 gradients of the whole layer."""
+    (kind, B, n_q, n_k, d_q, d_k, d_v, h, d_h, d_vh, d_o, causal, kl, use_add,
+     use_bias) = case
+    _say(f"[layer backward] {case}")
+    rng = np.random.default_rng(97 + n_q)
+    Q = _cast(rng.standard_normal((B, n_q, d_q)), "bf16")
+    if kind == "self":
+        K = V = Q
+    else:
+        K = _cast(rng.standard_normal((B, n_k, d_k)), "bf16")
+        V = _cast(rng.standard_normal((B, n_k, d_v)), "bf16")
+    W = {k: _cast(rng.standard_normal(s) / math.sqrt(s[0]), "bf16") for k, s in
+         (("W_Q", (d_q, h * d_h)), ("W_K", (d_k, h * d_h)), ("W_V", (d_v, h * d_vh)),
+          ("W_O", (h * d_vh, d_o)))}
+    bs = {k: _cast(rng.standard_normal(n) * 0.5, "bf16") for k, n in
+          (("b_Q", h * d_h), ("b_K", h * d_h), ("b_V", h * d_vh), ("b_O", d_o))} if use_bias else {}
+    key_len = None if kl is None else np.array(kl[:B], dtype=np.int32)
+    M = _additive(rng, B, n_q, n_k) if use_add else None
+    dY = rng.standard_normal((B, n_q, d_o)).astype(np.float32)
+    c = 1.0 / math.sqrt(d_h)
+    allow = allowed_set(B, n_q, n_k, causal=causal, key_len=key_len)
+    ref = mha_grad_ref(Q, K, V, W["W_Q"], W["W_K"], W["W_V"], W["W_O"], h, d_h, d_vh, c, allow,
+                       dY, add=M, biases=bs or None)
+
+    tQ = _to_dev(Q, "bf16")
+    tK, tV = (tQ, tQ) if kind == "self" else (_to_dev(K, "bf16"), _to_dev(V, "bf16"))
+    tW = {k: _to_dev(v, "bf16") for k, v in W.items()}
+    kl_dev = None if key_len is None else torch.from_numpy(key_len).to(DEV)
+    M_dev = None if M is None else torch.from_numpy(M).to(DEV)
+    dims = mha.MhaDims(B=B, h=h, n_q=n_q, n_k=n_k, d_q=d_q, d_k=d_k, d_v=d_v, d_h=d_h,
+                       d_vh=d_vh, d_o=d_o, scale=c, in_dtype=1, out_dtype=0, work_dtype=2)
+    fws = torch.empty(mha.mha_workspace_bytes(dims), dtype=torch.uint8, device=DEV)
+    rm = torch.empty((B, h, n_q), device=DEV)
+    rl = torch.empty_like(rm)
+    mha.mha_forward(tQ, tK, tV, tW["W_Q"], tW["W_K"], tW["W_V"], tW["W_O"], h, d_h, d_vh,
+                    scale=c, causal=causal, key_len=kl_dev, add=M_dev, row_m=rm, row_l=rl,
+                    workspace=fws, **{k: _to_dev(v, "bf16") for k, v in bs.items()})
+    g = mha.mha_backward(tQ, tK, tV, tW["W_Q"], tW["W_K"], tW["W_V"], tW["W_O"], h, d_h, d_vh,
+                         torch.from_numpy(dY).to(DEV), rm, rl, fws, scale=c, causal=causal,
+                         key_len=kl_dev, add=M_dev, bias_grads=True)
+    torch.cuda.synchronize()
+    for name in ("dQ", "dK", "dV", "dW_Q", "dW_K", "dW_V", "dW_O"):
+        got = g[name].cpu().numpy()
+        fro, mx = _grad_err(got, ref[name])
+        _say(f"  {name} normwise {fro:.3e} max {mx:.3e}")
+        assert fro <= LAYER_TOL[0] and mx <= LAYER_TOL[1], name
+    # a bias gradient is a column sum, which can cancel to nothing (db_K is
+    # exactly 0: a key bias moves every score of a row by one constant), so
+    # its error is measured against the sum of the terms' magnitudes
+    terms = {"db_Q": ref["dQ_cat"], "db_K": ref["dK_cat"], "db_V": ref["dV_cat"], "db_O": dY}
+    for name, t in terms.items():
+        scale = np.abs(np.asarray(t, np.float64)).sum(axis=(0, 1))
+        err = float(np.max(np.abs(g[name].cpu().numpy() - ref[name]) / scale))
+        _say(f"  {name} error / sum of |terms| {err:.3e}")
+        assert err <= LAYER_TOL[0], name

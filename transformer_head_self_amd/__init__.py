@@ -14,6 +14,9 @@ Entry points (same names as the C ABI):
 * ``attn_split_workspace_bytes``.
 * ``attn_core_backward``  gradients of the attention core from the forward's
   row statistics; ``attn_backward_workspace_bytes``.
+* ``mha_backward``  gradients of the whole layer (inputs, weights, biases)
+  from the forward's workspace and row statistics;
+  ``mha_backward_workspace_bytes``.
 * ``mha_workspace_bytes``, ``mha_status_string``.
 """
 
@@ -24,7 +27,8 @@ import math
 import os
 
 __all__ = [
-    "MhaError", "MhaDims", "MhaMask", "MhaBias", "lib", "mha_forward", "attn_core", "attn_core_split",
+    "MhaError", "MhaDims", "MhaMask", "MhaBias", "MhaBiasGrad", "lib", "mha_backward",
+    "mha_backward_workspace_bytes", "mha_forward", "attn_core", "attn_core_split",
     "attn_split_workspace_bytes", "attn_core_backward", "attn_backward_workspace_bytes",
     "mha_workspace_bytes", "mha_status_string", "MHA_F32", "MHA_BF16", "MHA_F16",
     "MHA_MASK_CAUSAL", "MHA_MASK_KEY_PADDING", "MHA_MASK_BOOL", "MHA_MASK_ADDITIVE",
@@ -53,6 +57,11 @@ class MhaMask(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_uint32), ("key_len", ctypes.c_void_p),
                 ("allowed", ctypes.c_void_p), ("allowed_batch_stride", ctypes.c_int64),
                 ("add", ctypes.c_void_p), ("add_batch_stride", ctypes.c_int64)]
+
+
+class MhaBiasGrad(ctypes.Structure):
+    _fields_ = [("db_Q", ctypes.c_void_p), ("db_K", ctypes.c_void_p), ("db_V", ctypes.c_void_p),
+                ("db_O", ctypes.c_void_p)]
 
 
 class MhaBias(ctypes.Structure):
@@ -90,6 +99,11 @@ def lib():
         L.attn_core_backward.argtypes = [P(MhaDims), P(MhaMask)] + [vp] * 11 + [ctypes.c_size_t,
                                                                                 vp]
         L.attn_core_backward.restype = ctypes.c_int
+        L.mha_backward_workspace_bytes.argtypes = [P(MhaDims)]
+        L.mha_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.mha_backward.argtypes = ([P(MhaDims), P(MhaMask)] + [vp] * 11 + [ctypes.c_size_t] +
+                                   [vp] * 7 + [P(MhaBiasGrad), vp, ctypes.c_size_t, vp])
+        L.mha_backward.restype = ctypes.c_int
         L.mha_status_string.argtypes = [ctypes.c_int]
         L.mha_status_string.restype = ctypes.c_char_p
         L.mha_max_head_dim.argtypes = []
@@ -317,3 +331,56 @@ def attn_core_backward(Qh, Kh, Vh, Z, dZ, row_m, row_l, *, scale=None, causal=Fa
     if st != 0:
         raise MhaError(st, "attn_core_backward")
     return dQh, dKh, dVh
+
+
+def mha_backward_workspace_bytes(dims: MhaDims):
+    return int(lib().mha_backward_workspace_bytes(ctypes.byref(dims) if dims is not None
+                                                  else None))
+
+
+def mha_backward(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, dY, row_m, row_l, fwd_workspace, *,
+                 scale=None, causal=False, key_len=None, allowed=None, add=None, work_dtype=None,
+                 bias_grads=False, workspace=None, stream=None):
+    """Gradients of the layer for the upstream gradient dY, after
+    ``mha_forward`` was called with the same arguments, ``workspace=
+    fwd_workspace`` and ``row_m``/``row_l`` requested.  Returns a dict with
+    dQ, dK, dV, dW_Q, dW_K, dW_V, dW_O (and db_Q, db_K, db_V, db_O if
+    ``bias_grads``), all of dY's element type."""
+    torch = _torch()
+    B, n_q, d_q = Q.shape
+    n_k, d_k = K.shape[1], K.shape[2]
+    d_v = V.shape[2]
+    d_o = W_O.shape[1]
+    work_dtype = default_work_dtype(Q.dtype) if work_dtype is None else work_dtype
+    dims = MhaDims(B=B, h=h, n_q=n_q, n_k=n_k, d_q=d_q, d_k=d_k, d_v=d_v, d_h=d_h, d_vh=d_vh,
+                   d_o=d_o, scale=(1.0 / math.sqrt(d_h)) if scale is None else float(scale),
+                   in_dtype=_dtype_code(Q.dtype), out_dtype=_dtype_code(dY.dtype),
+                   work_dtype=_dtype_code(work_dtype))
+    m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Q.device, add)
+    dev, od = Q.device, dY.dtype
+    out = {"dQ": torch.empty((B, n_q, d_q), dtype=od, device=dev),
+           "dK": torch.empty((B, n_k, d_k), dtype=od, device=dev),
+           "dV": torch.empty((B, n_k, d_v), dtype=od, device=dev),
+           "dW_Q": torch.empty(tuple(W_Q.shape), dtype=od, device=dev),
+           "dW_K": torch.empty(tuple(W_K.shape), dtype=od, device=dev),
+           "dW_V": torch.empty(tuple(W_V.shape), dtype=od, device=dev),
+           "dW_O": torch.empty(tuple(W_O.shape), dtype=od, device=dev)}
+    db = MhaBiasGrad()
+    if bias_grads:
+        for k, n in (("db_Q", h * d_h), ("db_K", h * d_h), ("db_V", h * d_vh), ("db_O", d_o)):
+            out[k] = torch.empty(n, dtype=od, device=dev)
+            setattr(db, k, out[k].data_ptr())
+    if workspace is None:
+        workspace = torch.empty(max(mha_backward_workspace_bytes(dims), 1), dtype=torch.uint8,
+                                device=dev)
+    st = lib().mha_backward(ctypes.byref(dims), ctypes.byref(m), _ptr(Q), _ptr(K), _ptr(V),
+                            _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_O), _ptr(dY), _ptr(row_m),
+                            _ptr(row_l), _ptr(fwd_workspace), fwd_workspace.numel(),
+                            _ptr(out["dQ"]), _ptr(out["dK"]), _ptr(out["dV"]), _ptr(out["dW_Q"]),
+                            _ptr(out["dW_K"]), _ptr(out["dW_V"]), _ptr(out["dW_O"]),
+                            ctypes.byref(db), _ptr(workspace), workspace.numel(),
+                            _stream(stream))
+    del keep
+    if st != 0:
+        raise MhaError(st, "mha_backward")
+    return out

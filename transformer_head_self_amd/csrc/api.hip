@@ -211,6 +211,52 @@ void attn_params(mha::AttnParams& p, const mha_dims* d, int elem_dtype, const vo
   p.num_q_tiles = 0;
 }
 
+void fill_bwd_mask(mha::AttnBwdParams& p, const mha_mask* m) {
+  if (!m) return;
+  p.causal = (m->flags & MHA_MASK_CAUSAL) ? 1 : 0;
+  if (m->flags & MHA_MASK_KEY_PADDING) p.key_len = m->key_len;
+  if (m->flags & MHA_MASK_BOOL) {
+    p.allowed = m->allowed;
+    p.allowed_batch_stride = m->allowed_batch_stride;
+  }
+  if (m->flags & MHA_MASK_ADDITIVE) {
+    p.add = m->add;
+    p.add_batch_stride = m->add_batch_stride;
+  }
+}
+
+// mha_backward scratch: dZ and the heads' gradients in the concatenated
+// layout (work_dtype), the core backward's row terms, column-sum partials.
+struct BwdWorkspace {
+  size_t dz, dq, dk, dv, lse, dsum, part, splitk, total;
+};
+
+BwdWorkspace carve_bwd(const mha_dims* d) {
+  const size_t B = d->B, h = d->h, es = esize(d->work_dtype);
+  BwdWorkspace w;
+  w.dz = 0;
+  w.dq = w.dz + round256(B * d->n_q * h * d->d_vh * es);
+  w.dk = w.dq + round256(B * d->n_q * h * d->d_h * es);
+  w.dv = w.dk + round256(B * d->n_k * h * d->d_h * es);
+  w.lse = w.dv + round256(B * d->n_k * h * d->d_vh * es);
+  w.dsum = w.lse + round256(B * h * d->n_q * 4);
+  w.part = w.dsum + round256(B * h * d->n_q * 4);
+  size_t parts = mha::colsum_scratch_floats((int)(B * d->n_q), d->d_o);
+  parts = std::max(parts, mha::colsum_scratch_floats((int)(B * d->n_q), (int)(h * d->d_h)));
+  parts = std::max(parts, mha::colsum_scratch_floats((int)(B * d->n_k), (int)(h * d->d_h)));
+  parts = std::max(parts, mha::colsum_scratch_floats((int)(B * d->n_k), (int)(h * d->d_vh)));
+  w.splitk = w.part + round256(parts * 4);
+  // split-K partials of the weight gradients (one product at a time)
+  const int Mq = (int)(B * d->n_q), Mk = (int)(B * d->n_k);
+  const int Nq = (int)(h * d->d_h), Nv = (int)(h * d->d_vh);
+  size_t sk = mha::gemm_any_partial_floats(Nv, d->d_o, Mq);
+  sk = std::max(sk, mha::gemm_any_partial_floats(d->d_q, Nq, Mq));
+  sk = std::max(sk, mha::gemm_any_partial_floats(d->d_k, Nq, Mk));
+  sk = std::max(sk, mha::gemm_any_partial_floats(d->d_v, Nv, Mk));
+  w.total = w.splitk + round256(sk * 4);
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -344,18 +390,7 @@ mha_status attn_core_backward(const mha_dims* d, const mha_mask* m, const void* 
   p.elem_dtype = d->in_dtype;
   p.z_dtype = d->out_dtype;
   p.g_dtype = d->out_dtype;
-  if (m) {
-    p.causal = (m->flags & MHA_MASK_CAUSAL) ? 1 : 0;
-    if (m->flags & MHA_MASK_KEY_PADDING) p.key_len = m->key_len;
-    if (m->flags & MHA_MASK_BOOL) {
-      p.allowed = m->allowed;
-      p.allowed_batch_stride = m->allowed_batch_stride;
-    }
-    if (m->flags & MHA_MASK_ADDITIVE) {
-      p.add = m->add;
-      p.add_batch_stride = m->add_batch_stride;
-    }
-  }
+  fill_bwd_mask(p, m);
   const int vin = vec_elems(d->in_dtype), vz = vec_elems(d->out_dtype);
   p.vec_q = aligned(Qh, 16) && d->d_h % vin == 0;
   p.vec_k = aligned(Kh, 16) && d->d_h % vin == 0;
@@ -367,6 +402,137 @@ mha_status attn_core_backward(const mha_dims* d, const mha_mask* m, const void* 
   p.vec_dv = aligned(dVh, a4) && d->d_vh % 4 == 0;
   if (mha::launch_attention_backward(p, d->in_dtype, (hipStream_t)stream) != hipSuccess)
     return MHA_ERR_LAUNCH;
+  return MHA_OK;
+}
+
+size_t mha_backward_workspace_bytes(const mha_dims* d) {
+  if (check_full_dims(d) != MHA_OK) return 0;
+  return carve_bwd(d).total;
+}
+
+mha_status mha_backward(const mha_dims* d, const mha_mask* m, const void* Q, const void* K,
+                        const void* V, const void* W_Q, const void* W_K, const void* W_V,
+                        const void* W_O, const void* dY, const float* row_m, const float* row_l,
+                        const void* fwd_workspace, size_t fwd_workspace_bytes, void* dQ,
+                        void* dK, void* dV, void* dW_Q, void* dW_K, void* dW_V, void* dW_O,
+                        const mha_bias_grad* dbias, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  mha_status s = check_full_dims(d);
+  if (s != MHA_OK) return s;
+  if (d->work_dtype == MHA_F32) return MHA_ERR_DTYPE;
+  if ((s = check_mask(d, m)) != MHA_OK) return s;
+  if (!Q || !K || !V || !W_Q || !W_K || !W_V || !W_O || !dY || !row_m || !row_l ||
+      !fwd_workspace)
+    return MHA_ERR_NULL;
+  const size_t ei = esize(d->in_dtype), eo = esize(d->out_dtype);
+  const mha_bias_grad nb = {nullptr, nullptr, nullptr, nullptr};
+  const mha_bias_grad& db = dbias ? *dbias : nb;
+  if (!aligned(Q, ei) || !aligned(K, ei) || !aligned(V, ei) || !aligned(W_Q, ei) ||
+      !aligned(W_K, ei) || !aligned(W_V, ei) || !aligned(W_O, ei) || !aligned(dY, eo) ||
+      !aligned(row_m, 4) || !aligned(row_l, 4) || !aligned(dQ, eo) || !aligned(dK, eo) ||
+      !aligned(dV, eo) || !aligned(dW_Q, eo) || !aligned(dW_K, eo) || !aligned(dW_V, eo) ||
+      !aligned(dW_O, eo) || !aligned(db.db_Q, eo) || !aligned(db.db_K, eo) ||
+      !aligned(db.db_V, eo) || !aligned(db.db_O, eo))
+    return MHA_ERR_ALIGN;
+  const Workspace fw = carve(d);
+  if (fwd_workspace_bytes < fw.total) return MHA_ERR_WORKSPACE;
+  if (!aligned(fwd_workspace, 256)) return MHA_ERR_ALIGN;
+  const BwdWorkspace bw = carve_bwd(d);
+  if (!workspace || workspace_bytes < bw.total) return MHA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MHA_ERR_ALIGN;
+
+  const char* fws = static_cast<const char*>(fwd_workspace);
+  char* ws = static_cast<char*>(workspace);
+  const int wd = d->work_dtype, od = d->out_dtype, id = d->in_dtype;
+  const int Mq = d->B * d->n_q, Mk = d->B * d->n_k;
+  const int Nq = d->h * d->d_h, Nv = d->h * d->d_vh;
+  float* part = reinterpret_cast<float*>(ws + bw.part);
+  hipStream_t st = (hipStream_t)stream;
+  auto gemm = [&](const void* A, int adt, long long lda, int at, const void* W, int wdt,
+                  long long ldw, int wt, void* C, int M, int N, int Kd) {
+    mha::GemmAny g;
+    memset(&g, 0, sizeof(g));
+    g.A = A;
+    g.W = W;
+    g.C = C;
+    g.M = M;
+    g.N = N;
+    g.K = Kd;
+    g.lda = lda;
+    g.ldw = ldw;
+    g.ldc = N;
+    g.a_trans = at;
+    g.w_trans = wt;
+    g.a_dtype = adt;
+    g.w_dtype = wdt;
+    g.c_dtype = C == ws + bw.dz ? wd : od;
+    return mha::launch_gemm_any(g, wd, reinterpret_cast<float*>(ws + bw.splitk), st) ==
+           hipSuccess;
+  };
+
+  // output projection: dZ = dY W_O^T (W_O [Nv, d_o] is W_O^T stored k-contiguous),
+  // dW_O = Z^T dY, db_O = column sums of dY
+  void* dZ = ws + bw.dz;
+  if (!gemm(dY, od, d->d_o, 0, W_O, id, d->d_o, 1, dZ, Mq, Nv, d->d_o)) return MHA_ERR_LAUNCH;
+  if (dW_O && !gemm(fws + fw.z, wd, Nv, 1, dY, od, d->d_o, 0, dW_O, Nv, d->d_o, Mq))
+    return MHA_ERR_LAUNCH;
+  if (db.db_O && mha::launch_colsum(dY, od, d->d_o, Mq, d->d_o, db.db_O, od, part, st) != hipSuccess)
+    return MHA_ERR_LAUNCH;
+
+  // the core backward, gradients in the concatenated layout
+  mha::AttnBwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.Q = fws + fw.q;
+  p.K = fws + fw.k;
+  p.V = fws + fw.v;
+  p.Z = fws + fw.z;
+  p.dZ = dZ;
+  p.row_m = row_m;
+  p.row_l = row_l;
+  p.dQ = ws + bw.dq;
+  p.dK = ws + bw.dk;
+  p.dV = ws + bw.dv;
+  p.lse2 = reinterpret_cast<float*>(ws + bw.lse);
+  p.dsum = reinterpret_cast<float*>(ws + bw.dsum);
+  p.B = d->B;
+  p.h = d->h;
+  p.n_q = d->n_q;
+  p.n_k = d->n_k;
+  p.d_h = d->d_h;
+  p.d_vh = d->d_vh;
+  p.ldz = Nv;
+  p.scale = d->scale;
+  p.scale_log2 = d->scale * 1.4426950408889634f;
+  p.grad_concat = 1;
+  p.elem_dtype = wd;
+  p.z_dtype = wd;
+  p.g_dtype = wd;
+  fill_bwd_mask(p, m);
+  p.vec_q = p.vec_k = (d->d_h % 8 == 0);      // workspace regions are 256-byte aligned
+  p.vec_v = (d->d_vh % 8 == 0);
+  p.vec_z = (d->d_vh % 8 == 0);
+  p.vec_dq = p.vec_dk = (d->d_h % 4 == 0);
+  p.vec_dv = (d->d_vh % 4 == 0);
+  if (mha::launch_attention_backward(p, wd, st) != hipSuccess) return MHA_ERR_LAUNCH;
+
+  // projections: dW = X^T dX_cat, db = column sums of dX_cat, dX = dX_cat W^T
+  struct Proj {
+    const void* X; int M, d_in; const void* W; int N; const char* cat;
+    void* dX; void* dW; void* db;
+  };
+  const Proj proj[3] = {
+      {Q, Mq, d->d_q, W_Q, Nq, ws + bw.dq, dQ, dW_Q, db.db_Q},
+      {K, Mk, d->d_k, W_K, Nq, ws + bw.dk, dK, dW_K, db.db_K},
+      {V, Mk, d->d_v, W_V, Nv, ws + bw.dv, dV, dW_V, db.db_V},
+  };
+  for (const Proj& r : proj) {
+    if (r.dW && !gemm(r.X, id, r.d_in, 1, r.cat, wd, r.N, 0, r.dW, r.d_in, r.N, r.M))
+      return MHA_ERR_LAUNCH;
+    if (r.db && mha::launch_colsum(r.cat, wd, r.N, r.M, r.N, r.db, od, part, st) != hipSuccess)
+      return MHA_ERR_LAUNCH;
+    if (r.dX && !gemm(r.cat, wd, r.N, 0, r.W, id, r.N, 1, r.dX, r.M, r.d_in, r.N))
+      return MHA_ERR_LAUNCH;
+  }
   return MHA_OK;
 }
 

@@ -372,8 +372,11 @@ void attn_bwd_kv_kernel(AttnBwdParams p) {
 
   // dK = c (dK^T)^T, dV = (dV^T)^T: lane writes its key's row
   if (key < p.n_k) {
-    const size_t kro = ((size_t)bh * p.n_k + key) * p.d_h;
-    const size_t vro = ((size_t)bh * p.n_k + key) * p.d_vh;
+    // head-major [B, h, n_k, d] or concatenated [B, n_k, h*d]
+    const size_t krow = p.grad_concat ? ((size_t)b * p.n_k + key) * p.h + r
+                                      : (size_t)bh * p.n_k + key;
+    const size_t kro = krow * p.d_h;
+    const size_t vro = krow * p.d_vh;
     #pragma unroll
     for (int d = 0; d < C::NDH; ++d)
       #pragma unroll
@@ -534,7 +537,8 @@ void attn_bwd_q_kernel(AttnBwdParams p) {
   }
 
   if (qi < p.n_q) {
-    const size_t qro = ((size_t)bh * p.n_q + qi) * p.d_h;
+    const size_t qro = (p.grad_concat ? ((size_t)b * p.n_q + qi) * p.h + r
+                                      : (size_t)bh * p.n_q + qi) * p.d_h;
     #pragma unroll
     for (int d = 0; d < C::NDH; ++d)
       #pragma unroll

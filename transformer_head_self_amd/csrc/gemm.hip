@@ -1,6 +1,9 @@
+#include <algorithm>
+
 // Launchers for the projection GEMMs: the direct-to-LDS 2-byte kernel where
 // its conditions hold, else the general 128x128 kernel (every element type).
 #include "gemm.hpp"
+#include "gemm_any.hpp"
 #include "gemm_dma.hpp"
 #include "gemm_dma_wide.hpp"
 
@@ -83,6 +86,73 @@ hipError_t launch_gemm(const GemmBatch& in, int compute_dtype, int w_dtype, hipS
     hipLaunchKernelGGL((gemm_kernel<float, float>), dim3(total), dim3(256), 0, stream, b);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+static bool aligned_to(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+static size_t elem_size(int dt) { return dt == kF32 ? 4 : 2; }
+
+// Split-K partitions: only when the output has few tiles (fewer than 256
+// workgroups) and K is long; about 512 workgroups, K chunks of at least 512.
+static int gemm_any_splits(int M, int N, int K) {
+  const long long tiles = (long long)((M + 127) / 128) * ((N + 127) / 128);
+  if (tiles >= 256 || K < 1024) return 1;
+  long long s = (512 + tiles - 1) / tiles;
+  s = std::min<long long>(s, K / 512);
+  return (int)std::max<long long>(s, 1);
+}
+
+size_t gemm_any_partial_floats(int M, int N, int K) {
+  const int s = gemm_any_splits(M, N, K);
+  return s > 1 ? (size_t)s * M * N : 0;
+}
+
+hipError_t launch_gemm_any(GemmAny g, int compute_dtype, float* partial, hipStream_t stream) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  const int vec = compute_dtype == kF32 ? 4 : 8;
+  // chunks of `vec` elements along the contiguous dimension start at multiples
+  // of `vec`; a full chunk is one or two aligned vector loads
+  g.vec_a = aligned_to(g.A, 16) && g.lda % vec == 0;
+  g.vec_w = aligned_to(g.W, 16) && g.ldw % vec == 0;
+  g.vec_c = aligned_to(g.C, 4 * elem_size(g.c_dtype)) && g.ldc % 4 == 0;
+  g.ksplit = gemm_any_splits(g.M, g.N, g.K);
+  if (g.ksplit > 1 && partial == nullptr) return hipErrorInvalidValue;
+  // K chunks are whole 32-element stages (vector loads stay aligned)
+  g.kchunk = g.ksplit > 1 ? ((g.K + g.ksplit - 1) / g.ksplit + 31) / 32 * 32 : g.K;
+  g.ksplit = (g.K + g.kchunk - 1) / g.kchunk;
+  if (g.ksplit < 1) g.ksplit = 1;
+  g.partial = partial;
+  const long long tiles = (long long)((g.M + 127) / 128) * ((g.N + 127) / 128) * g.ksplit;
+  if (tiles > 2147483647LL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tiles);
+  if (compute_dtype == kBF16)
+    hipLaunchKernelGGL(gemm_any_kernel<bf16>, grid, dim3(256), 0, stream, g);
+  else if (compute_dtype == kF16)
+    hipLaunchKernelGGL(gemm_any_kernel<f16>, grid, dim3(256), 0, stream, g);
+  else
+    hipLaunchKernelGGL(gemm_any_kernel<float>, grid, dim3(256), 0, stream, g);
+  if (g.ksplit > 1) {
+    const size_t n = (size_t)g.M * g.N;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, partial, g.ksplit, g.M, g.N, g.C, g.c_dtype, g.ldc);
+  }
+  return hipGetLastError();
+}
+
+size_t colsum_scratch_floats(int M, int N) {
+  return (size_t)((M + 255) / 256) * (size_t)N;
+}
+
+hipError_t launch_colsum(const void* X, int dtype, long long ld, int M, int N, void* out,
+                         int out_dtype, float* part, hipStream_t stream) {
+  if (N <= 0) return hipSuccess;
+  const int R = (M + 255) / 256;
+  if (R > 0) {
+    hipLaunchKernelGGL(colsum_partial_kernel, dim3((N + 255) / 256, R), dim3(256), 0, stream, X,
+                       dtype, ld, M, N, part);
+  }
+  hipLaunchKernelGGL(colsum_finish_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, part, R,
+                     N, out, out_dtype);
   return hipGetLastError();
 }
 

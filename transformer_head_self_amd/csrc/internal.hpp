@@ -44,6 +44,35 @@ struct GemmBatch {
 
 hipError_t launch_gemm(const GemmBatch& batch, int compute_dtype, int w_dtype, hipStream_t stream);
 
+// General product for the gradients: C[M, N] = A[M, K] * W[K, N] with either
+// operand stored transposed (a_trans: A(m, k) = A[k*lda + m]; w_trans:
+// W(k, n) = W[n*ldw + k]) and per-operand element types, computed in
+// compute_dtype with fp32 accumulation; C row-major with row stride ldc.
+struct GemmAny {
+  const void* A;
+  const void* W;
+  void* C;
+  int M, N, K;
+  long long lda, ldw, ldc;
+  int a_trans, w_trans;
+  int a_dtype, w_dtype, c_dtype;
+  int vec_a, vec_w, vec_c;   // vector loads / 4-element stores allowed (set by the launcher)
+  int ksplit, kchunk;        // split-K (set by the launcher): ksplit partitions of kchunk
+  float* partial;            // fp32 [ksplit, M, N] partial products when ksplit > 1
+};
+// `partial`: fp32 scratch of gemm_any_partial_floats(M, N, K) elements (may
+// be NULL when that is 0).  Long-K products with few output tiles (the
+// weight gradients) are split along K into partitions summed afterwards in a
+// fixed order.
+size_t gemm_any_partial_floats(int M, int N, int K);
+hipError_t launch_gemm_any(GemmAny g, int compute_dtype, float* partial, hipStream_t stream);
+
+// out[n] = sum over m < M of X[m * ld + n] (n < N), in a fixed order;
+// `part` is fp32 scratch of colsum_scratch_floats(M, N) elements.
+size_t colsum_scratch_floats(int M, int N);
+hipError_t launch_colsum(const void* X, int dtype, long long ld, int M, int N, void* out,
+                         int out_dtype, float* part, hipStream_t stream);
+
 // ---------------------------------------------------------------------------
 // Fused attention: Z[b, i, r*d_vh + e] = sum_j softmax_j(c * q_i . k_j | mask) v_j[e]
 // computed with running (m, l, z) summaries over key blocks.
@@ -117,6 +146,8 @@ struct AttnBwdParams {
   float scale;       // c
   float scale_log2;  // c log2(e)
   int causal;
+  int grad_concat;   // 1: dQ, dK, dV written in the concatenated layout
+                     //    [B, n, h*d] (head r at columns r*d..), else head-major
   int elem_dtype;    // T: element type of Q, K, V and of the MFMA operands
   int z_dtype, g_dtype;
   int vec_q, vec_k, vec_v, vec_z;    // 16-byte loads allowed

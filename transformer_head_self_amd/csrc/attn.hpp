@@ -448,7 +448,25 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
     const int cur = (blk - blk0) & 1;   // register staging: buffer of this block
     const T* ks = Ks + cur * C::KBUF;
     const T* vs = Vs + cur * C::VBUF;
-    const char* stage = smem + (blk % C::NS) * C::STAGE;   // DMA
+    // DMA: this block's stage.  Each read pattern gets one base address per
+    // block, made opaque so that the compiler keeps it in one register and
+    // folds every other offset into the read instructions (left to itself
+    // it kept a separate strength-reduced address per read).
+    unsigned kaddr[DMA ? C::KCH : 1], vaddr[DMA ? C::NDV : 1];
+    if constexpr (DMA) {
+      unsigned st_addr = lds_base + (unsigned)((blk % C::NS) * C::STAGE);
+      asm("" : "+s"(st_addr));
+      #pragma unroll
+      for (int c = 0; c < C::KCH; ++c) {
+        kaddr[c] = st_addr + (unsigned)kro[c];
+        asm("" : "+v"(kaddr[c]));
+      }
+      #pragma unroll
+      for (int d = 0; d < C::NDV; ++d) {
+        vaddr[d] = st_addr + (unsigned)vro[d];
+        asm("" : "+v"(vaddr[d]));
+      }
+    }
     const int k0 = blk * BN;
     // A wave whose rows all precede this block's first key (causal) sees an
     // empty key set here: its summary is the empty state, a no-op merge.
@@ -473,7 +491,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
           for (int c = 0; c < C::KCH; ++c) {
             vec kf;
             if constexpr (DMA)
-              kf = *reinterpret_cast<const vec*>(stage + kb * 32 * C::KRB + kro[c]);
+              kf = lds_load_at<vec>(kaddr[c] + kb * 32 * C::KRB);
             else
               kf = *reinterpret_cast<const vec*>(
                   &ks[(kb * 32 + l32) * C::KPAD + c * 2 * VEC + g * VEC]);
@@ -658,9 +676,9 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
             for (int d = 0; d < C::NDV; ++d) {
               vec4 lo, hi;
               if constexpr (DMA) {
-                const char* v0 = stage + (kb * 32 + 16 * st) * C::VRB + vro[d];
-                lo = lds_read_tr4<T>(reinterpret_cast<const T*>(v0));
-                hi = lds_read_tr4<T>(reinterpret_cast<const T*>(v0 + 8 * C::VRB));
+                const unsigned v0 = vaddr[d] + (kb * 32 + 16 * st) * C::VRB;
+                lo = lds_read_tr4_at<T>(v0);
+                hi = lds_read_tr4_at<T>(v0 + 8 * C::VRB);
               } else {
                 const T* v0 = &vs[(kb * 32 + 16 * st + srow) * C::VROW + d * 32 + scol];
                 lo = lds_read_tr4<T>(v0);

@@ -175,9 +175,22 @@ __global__ __launch_bounds__(256, OCC) void attn_pipe_kernel(AttnParams p) {
   vec pw[NKB][2];      // weights of the block whose value product is next
   floatx16 s[NKB];     // scores of the block after it
 
-  auto stage_ptr = [&](int blk) { return smem + (blk % NS) * C::STAGE; };
+  // LDS byte address of a block's stage, opaque to the compiler: the reads
+  // below add one per-lane offset to it and fold the rest into immediates
+  // (left to itself the compiler kept a strength-reduced address per read).
+  auto stage_ptr = [&](int blk) {
+    unsigned a = lds_base + (unsigned)((blk % NS) * C::STAGE);
+    asm("" : "+s"(a));
+    return a;
+  };
   // s = acc + K_blk Q^T  (acc = -mu or 0)
-  auto scores = [&](const char* st, bool at_mu) {
+  auto scores = [&](unsigned st, bool at_mu) {
+    unsigned kaddr[C::KCH];
+    #pragma unroll
+    for (int c = 0; c < C::KCH; ++c) {
+      kaddr[c] = st + (unsigned)kro[c];
+      asm("" : "+v"(kaddr[c]));
+    }
     #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       if (at_mu) {
@@ -188,7 +201,7 @@ __global__ __launch_bounds__(256, OCC) void attn_pipe_kernel(AttnParams p) {
       }
       #pragma unroll
       for (int c = 0; c < C::KCH; ++c) {
-        const vec kf = *reinterpret_cast<const vec*>(st + kb * 32 * C::KRB + kro[c]);
+        const vec kf = lds_load_at<vec>(kaddr[c] + kb * 32 * C::KRB);
         mfma_chunk(s[kb], kf, qf[c]);
       }
     }
@@ -225,14 +238,20 @@ __global__ __launch_bounds__(256, OCC) void attn_pipe_kernel(AttnParams p) {
     }
   };
   // o += V_blk^T P^T for the weights in pw (sub-block kb)
-  auto value_product = [&](const char* st, int kb) {
+  auto value_product = [&](unsigned st, int kb) {
+    unsigned vaddr[C::NDV];
+    #pragma unroll
+    for (int d = 0; d < C::NDV; ++d) {
+      vaddr[d] = st + (unsigned)vro[d];
+      asm("" : "+v"(vaddr[d]));
+    }
     #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
       #pragma unroll
       for (int d = 0; d < C::NDV; ++d) {
-        const char* v0 = st + (kb * 32 + 16 * h2) * C::VRB + vro[d];
-        const vec4 lo = lds_read_tr4<T>(reinterpret_cast<const T*>(v0));
-        const vec4 hi = lds_read_tr4<T>(reinterpret_cast<const T*>(v0 + 8 * C::VRB));
+        const unsigned v0 = vaddr[d] + (kb * 32 + 16 * h2) * C::VRB;
+        const vec4 lo = lds_read_tr4_at<T>(v0);
+        const vec4 hi = lds_read_tr4_at<T>(v0 + 8 * C::VRB);
         const vec va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         mfma_chunk(o[d], va, pw[kb][h2]);
       }
@@ -281,9 +300,9 @@ __global__ __launch_bounds__(256, OCC) void attn_pipe_kernel(AttnParams p) {
       if (j + NS - 1 < nblk) issue_kv(j + NS - 1);
     }
     if (j >= nact) continue;
-    const char* stj = stage_ptr(j);
+    const unsigned stj = stage_ptr(j);
     if (j + 1 < nact) {
-      const char* stn = stage_ptr(j + 1);
+      const unsigned stn = stage_ptr(j + 1);
       scores(stn, true);              // S_{j+1} - mu (matrix cores)
       if (j + 1 >= nfree) mask(j + 1);
       // value product of block j, sub-block by sub-block, interleaved with

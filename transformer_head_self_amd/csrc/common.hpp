@@ -175,6 +175,21 @@ __device__ __forceinline__ typename Elem<T>::vec4 lds_read_tr4(const T* p) {
   return __builtin_bit_cast(typename Elem<T>::vec4, v);
 }
 
+// LDS reads at a byte address (address space 3).  The kernels form one base
+// per read pattern and block and add compile-time offsets, which the
+// instructions take as immediates.
+template <typename V>
+__device__ __forceinline__ V lds_load_at(unsigned addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) V*>(addr);
+}
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::vec4 lds_read_tr4_at(unsigned addr) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const s4 v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) s4*>(addr));
+  return __builtin_bit_cast(typename Elem<T>::vec4, v);
+}
+
 // Combine a per-lane value with the lane 32 positions away (the other half
 // of the wave).  v_permlane32_swap exchanges the halves of two registers;
 // with both operands equal, the two results hold the lower half's and the

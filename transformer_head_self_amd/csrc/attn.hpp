@@ -500,6 +500,21 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
         }
       };
       raw_scores(shifted);
+      // value fragments of this block, read ahead of the weights
+      vec vpre[DMA ? NKB : 1][2][DMA ? C::NDV : 1];
+      if constexpr (DMA) {
+        #pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          #pragma unroll
+          for (int st = 0; st < 2; ++st)
+            #pragma unroll
+            for (int d = 0; d < C::NDV; ++d) {
+              const unsigned v0 = vaddr[d] + (kb * 32 + 16 * st) * C::VRB;
+              const vec4 lo = lds_read_tr4_at<T>(v0);
+              const vec4 hi = lds_read_tr4_at<T>(v0 + 8 * C::VRB);
+              vpre[kb][st][d] = vec{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+      }
 
       // ---- mask: forbidden scores become -inf (weight exactly 0) -------------
       // Score slot (kb, i) of this lane is key k0 + off(kb, i) + 4 g with
@@ -674,18 +689,15 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
           for (int st = 0; st < 2; ++st)
             #pragma unroll
             for (int d = 0; d < C::NDV; ++d) {
-              vec4 lo, hi;
               if constexpr (DMA) {
-                const unsigned v0 = vaddr[d] + (kb * 32 + 16 * st) * C::VRB;
-                lo = lds_read_tr4_at<T>(v0);
-                hi = lds_read_tr4_at<T>(v0 + 8 * C::VRB);
+                mfma_chunk(o[d], vpre[kb][st][d], pb[kb][st]);
               } else {
                 const T* v0 = &vs[(kb * 32 + 16 * st + srow) * C::VROW + d * 32 + scol];
-                lo = lds_read_tr4<T>(v0);
-                hi = lds_read_tr4<T>(v0 + 8 * C::VROW);
+                const vec4 lo = lds_read_tr4<T>(v0);
+                const vec4 hi = lds_read_tr4<T>(v0 + 8 * C::VROW);
+                const vec va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                mfma_chunk(o[d], va, pb[kb][st]);
               }
-              const vec va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-              mfma_chunk(o[d], va, pb[kb][st]);
             }
       } else {
         #pragma unroll

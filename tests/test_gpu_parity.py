@@ -820,6 +820,13 @@ BWD_CASES = [
     ("bf16", "f32", 2, 2, 96, 160, 32, 32, False, None, True, False),
     ("f16", "f32", 2, 2, 150, 150, 64, 64, True, None, False, True),
     ("f16", "f32", 2, 2, 1, 700, 64, 64, False, (700, 300), False, False),
+    # dZ in the heads' type, n_q a multiple of 4: the direct-load dK/dV kernel
+    # (ragged query and key tiles, causal, padding, both widths, 4 rows)
+    ("f16", "f16", 2, 3, 100, 333, 64, 64, False, None, False, False),
+    ("bf16", "bf16", 2, 2, 200, 200, 64, 64, True, (200, 77), False, False),
+    ("f16", "f16", 1, 2, 300, 300, 128, 128, True, (300,), False, False),
+    ("f16", "f16", 2, 2, 4, 700, 64, 64, False, (700, 300), False, False),
+    ("bf16", "bf16", 2, 2, 132, 90, 128, 128, False, (90, 45), False, False),
 ]
 
 
@@ -870,14 +877,16 @@ def test_backward_zero_scale_and_determinism():
         assert np.array_equal(a, b)
 
 
-def test_backward_full_size_two_heads():
-    """The 4 x 4096-token causal shape with 16 heads of 64 (fp16 heads, fp32
-    gradients); two (item, head) pairs checked in full against the oracle."""
+@pytest.mark.parametrize("zdt", ["f32", "f16"])
+def test_backward_full_size_two_heads(zdt):
+    """The 4 x 4096-token causal shape with 16 heads of 64 (fp16 heads; Z,
+    dZ and the gradients in fp32, or in fp16 as the benchmark runs it); two
+    (item, head) pairs checked in full against the oracle."""
     B, h, T, d = 4, 16, 4096, 64
-    _say(f"[backward full size] B={B} h={h} T={T} d={d} causal")
+    _say(f"[backward full size] B={B} h={h} T={T} d={d} causal z={zdt}")
     Qh, Kh, Vh = make_heads(B, h, T, T, d, d, "f32", seed=64)
     dZ = np.random.default_rng(65).standard_normal((B, T, h * d)).astype(np.float32)
-    grads, host, dZh = _bwd_run("f16", "f32", Qh, Kh, Vh, dZ, 0.125, causal=True)
+    grads, host, dZh = _bwd_run("f16", zdt, Qh, Kh, Vh, dZ, 0.125, causal=True)
     allow = allowed_set(1, T, T, causal=True)
     for b, r in ((0, 0), (3, 11)):
         sub = [x[b:b + 1, r:r + 1] for x in host]

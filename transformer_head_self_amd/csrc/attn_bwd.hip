@@ -9,9 +9,27 @@ static hipError_t launch_bwd_fixed(const AttnBwdParams& p, hipStream_t stream) {
   const long long gkv = (long long)((p.n_k + 127) / 128) * BH;
   const long long gq = (long long)((p.n_q + 127) / 128) * BH;
   if (gkv > 2147483647LL || gq > 2147483647LL) return hipErrorInvalidValue;
-  if (gkv > 0)
-    hipLaunchKernelGGL((attn_bwd_kv_kernel<T, DH, DV>), dim3((unsigned)gkv), dim3(256), 0, stream,
-                       p);
+  // Direct-to-LDS tiles for the dK/dV pass: 2-byte dZ of the heads' type,
+  // exact widths of 64 or 128, 16-byte aligned rows, n_q a multiple of 4
+  // (whole 16-byte chunks of the row terms), causal / key-padding masks only.
+  constexpr bool dma_widths = (DH == 64 || DH == 128) && (DV == 64 || DV == 128);
+  const bool dma = dma_widths && p.d_h == DH && p.d_vh == DV && p.z_dtype == p.elem_dtype &&
+                   p.vec_q && p.vec_z && p.ldz % 8 == 0 && p.n_q % 4 == 0 &&
+                   p.allowed == nullptr && p.add == nullptr;
+  if (gkv > 0) {
+    if constexpr (dma_widths) {
+      if (dma) {
+        hipLaunchKernelGGL((attn_bwd_kv_dma_kernel<T, DH, DV>), dim3((unsigned)gkv), dim3(256), 0,
+                           stream, p);
+      } else {
+        hipLaunchKernelGGL((attn_bwd_kv_kernel<T, DH, DV>), dim3((unsigned)gkv), dim3(256), 0,
+                           stream, p);
+      }
+    } else {
+      hipLaunchKernelGGL((attn_bwd_kv_kernel<T, DH, DV>), dim3((unsigned)gkv), dim3(256), 0, stream,
+                         p);
+    }
+  }
   if (gq > 0)
     hipLaunchKernelGGL((attn_bwd_q_kernel<T, DH, DV>), dim3((unsigned)gq), dim3(256), 0, stream, p);
   return hipGetLastError();

@@ -30,6 +30,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "lds_dma.hpp"
 
 namespace mha {
 
@@ -391,6 +392,310 @@ void attn_bwd_kv_kernel(AttnBwdParams p) {
       for (int a = 0; a < 4; ++a) {
         const int e0 = d * 32 + 8 * a + 4 * g;
         store4(p.dV, p.g_dtype, vro + e0, p.vec_dv, p.d_vh - e0, dv[d][4 * a], dv[d][4 * a + 1],
+               dv[d][4 * a + 2], dv[d][4 * a + 3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV with direct-to-LDS tiles (2-byte Q and dZ of exactly DH / DV
+// columns, 16-byte aligned rows, n_q a multiple of 4).  Same products, order
+// of summation and results as attn_bwd_kv_kernel; the 64-row Q and dZ tiles
+// and the rows' L and D move from global memory straight into LDS (three
+// stages in flight) instead of through registers.
+//
+// Each tile is read with two patterns: 16-byte row reads (the A operand of
+// S = Q K^T and dA = dZ V^T) and transposing reads (dZ^T, Q^T).  Rows are
+// stored unpadded with chunk c of row r in slot c ^ bwd_swizzle(r); with the
+// bank line of 256 bytes, h = r / (256 / RB) the bank line of row r and q the
+// number of 64-byte quarters in a row, bwd_swizzle = 4 (h % q) + (h / q) % 4:
+// 16 consecutive rows at one chunk fall in 16 distinct 16-byte bank groups,
+// and the four rows a transposing read touches at one column fall in four
+// distinct 64-byte quarters (checked exhaustively on the CPU).
+// ---------------------------------------------------------------------------
+template <int RB>
+__device__ __forceinline__ int bwd_swizzle(int row) {
+  static_assert(RB == 128 || RB == 256, "rows of 64 or 128 two-byte elements");
+  constexpr int RPB = 256 / RB, Q = RB / 64, CK = RB / 16;
+  const int h = row / RPB;
+  return ((h % Q) * 4 + (h / Q) % 4) % CK;
+}
+
+template <int DH, int DV>
+struct BwdDmaCfg {
+  static constexpr int QRB = DH * 2, ZRB = DV * 2;          // row bytes
+  static constexpr int QT = 64 * QRB, ZT = 64 * ZRB;        // tile bytes
+  static constexpr int AUX = 2048;                          // L (1 KB), D (1 KB)
+  static constexpr int STAGE = QT + ZT + AUX, NS = 3;
+  static constexpr int Q_WIN = QT / 1024 / 4, Z_WIN = ZT / 1024 / 4;   // per wave
+  static constexpr int LDS = NS * STAGE;
+};
+
+template <typename T, int DH, int DV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BwdCfg<DH, DV>::KV_OCC, 2)))
+void attn_bwd_kv_dma_kernel(AttnBwdParams p) {
+  typedef BwdCfg<DH, DV> C;
+  typedef BwdDmaCfg<DH, DV> D;
+  typedef typename Elem<T>::vec vec;
+  typedef typename Elem<T>::vec4 vec4;
+  __shared__ __attribute__((aligned(1024))) char smem[D::LDS];
+  const unsigned lds_base = (unsigned)(size_t)(__attribute__((address_space(3))) char*)smem;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int BH = p.B * p.h;
+  const int kt = blockIdx.x / BH;             // key tile (earliest keys first: most queries)
+  const int bh = blockIdx.x - kt * BH;
+  const int b = bh / p.h, r = bh - b * p.h;
+  const int k0 = kt * 128, k0w = k0 + 32 * wave;
+  const int key = k0w + l32;                  // this lane's key
+  int kvalid = p.n_k;
+  if (p.key_len) kvalid = min(kvalid, p.key_len[b]);
+
+  const T* Qb = reinterpret_cast<const T*>(p.Q) + (size_t)bh * p.n_q * DH;
+  const T* Kb = reinterpret_cast<const T*>(p.K) + (size_t)bh * p.n_k * DH;
+  const T* Vb = reinterpret_cast<const T*>(p.V) + (size_t)bh * p.n_k * DV;
+  const T* Zb = reinterpret_cast<const T*>(p.dZ) + (size_t)b * p.n_q * p.ldz + (size_t)r * DV;
+  const uint8_t* G = p.allowed ? p.allowed + (size_t)b * p.allowed_batch_stride : nullptr;
+  const float* M = p.add ? p.add + (size_t)b * p.add_batch_stride : nullptr;
+  const float* lse = p.lse2 + (size_t)bh * p.n_q;
+  const float* dsm = p.dsum + (size_t)bh * p.n_q;
+
+  vec kf[C::KCH], vf[C::VCH];
+  #pragma unroll
+  for (int c = 0; c < C::KCH; ++c)
+    kf[c] = key < p.n_k ? *reinterpret_cast<const vec*>(Kb + (size_t)key * DH + 16 * c + 8 * g)
+                        : zero_vec<vec>();
+  #pragma unroll
+  for (int c = 0; c < C::VCH; ++c)
+    vf[c] = key < p.n_k ? *reinterpret_cast<const vec*>(Vb + (size_t)key * DV + 16 * c + 8 * g)
+                        : zero_vec<vec>();
+
+  floatx16 dk[C::NDH], dv[C::NDV];
+  #pragma unroll
+  for (int d = 0; d < C::NDH; ++d)
+    #pragma unroll
+    for (int i = 0; i < 16; ++i) dk[d][i] = 0.f;
+  #pragma unroll
+  for (int d = 0; d < C::NDV; ++d)
+    #pragma unroll
+    for (int i = 0; i < 16; ++i) dv[d][i] = 0.f;
+
+  const int qb0 = (p.causal ? k0 : 0) / C::BR;
+  const int nqb = (k0 < kvalid) ? (p.n_q + C::BR - 1) / C::BR : qb0;
+
+  // ---- direct loads: window q of this wave covers tile bytes
+  // (wave * WIN + q) KB; lane i fills 16 bytes at 16 i, i.e. tile row t / RB,
+  // slot (t % RB) / 16, from the global chunk the slot holds.  Rows past n_q
+  // read the last row (never used: their weights are 0).
+  auto q_row = [&](int win) { return (win * 1024 + 16 * lane) / D::QRB; };
+  auto z_row = [&](int win) { return (win * 1024 + 16 * lane) / D::ZRB; };
+  auto q_chunk = [&](int win) {
+    const int t = win * 1024 + 16 * lane, row = t / D::QRB;
+    return ((t % D::QRB) / 16) ^ bwd_swizzle<D::QRB>(row);
+  };
+  auto z_chunk = [&](int win) {
+    const int t = win * 1024 + 16 * lane, row = t / D::ZRB;
+    return ((t % D::ZRB) / 16) ^ bwd_swizzle<D::ZRB>(row);
+  };
+  // L (wave 0) and D (wave 1): lane i loads rows 4 (i % 16) .. +3 of the
+  // tile; lanes 16..63 repeat them into spare LDS bytes.  n_q % 4 == 0, so
+  // a 4-row chunk is either all valid or all past n_q (then the last chunk).
+  const bool aux_wave = wave < 2;
+  const float* aux_src = wave == 0 ? lse : dsm;
+  auto issue = [&](int qb) {
+    const int q0 = qb * C::BR;
+    const unsigned st = lds_base + (unsigned)((qb % D::NS) * D::STAGE);
+    const char* qg = reinterpret_cast<const char*>(Qb + (size_t)q0 * DH);
+    const char* zg = reinterpret_cast<const char*>(Zb + (size_t)q0 * p.ldz);
+    const int last = p.n_q - 1 - q0;   // last valid row of the tile
+    #pragma unroll
+    for (int q = 0; q < D::Q_WIN; ++q) {
+      const int win = wave * D::Q_WIN + q;
+      const unsigned off = (unsigned)(min(q_row(win), last) * D::QRB + q_chunk(win) * 16);
+      lds_dma16(qg, off, st + win * 1024);
+    }
+    #pragma unroll
+    for (int q = 0; q < D::Z_WIN; ++q) {
+      const int win = wave * D::Z_WIN + q;
+      const unsigned off =
+          (unsigned)(min(z_row(win), last) * p.ldz * 2 + z_chunk(win) * 16);
+      lds_dma16(zg, off, st + D::QT + win * 1024);
+    }
+    if (aux_wave) {
+      const int row = min(q0 + 4 * (lane & 15), p.n_q - 4);
+      lds_dma16(aux_src, (unsigned)row * 4u, st + D::QT + D::ZT + wave * 1024);
+    }
+  };
+
+  // ---- per-lane LDS read offsets within a stage (bytes) ----------------------
+  // 16-byte row reads: row 32 sb + l32, chunk 2 c + g (the swizzle depends on
+  // the row through l32 only).  Transposing reads: row 32 sb + 16 st + 8 hh +
+  // 4 g + (lane % 16) / 4, columns 32 d + scol; the swizzle depends on the row
+  // through 8 hh + 4 g + (lane % 16) / 4, so hh gets its own base.
+  int qro[C::KCH], zro[C::VCH], qtr[C::NDH][2], ztr[C::NDV][2];
+  #pragma unroll
+  for (int c = 0; c < C::KCH; ++c)
+    qro[c] = l32 * D::QRB + (((2 * c + g) ^ bwd_swizzle<D::QRB>(l32)) * 16);
+  #pragma unroll
+  for (int c = 0; c < C::VCH; ++c)
+    zro[c] = D::QT + l32 * D::ZRB + (((2 * c + g) ^ bwd_swizzle<D::ZRB>(l32)) * 16);
+  {
+    const int scol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    #pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int vr = 8 * hh + 4 * g + ((lane & 15) >> 2);
+      #pragma unroll
+      for (int d = 0; d < C::NDH; ++d) {
+        const int col = d * 32 + scol;
+        qtr[d][hh] = vr * D::QRB + (((col / 8) ^ bwd_swizzle<D::QRB>(vr)) * 16) + (col % 8) * 2;
+      }
+      #pragma unroll
+      for (int d = 0; d < C::NDV; ++d) {
+        const int col = d * 32 + scol;
+        ztr[d][hh] = D::QT + vr * D::ZRB + (((col / 8) ^ bwd_swizzle<D::ZRB>(vr)) * 16) +
+                     (col % 8) * 2;
+      }
+    }
+  }
+  const int aro = D::QT + D::ZT + 16 * g;   // L of query 4 g + 8 a + 32 sb: + 4 (8 a + 32 sb)
+
+  constexpr int LOADS = D::Q_WIN + D::Z_WIN;   // per wave per tile, plus one on waves 0, 1
+  if (nqb > qb0) issue(qb0);
+  if (nqb > qb0 + 1) issue(qb0 + 1);
+  const float cs = p.scale_log2;
+
+  for (int qb = qb0; qb < nqb; ++qb) {
+    // tile qb has landed once only tile qb+1's loads are outstanding; after
+    // the barrier no wave reads tile qb-1, whose stage gets tile qb+2
+    if (qb + 1 < nqb) {
+      if (aux_wave) wait_vm_lds<LOADS + 1>();
+      else wait_vm_lds<LOADS>();
+    } else {
+      wait_vm_lds<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    if (qb + 2 < nqb) issue(qb + 2);
+
+    unsigned st_addr = lds_base + (unsigned)((qb % D::NS) * D::STAGE);
+    asm("" : "+s"(st_addr));
+    unsigned qa_addr[C::KCH], za_addr[C::VCH], qt_addr[C::NDH][2], zt_addr[C::NDV][2], a_addr;
+    #pragma unroll
+    for (int c = 0; c < C::KCH; ++c) {
+      qa_addr[c] = st_addr + (unsigned)qro[c];
+      asm("" : "+v"(qa_addr[c]));
+    }
+    #pragma unroll
+    for (int c = 0; c < C::VCH; ++c) {
+      za_addr[c] = st_addr + (unsigned)zro[c];
+      asm("" : "+v"(za_addr[c]));
+    }
+    #pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      #pragma unroll
+      for (int d = 0; d < C::NDH; ++d) {
+        qt_addr[d][hh] = st_addr + (unsigned)qtr[d][hh];
+        asm("" : "+v"(qt_addr[d][hh]));
+      }
+      #pragma unroll
+      for (int d = 0; d < C::NDV; ++d) {
+        zt_addr[d][hh] = st_addr + (unsigned)ztr[d][hh];
+        asm("" : "+v"(zt_addr[d][hh]));
+      }
+    }
+    a_addr = st_addr + (unsigned)aro;
+    asm("" : "+v"(a_addr));
+
+    const int q0 = qb * C::BR;
+    #pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int qs0 = q0 + 32 * sb;
+      if ((p.causal && qs0 + 31 < k0w) || k0w >= kvalid || qs0 >= p.n_q) continue;
+      floatx16 sacc, dpacc;
+      #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sacc[i] = 0.f;
+        dpacc[i] = 0.f;
+      }
+      #pragma unroll
+      for (int c = 0; c < C::KCH; ++c)
+        mfma_chunk(sacc, lds_load_at<vec>(qa_addr[c] + 32 * sb * D::QRB), kf[c]);
+      #pragma unroll
+      for (int c = 0; c < C::VCH; ++c)
+        mfma_chunk(dpacc, lds_load_at<vec>(za_addr[c] + 32 * sb * D::ZRB), vf[c]);
+      // L and D of slot i's query 32 sb + 8 (i/4) + 4 g + i%4
+      floatx4 lq[4], dq[4];
+      #pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        lq[a] = lds_load_at<floatx4>(a_addr + 4 * (8 * a + 32 * sb));
+        dq[a] = lds_load_at<floatx4>(a_addr + 1024 + 4 * (8 * a + 32 * sb));
+      }
+      const bool need_mask = (p.causal && qs0 < k0w + 31) || (k0w + 31 >= kvalid) ||
+                             (qs0 + 31 >= p.n_q) || G != nullptr || M != nullptr;
+      #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int q = qs0 + 8 * (i >> 2) + 4 * g + (i & 3);
+        float x = sacc[i] * cs;
+        bool ok = true;
+        if (need_mask) {
+          ok = bwd_allowed(p, G, q, key, kvalid);
+          if (M != nullptr && ok) x = fmaf(M[(size_t)q * p.n_k + key], kLog2e, x);
+        }
+        const float a = ok ? __builtin_amdgcn_exp2f(x - lq[i >> 2][i & 3]) : 0.f;
+        sacc[i] = a;
+        dpacc[i] = a * (dpacc[i] - dq[i >> 2][i & 3]);
+      }
+      #pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        floatx8 af, sf;
+        #pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          af[t] = sacc[8 * st + t];
+          sf[t] = dpacc[8 * st + t];
+        }
+        const vec ab = Cvt<T>::eight(af);
+        const vec sbv = Cvt<T>::eight(sf);
+        #pragma unroll
+        for (int d = 0; d < C::NDV; ++d) {
+          const unsigned o = (32 * sb + 16 * st) * D::ZRB;
+          const vec4 lo = lds_read_tr4_at<T>(zt_addr[d][0] + o);
+          const vec4 hi = lds_read_tr4_at<T>(zt_addr[d][1] + o);
+          const vec za = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          mfma_chunk(dv[d], za, ab);
+        }
+        #pragma unroll
+        for (int d = 0; d < C::NDH; ++d) {
+          const unsigned o = (32 * sb + 16 * st) * D::QRB;
+          const vec4 lo = lds_read_tr4_at<T>(qt_addr[d][0] + o);
+          const vec4 hi = lds_read_tr4_at<T>(qt_addr[d][1] + o);
+          const vec qa = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          mfma_chunk(dk[d], qa, sbv);
+        }
+      }
+    }
+  }
+
+  if (key < p.n_k) {
+    const size_t krow = p.grad_concat ? ((size_t)b * p.n_k + key) * p.h + r
+                                      : (size_t)bh * p.n_k + key;
+    const size_t kro = krow * DH;
+    const size_t vro = krow * DV;
+    #pragma unroll
+    for (int d = 0; d < C::NDH; ++d)
+      #pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int e0 = d * 32 + 8 * a + 4 * g;
+        store4(p.dK, p.g_dtype, kro + e0, p.vec_dk, DH - e0, dk[d][4 * a] * p.scale,
+               dk[d][4 * a + 1] * p.scale, dk[d][4 * a + 2] * p.scale, dk[d][4 * a + 3] * p.scale);
+      }
+    #pragma unroll
+    for (int d = 0; d < C::NDV; ++d)
+      #pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int e0 = d * 32 + 8 * a + 4 * g;
+        store4(p.dV, p.g_dtype, vro + e0, p.vec_dv, DV - e0, dv[d][4 * a], dv[d][4 * a + 1],
                dv[d][4 * a + 2], dv[d][4 * a + 3]);
       }
   }

@@ -30,8 +30,24 @@ static hipError_t launch_bwd_fixed(const AttnBwdParams& p, hipStream_t stream) {
                          p);
     }
   }
-  if (gq > 0)
-    hipLaunchKernelGGL((attn_bwd_q_kernel<T, DH, DV>), dim3((unsigned)gq), dim3(256), 0, stream, p);
+  // Direct-to-LDS key tiles for the dQ pass: K and V exactly 64 or 128
+  // wide with 16-byte aligned rows, causal / key-padding masks only.
+  const bool qdma = dma_widths && p.d_h == DH && p.d_vh == DV && p.vec_k && p.vec_v &&
+                    p.allowed == nullptr && p.add == nullptr;
+  if (gq > 0) {
+    if constexpr (dma_widths) {
+      if (qdma) {
+        hipLaunchKernelGGL((attn_bwd_q_dma_kernel<T, DH, DV>), dim3((unsigned)gq), dim3(256), 0,
+                           stream, p);
+      } else {
+        hipLaunchKernelGGL((attn_bwd_q_kernel<T, DH, DV>), dim3((unsigned)gq), dim3(256), 0,
+                           stream, p);
+      }
+    } else {
+      hipLaunchKernelGGL((attn_bwd_q_kernel<T, DH, DV>), dim3((unsigned)gq), dim3(256), 0, stream,
+                         p);
+    }
+  }
   return hipGetLastError();
 }
 

@@ -231,8 +231,9 @@ typedef struct mha_bias_grad {
 
 /* Scratch mha_backward needs for these dims, 256-byte aligned regions:
  * dZ, and the three heads' gradients in the concatenated layout (work_dtype),
- * the backward's row terms, and the column-sum partials of the bias
- * gradients.  Returns 0 if `d` is NULL or invalid. */
+ * the backward's row terms, the column-sum partials of the bias gradients,
+ * the fp32 partial products of the K-split weight gradients, and (out_dtype
+ * F32) dY rounded to work_dtype.  Returns 0 if `d` is NULL or invalid. */
 size_t mha_backward_workspace_bytes(const mha_dims* d);
 
 /* Backward pass of mha_forward: gradients of a scalar loss with respect to

@@ -952,7 +952,14 @@ LAYER_BWD_CASES = [
     ("self", 2, 96, 96, 64, 64, 64, 4, 16, 16, 64, True, None, False, True),
     ("cross", 2, 70, 150, 96, 80, 112, 3, 32, 48, 72, False, (150, 40), True, False),
     ("self", 2, 512, 512, 512, 512, 512, 8, 64, 64, 512, True, None, False, True),
+    # the direct-load gradient products with K split in four (weight
+    # gradients over 4096 rows), and with bf16 intermediates
+    ("self", 2, 2048, 2048, 256, 256, 256, 4, 64, 64, 256, True, None, False, True),
+    ("self", 2, 512, 512, 512, 512, 512, 8, 64, 64, 512, True, None, False, True, "bf16"),
 ]
+
+# bf16 intermediates: each rounding is 2^-8 instead of fp16's 2^-11
+LAYER_TOL_BF16 = (8 * LAYER_TOL[0], 8 * LAYER_TOL[1])
 
 
 @pytest.mark.parametrize("case", LAYER_BWD_CASES, ids=lambda c: "-".join(map(str, c)))
@@ -961,7 +968,9 @@ def test_layer_backward_matches_oracle(case):
     the forward through the library (its workspace and row statistics kept),
     then mha_backward, against the float64 gradients of the whole layer."""
     (kind, B, n_q, n_k, d_q, d_k, d_v, h, d_h, d_vh, d_o, causal, kl, use_add,
-     use_bias) = case
+     use_bias) = case[:15]
+    wdt = case[15] if len(case) > 15 else "f16"
+    tol = LAYER_TOL if wdt == "f16" else LAYER_TOL_BF16
     _say(f"[layer backward] {case}")
     rng = np.random.default_rng(97 + n_q)
     Q = _cast(rng.standard_normal((B, n_q, d_q)), "bf16")
@@ -989,22 +998,25 @@ def test_layer_backward_matches_oracle(case):
     kl_dev = None if key_len is None else torch.from_numpy(key_len).to(DEV)
     M_dev = None if M is None else torch.from_numpy(M).to(DEV)
     dims = mha.MhaDims(B=B, h=h, n_q=n_q, n_k=n_k, d_q=d_q, d_k=d_k, d_v=d_v, d_h=d_h,
-                       d_vh=d_vh, d_o=d_o, scale=c, in_dtype=1, out_dtype=0, work_dtype=2)
+                       d_vh=d_vh, d_o=d_o, scale=c, in_dtype=1, out_dtype=0,
+                       work_dtype=2 if wdt == "f16" else 1)
     fws = torch.empty(mha.mha_workspace_bytes(dims), dtype=torch.uint8, device=DEV)
     rm = torch.empty((B, h, n_q), device=DEV)
     rl = torch.empty_like(rm)
+    wt = torch.float16 if wdt == "f16" else torch.bfloat16
     mha.mha_forward(tQ, tK, tV, tW["W_Q"], tW["W_K"], tW["W_V"], tW["W_O"], h, d_h, d_vh,
                     scale=c, causal=causal, key_len=kl_dev, add=M_dev, row_m=rm, row_l=rl,
-                    workspace=fws, **{k: _to_dev(v, "bf16") for k, v in bs.items()})
+                    workspace=fws, work_dtype=wt,
+                    **{k: _to_dev(v, "bf16") for k, v in bs.items()})
     g = mha.mha_backward(tQ, tK, tV, tW["W_Q"], tW["W_K"], tW["W_V"], tW["W_O"], h, d_h, d_vh,
                          torch.from_numpy(dY).to(DEV), rm, rl, fws, scale=c, causal=causal,
-                         key_len=kl_dev, add=M_dev, bias_grads=True)
+                         key_len=kl_dev, add=M_dev, work_dtype=wt, bias_grads=True)
     torch.cuda.synchronize()
     for name in ("dQ", "dK", "dV", "dW_Q", "dW_K", "dW_V", "dW_O"):
         got = g[name].cpu().numpy()
         fro, mx = _grad_err(got, ref[name])
         _say(f"  {name} normwise {fro:.3e} max {mx:.3e}")
-        assert fro <= LAYER_TOL[0] and mx <= LAYER_TOL[1], name
+        assert fro <= tol[0] and mx <= tol[1], name
     # a bias gradient is a column sum, which can cancel to nothing (db_K is
     # exactly 0: a key bias moves every score of a row by one constant), so
     # its error is measured against the sum of the terms' magnitudes
@@ -1013,4 +1025,4 @@ def test_layer_backward_matches_oracle(case):
         scale = np.abs(np.asarray(t, np.float64)).sum(axis=(0, 1))
         err = float(np.max(np.abs(g[name].cpu().numpy() - ref[name]) / scale))
         _say(f"  {name} error / sum of |terms| {err:.3e}")
-        assert err <= LAYER_TOL[0], name
+        assert err <= tol[0], name

@@ -228,7 +228,7 @@ void fill_bwd_mask(mha::AttnBwdParams& p, const mha_mask* m) {
 // mha_backward scratch: dZ and the heads' gradients in the concatenated
 // layout (work_dtype), the core backward's row terms, column-sum partials.
 struct BwdWorkspace {
-  size_t dz, dq, dk, dv, lse, dsum, part, splitk, total;
+  size_t dz, dq, dk, dv, lse, dsum, part, splitk, dy, total;
 };
 
 BwdWorkspace carve_bwd(const mha_dims* d) {
@@ -253,7 +253,11 @@ BwdWorkspace carve_bwd(const mha_dims* d) {
   sk = std::max(sk, mha::gemm_any_partial_floats(d->d_q, Nq, Mq));
   sk = std::max(sk, mha::gemm_any_partial_floats(d->d_k, Nq, Mk));
   sk = std::max(sk, mha::gemm_any_partial_floats(d->d_v, Nv, Mk));
-  w.total = w.splitk + round256(sk * 4);
+  w.dy = w.splitk + round256(sk * 4);
+  // an fp32 dY rounded once to work_dtype for the products that use it (the
+  // general product would round it the same way as it stages it)
+  const size_t dy_bytes = d->out_dtype == MHA_F32 ? (size_t)Mq * d->d_o * es : 0;
+  w.total = w.dy + round256(dy_bytes);
   return w;
 }
 
@@ -471,10 +475,19 @@ mha_status mha_backward(const mha_dims* d, const mha_mask* m, const void* Q, con
   };
 
   // output projection: dZ = dY W_O^T (W_O [Nv, d_o] is W_O^T stored k-contiguous),
-  // dW_O = Z^T dY, db_O = column sums of dY
+  // dW_O = Z^T dY, db_O = column sums of dY (of dY as given)
   void* dZ = ws + bw.dz;
-  if (!gemm(dY, od, d->d_o, 0, W_O, id, d->d_o, 1, dZ, Mq, Nv, d->d_o)) return MHA_ERR_LAUNCH;
-  if (dW_O && !gemm(fws + fw.z, wd, Nv, 1, dY, od, d->d_o, 0, dW_O, Nv, d->d_o, Mq))
+  const void* dYp = dY;
+  int dydt = od;
+  if (od == MHA_F32) {
+    if (mha::launch_round_f32(static_cast<const float*>(dY), ws + bw.dy, (size_t)Mq * d->d_o, wd,
+                              st) != hipSuccess)
+      return MHA_ERR_LAUNCH;
+    dYp = ws + bw.dy;
+    dydt = wd;
+  }
+  if (!gemm(dYp, dydt, d->d_o, 0, W_O, id, d->d_o, 1, dZ, Mq, Nv, d->d_o)) return MHA_ERR_LAUNCH;
+  if (dW_O && !gemm(fws + fw.z, wd, Nv, 1, dYp, dydt, d->d_o, 0, dW_O, Nv, d->d_o, Mq))
     return MHA_ERR_LAUNCH;
   if (db.db_O && mha::launch_colsum(dY, od, d->d_o, Mq, d->d_o, db.db_O, od, part, st) != hipSuccess)
     return MHA_ERR_LAUNCH;

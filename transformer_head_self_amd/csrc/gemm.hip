@@ -6,6 +6,7 @@
 #include "gemm_any.hpp"
 #include "gemm_dma.hpp"
 #include "gemm_dma_wide.hpp"
+#include "gemm_grad.hpp"
 
 namespace mha {
 
@@ -102,9 +103,76 @@ static int gemm_any_splits(int M, int N, int K) {
   return (int)std::max<long long>(s, 1);
 }
 
+// Direct-load gradient GEMM (gemm_grad_kernel): whole 256 x 256 tiles and
+// 64-deep k stages.  Split-K when the output has fewer than 128 tiles and K
+// is long: about 256 workgroups, K partitions of at least 1024 (multiples of
+// 64).
+static bool grad_dims_fit(int M, int N, int K) {
+  return M > 0 && N > 0 && K > 0 && M % 256 == 0 && N % 256 == 0 && K % 64 == 0;
+}
+static int grad_splits(int M, int N, int K) {
+  if (!grad_dims_fit(M, N, K)) return 1;
+  const long long tiles = (long long)(M / 256) * (N / 256);
+  if (tiles >= 128 || K < 2048) return 1;
+  long long s = (256 + tiles - 1) / tiles;
+  s = std::min<long long>(s, K / 1024);
+  return (int)std::max<long long>(s, 1);
+}
+
 size_t gemm_any_partial_floats(int M, int N, int K) {
-  const int s = gemm_any_splits(M, N, K);
+  const int s = std::max(gemm_any_splits(M, N, K), grad_splits(M, N, K));
   return s > 1 ? (size_t)s * M * N : 0;
+}
+
+// The direct-load gradient GEMM applies: 2-byte operands (both bf16 for a
+// bf16 product), one of its two layouts, whole tiles, 16-byte aligned rows,
+// byte offsets within a stage below 2^31.
+static bool grad_gemm_applies(const GemmAny& g, int compute_dtype) {
+  const bool two = g.a_dtype != kF32 && g.w_dtype != kF32;
+  const bool types = compute_dtype == kF16
+                         ? two
+                         : (compute_dtype == kBF16 && g.a_dtype == kBF16 && g.w_dtype == kBF16);
+  const bool layout = (g.a_trans == 0 && g.w_trans == 1) || (g.a_trans == 1 && g.w_trans == 0);
+  if (!types || !layout || !grad_dims_fit(g.M, g.N, g.K) || !g.vec_a || !g.vec_w) return false;
+  // row tiles: (rows - 1) * ld + 64 elements; k-major tiles: 64 * ld + rows
+  const long long ra = g.a_trans ? 64LL * g.lda + g.M : (long long)g.M * g.lda;
+  const long long rw = g.w_trans ? (long long)g.N * g.ldw : 64LL * g.ldw + g.N;
+  return 2 * ra < (1LL << 31) && 2 * rw < (1LL << 31);
+}
+
+template <typename T, typename TA, typename TW>
+static void launch_grad_typed(const GemmAny& g, dim3 grid, hipStream_t stream) {
+  if (g.a_trans)
+    hipLaunchKernelGGL((gemm_grad_kernel<T, TA, TW, true, false>), grid, dim3(512), 0, stream, g);
+  else
+    hipLaunchKernelGGL((gemm_grad_kernel<T, TA, TW, false, true>), grid, dim3(512), 0, stream, g);
+}
+
+static hipError_t launch_gemm_grad(GemmAny g, int compute_dtype, float* partial,
+                                   hipStream_t stream) {
+  g.ksplit = grad_splits(g.M, g.N, g.K);
+  if (g.ksplit > 1 && partial == nullptr) return hipErrorInvalidValue;
+  g.kchunk = g.ksplit > 1 ? ((g.K + g.ksplit - 1) / g.ksplit + 63) / 64 * 64 : g.K;
+  g.ksplit = (g.K + g.kchunk - 1) / g.kchunk;
+  g.partial = partial;
+  const long long wgs = (long long)(g.M / 256) * (g.N / 256) * g.ksplit;
+  if (wgs > 2147483647LL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wgs);
+  if (compute_dtype == kBF16) {
+    launch_grad_typed<bf16, bf16, bf16>(g, grid, stream);
+  } else if (g.a_dtype == kBF16) {
+    if (g.w_dtype == kBF16) launch_grad_typed<f16, bf16, bf16>(g, grid, stream);
+    else launch_grad_typed<f16, bf16, f16>(g, grid, stream);
+  } else {
+    if (g.w_dtype == kBF16) launch_grad_typed<f16, f16, bf16>(g, grid, stream);
+    else launch_grad_typed<f16, f16, f16>(g, grid, stream);
+  }
+  if (g.ksplit > 1) {
+    const size_t n = (size_t)g.M * g.N;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, partial, g.ksplit, g.M, g.N, g.C, g.c_dtype, g.ldc);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_any(GemmAny g, int compute_dtype, float* partial, hipStream_t stream) {
@@ -115,6 +183,7 @@ hipError_t launch_gemm_any(GemmAny g, int compute_dtype, float* partial, hipStre
   g.vec_a = aligned_to(g.A, 16) && g.lda % vec == 0;
   g.vec_w = aligned_to(g.W, 16) && g.ldw % vec == 0;
   g.vec_c = aligned_to(g.C, 4 * elem_size(g.c_dtype)) && g.ldc % 4 == 0;
+  if (grad_gemm_applies(g, compute_dtype)) return launch_gemm_grad(g, compute_dtype, partial, stream);
   g.ksplit = gemm_any_splits(g.M, g.N, g.K);
   if (g.ksplit > 1 && partial == nullptr) return hipErrorInvalidValue;
   // K chunks are whole 32-element stages (vector loads stay aligned)
@@ -136,6 +205,15 @@ hipError_t launch_gemm_any(GemmAny g, int compute_dtype, float* partial, hipStre
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        stream, partial, g.ksplit, g.M, g.N, g.C, g.c_dtype, g.ldc);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_round_f32(const float* x, void* y, size_t n, int y_dtype, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256;
+  if (blocks > 2147483647ULL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(round_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, y, n,
+                     y_dtype);
   return hipGetLastError();
 }
 

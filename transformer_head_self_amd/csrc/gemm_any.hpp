@@ -225,6 +225,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* partial
   else reinterpret_cast<f16*>(C)[o] = (f16)sum;
 }
 
+// y[i] = x[i] rounded to y's element type (nearest even), fp32 source.
+__global__ __launch_bounds__(256) void round_f32_kernel(const float* x, void* y, size_t n,
+                                                        int y_dtype) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  if (y_dtype == kBF16) reinterpret_cast<bf16*>(y)[i] = (bf16)x[i];
+  else reinterpret_cast<f16*>(y)[i] = (f16)x[i];
+}
+
 // Column sums of a row-major [M, N] array of type dt (row stride ld): pass 1
 // sums rows [256 r, 256 r + 256) of column n into part[r * N + n]; pass 2 sums
 // the R partial rows into out[n] (type out_dtype).  Fixed order: deterministic.

@@ -67,6 +67,9 @@ struct GemmAny {
 size_t gemm_any_partial_floats(int M, int N, int K);
 hipError_t launch_gemm_any(GemmAny g, int compute_dtype, float* partial, hipStream_t stream);
 
+// y = x rounded to y_dtype (bf16 or fp16, nearest even); n fp32 elements.
+hipError_t launch_round_f32(const float* x, void* y, size_t n, int y_dtype, hipStream_t stream);
+
 // out[n] = sum over m < M of X[m * ld + n] (n < N), in a fixed order;
 // `part` is fp32 scratch of colsum_scratch_floats(M, N) elements.
 size_t colsum_scratch_floats(int M, int N);

@@ -257,7 +257,7 @@ def backward_bench(args, torch):
         "dtype": "f16", "data": "synthetic",
         "config": {"workload": "attn-backward-f16-B4-T4096-h16-d64-causal",
                    "flops_per_step": bwd_flops},
-        "roofline": {"bound": "mfma", "kernel": "attn_bwd_kv_kernel + attn_bwd_q_kernel",
+        "roofline": {"bound": "mfma", "kernel": "attn_bwd_kv_dma_kernel + attn_bwd_q_dma_kernel",
                      "achieved": round(tf, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tf / peak, 4)},
         "forward_ms": round(ms_fwd, 5),

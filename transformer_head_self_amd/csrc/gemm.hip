@@ -210,10 +210,15 @@ hipError_t launch_gemm_any(GemmAny g, int compute_dtype, float* partial, hipStre
 
 hipError_t launch_round_f32(const float* x, void* y, size_t n, int y_dtype, hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  const size_t blocks = (n + 255) / 256;
+  const size_t blocks = (n + 2047) / 2048;   // eight elements per thread
   if (blocks > 2147483647ULL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(round_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, y, n,
-                     y_dtype);
+  const int vec = aligned_to(x, 16) && aligned_to(y, 16);
+  if (y_dtype == kBF16)
+    hipLaunchKernelGGL(round_f32_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                       reinterpret_cast<bf16*>(y), n, vec);
+  else
+    hipLaunchKernelGGL(round_f32_kernel<f16>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
+                       reinterpret_cast<f16*>(y), n, vec);
   return hipGetLastError();
 }
 

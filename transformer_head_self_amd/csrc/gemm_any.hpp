@@ -225,13 +225,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* partial
   else reinterpret_cast<f16*>(C)[o] = (f16)sum;
 }
 
-// y[i] = x[i] rounded to y's element type (nearest even), fp32 source.
-__global__ __launch_bounds__(256) void round_f32_kernel(const float* x, void* y, size_t n,
-                                                        int y_dtype) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  if (y_dtype == kBF16) reinterpret_cast<bf16*>(y)[i] = (bf16)x[i];
-  else reinterpret_cast<f16*>(y)[i] = (f16)x[i];
+// y[i] = x[i] rounded to y's element type (nearest even), fp32 source; each
+// thread takes eight consecutive elements (two 16-byte loads, one 16-byte
+// store when x and y are 16-byte aligned and all eight exist).
+template <typename TY>
+__global__ __launch_bounds__(256) void round_f32_kernel(const float* x, TY* y, size_t n,
+                                                        int vec_ok) {
+  typedef typename Elem<TY>::vec V;
+  const size_t i0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i0 >= n) return;
+  if (vec_ok && i0 + 8 <= n) {
+    const floatx4 a = *reinterpret_cast<const floatx4*>(x + i0);
+    const floatx4 b = *reinterpret_cast<const floatx4*>(x + i0 + 4);
+    const floatx8 f = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    *reinterpret_cast<V*>(y + i0) = __builtin_convertvector(f, V);
+  } else {
+    for (size_t i = i0; i < n && i < i0 + 8; ++i) y[i] = (TY)x[i];
+  }
 }
 
 // Column sums of a row-major [M, N] array of type dt (row stride ld): pass 1

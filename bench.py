@@ -46,6 +46,24 @@ def attn_source_hash():
     return h.hexdigest()[:16]
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # MI355X dense matrix-core peaks
 HBM_PEAK_GBS = 8000.0
+# Exponential (v_exp_f32) peak: 256 CUs x 4 SIMDs x 8 results per cycle (a
+# wave64 exponential occupies its SIMD for 8 cycles: SQ_ACTIVE_INST_VALU of the
+# attention kernel accounts for 32 exponentials per block at 8 cycles and the
+# other VALU instructions at 4) x 2.4 GHz.
+EXP_PEAK_T_PER_S = 256 * 4 * 8 * 2.4e9 / 1e12
+
+
+def gpu_sclk_mhz():
+    """Current shader clock from the driver's DPM table (sysfs), or None."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(path):
+                if line.rstrip().endswith("*"):
+                    return int(line.split(":")[1].strip().lower().split("mhz")[0])
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
 
 
 def parse():
@@ -361,6 +379,7 @@ def main():
     for _ in range(args.steps):
         core()
     c1.record(stream)
+    sclk = gpu_sclk_mhz()   # read while the timed launches run
     torch.cuda.synchronize()
     ms_core = c0.elapsed_time(c1) / args.steps
 
@@ -369,6 +388,7 @@ def main():
     value = total_flops / (ms_step * 1e-3) / 1e12
     core_tflops = core_flops / (ms_core * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
+    exps = core_flops / (2.0 * (w.d_h + w.d_vh))   # allowed scores
 
     traffic = None
     if os.path.exists(args.traffic_json):
@@ -407,6 +427,13 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel (attention core)",
                      "achieved": round(core_tflops, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(core_tflops / peak, 4), "traffic": traffic},
+        # the softmax's second ceiling: one exponential per allowed score
+        # (counted as the metric counts scores)
+        "exp_co_roof": {"exps_per_launch": int(exps),
+                        "achieved": round(exps / (ms_core * 1e-3) / 1e12, 3),
+                        "peak": round(EXP_PEAK_T_PER_S, 2), "unit": "T exp/s",
+                        "frac": round(exps / (ms_core * 1e-3) / 1e12 / EXP_PEAK_T_PER_S, 4)},
+        "sclk_mhz": sclk,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)

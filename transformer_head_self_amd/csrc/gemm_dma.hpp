@@ -186,11 +186,17 @@ void gemm_dma_kernel(GemmBatch batch) {
   };
   issue_stage(B0(), 0);
   if (1 < nstage) issue_stage(B1(), 1);
-  for (int s = 0; s < nstage; s += 3) {
+  // whole groups of three stages, then the rest outside the loop (no
+  // conditional steps inside it: they made the compiler copy the
+  // accumulators between register assignments on every iteration)
+  int s = 0;
+  for (; s + 2 < nstage; s += 3) {
     step(B0(), B2(), s);
-    if (s + 1 < nstage) step(B1(), B0(), s + 1);
-    if (s + 2 < nstage) step(B2(), B1(), s + 2);
+    step(B1(), B0(), s + 1);
+    step(B2(), B1(), s + 2);
   }
+  if (s < nstage) step(B0(), B2(), s);
+  if (s + 1 < nstage) step(B1(), B0(), s + 1);
 
   // The epilogue's index arithmetic starts here: opaque copies of its inputs
   // keep the compiler from computing it before the loop, where it would hold

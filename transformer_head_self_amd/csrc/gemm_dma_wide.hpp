@@ -179,10 +179,15 @@ void gemm_dma_wide_kernel(GemmBatch batch) {
     compute(b);
   };
   issue_stage(B0(), 0);
-  for (int s = 0; s < nstage; s += 2) {
+  // pairs of stages, then an odd last one outside the loop: a conditional
+  // second step inside the loop made the compiler copy the accumulators
+  // between two register assignments on every iteration
+  int s = 0;
+  for (; s + 1 < nstage; s += 2) {
     step(B0(), B1(), s);
-    if (s + 1 < nstage) step(B1(), B0(), s + 1);
+    step(B1(), B0(), s + 1);
   }
+  if (s < nstage) step(B0(), B1(), s);
 
   // The epilogue's index arithmetic starts here (opaque copies of its inputs
   // keep the compiler from computing it before the loop).

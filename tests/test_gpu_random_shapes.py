@@ -1,0 +1,102 @@
+"""Seeded random shapes through the attention core forward and backward
+against the float64 oracle.
+
+The shapes are drawn once from a fixed seed (ragged n_q and n_k, head widths
+32 to 128, causal and key-padding masks, fp16 and bf16 heads, with and without
+row statistics, Z / dZ in the heads' type or fp32), so every launch path of
+the core kernels (direct-load fast paths, the general path, the decode-shaped
+and the register-staged backward) meets shapes no hand-written case picked.
+Bars as in test_gpu_parity: the forward's max |err| / RMS, the backward's
+normwise and max-normalised errors.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import transformer_head_self_amd as mha
+from oracle import allowed_set, attn_core_grad_ref, attn_core_ref
+from test_gpu_parity import BWD_TOL, DEV, _bwd_run, _grad_err, _rel_err, _say
+from transformer_head_self_amd.inputs import make_heads
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw(seed, n):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dt = ("f16", "bf16")[i % 2]
+        d_h = int(rng.choice([32, 64, 128]))
+        d_vh = int(rng.choice([32, 64, 96, 128]))
+        if i % 3 == 0:
+            d_h = d_vh = 64
+        B, h = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        n_q, n_k = int(rng.integers(1, 500)), int(rng.integers(1, 500))
+        if i % 2 == 0:
+            n_q = (n_q // 4 + 1) * 4        # whole 4-row chunks (direct-load backward)
+        causal = bool(rng.integers(0, 2))
+        if causal:
+            n_k = n_q
+        kl = tuple(int(v) for v in rng.integers(1, n_k + 1, size=B)) if rng.integers(0, 2) else None
+        flag = bool(rng.integers(0, 2))
+        cases.append((dt, B, h, n_q, n_k, d_h, d_vh, causal, kl, flag))
+    return cases
+
+
+FWD_CASES = _draw(1234, 16)
+BWD_CASES = _draw(4321, 12)
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_random_forward_core(case):
+    dt, B, h, n_q, n_k, d_h, d_vh, causal, kl, stats = case
+    _say(f"[random forward] {case}")
+    Qh, Kh, Vh = make_heads(B, h, n_q, n_k, d_h, d_vh, "f32" if dt == "f16" else dt,
+                            seed=500 + n_q + n_k)
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    dev = [torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(tdt) for a in (Qh, Kh, Vh)]
+    host = [t.float().cpu().numpy().astype(np.float64) for t in dev]
+    c = 1.0 / math.sqrt(d_h)
+    key_len = None if kl is None else np.array(kl, dtype=np.int32)
+    rm = torch.empty((B, h, n_q), device=DEV) if stats else None
+    rl = torch.empty((B, h, n_q), device=DEV) if stats else None
+    Z = mha.attn_core(*dev, scale=c, causal=causal,
+                      key_len=None if key_len is None else torch.from_numpy(key_len).to(DEV),
+                      out_dtype=torch.float32, row_m=rm, row_l=rl)
+    torch.cuda.synchronize()
+    ref = attn_core_ref(*host, c, allowed_set(B, n_q, n_k, causal=causal, key_len=key_len))
+    err = _rel_err(Z.cpu().numpy(), ref["Z"])
+    _say(f"  Z err {err:.3e}")
+    # fp16: two 2^-11 roundings (query scale, weights); bf16: the weights' 2^-9
+    assert err <= (1e-2 if dt == "f16" else 2e-2)
+    if stats:
+        np.testing.assert_allclose(rm.cpu().numpy(), ref["m"], rtol=1e-3, atol=1e-3)
+        np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-2)
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_random_backward_core(case):
+    dt, B, h, n_q, n_k, d_h, d_vh, causal, kl, z_in_heads_type = case
+    zdt = dt if z_in_heads_type else "f32"
+    _say(f"[random backward] {case} z={zdt}")
+    Qh, Kh, Vh = make_heads(B, h, n_q, n_k, d_h, d_vh, "f32", seed=700 + n_q + n_k)
+    dZ = np.random.default_rng(701 + n_k).standard_normal((B, n_q, h * d_vh)).astype(np.float32)
+    c = 1.0 / math.sqrt(d_h)
+    key_len = None if kl is None else np.array(kl, dtype=np.int32)
+    grads, host, dZh = _bwd_run(dt, zdt, Qh, Kh, Vh, dZ, c, causal, key_len)
+    ref = attn_core_grad_ref(*host, c, allowed_set(B, n_q, n_k, causal=causal, key_len=key_len),
+                             dZh)
+    scale = float(np.abs(ref["dVh"]).max())
+    for name, got in zip(("dQh", "dKh", "dVh"), grads):
+        r = np.asarray(ref[name], np.float64)
+        if float(np.abs(r).max()) <= 1e-9 * scale:
+            # every row has a single allowed key: its weights do not depend on
+            # Q or K, so dQ = dK = 0 up to the rounding of dA - D
+            assert float(np.abs(np.asarray(got, np.float64)).max()) <= 1e-3 * scale, name
+            continue
+        fro, mx = _grad_err(got, r)
+        _say(f"  {name} normwise {fro:.3e} max {mx:.3e}")
+        assert fro <= BWD_TOL[dt][0] and mx <= BWD_TOL[dt][1], name

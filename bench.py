@@ -53,6 +53,21 @@ HBM_PEAK_GBS = 8000.0
 EXP_PEAK_T_PER_S = 256 * 4 * 8 * 2.4e9 / 1e12
 
 
+def core_kernel_name(w):
+    """The attention kernel the library's launcher picks for this workload's
+    forward (fp16 heads for bf16 inputs, no row statistics requested)."""
+    if w.dtype != "bf16":
+        return "attn_fwd_kernel (attention core)"
+    dh = next(d for d in (32, 64, 128) if w.d_h <= d)
+    dv = next(d for d in (32, 64, 96, 128) if w.d_vh <= d)
+    fast = dh == w.d_h and dv == w.d_vh
+    if fast and dh in (64, 128) and dv in (64, 128) and 128 in (dh, dv):
+        return "attn_pipe_kernel, eight waves (attention core)"
+    if fast and (dv >= 96 or dh >= 128):
+        return "attn_pipe_kernel (attention core)"
+    return "attn_fwd_kernel (attention core)"
+
+
 def gpu_sclk_mhz():
     """Current shader clock from the driver's DPM table (sysfs), or None."""
     import glob
@@ -424,7 +439,7 @@ def main():
         "attn_core": {"ms": round(ms_core, 5), "tflops": round(core_tflops, 3),
                       "frac_of_peak": round(core_tflops / peak, 4),
                       "gflop": round(core_flops / 1e9, 3)},
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel (attention core)",
+        "roofline": {"bound": "mfma", "kernel": core_kernel_name(w),
                      "achieved": round(core_tflops, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(core_tflops / peak, 4), "traffic": traffic},
         # the softmax's second ceiling: one exponential per allowed score

@@ -160,6 +160,8 @@ CORE_CASES = [
     ("bf16", 1, 4, 65, 65, 32, 32, True, (10, 65), True),
     ("f32", 2, 2, 50, 70, 16, 16, False, None, True),
     ("bf16", 3, 2, 1, 129, 64, 64, False, (1, 129), False),
+    ("bf16", 2, 3, 257, 257, 64, 128, True, (1, 257), False),
+    ("bf16", 1, 2, 300, 400, 128, 64, False, (100, 400), False),
 ]
 
 
@@ -473,13 +475,15 @@ def test_attn_core_f16_late_score_jumps(row_stats, d):
         np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-2)
 
 
-@pytest.mark.parametrize("dims", [(128, 128), (64, 96), (64, 64)])
+@pytest.mark.parametrize("dims", [(128, 128), (64, 128), (128, 64), (64, 96), (64, 64)])
 @pytest.mark.parametrize("causal", [True, False])
-def test_attn_core_f16_ragged_blocks(dims, causal):
-    """fp16 heads, no row statistics, key and query counts that are not
-    multiples of the 64-key block or the 128-row tile, key padding with
-    lengths down to 1: the last K/V block reads past n_k (clamped rows,
-    masked) and some rows see a single allowed key."""
+@pytest.mark.parametrize("row_stats", [False, True])
+def test_attn_core_f16_ragged_blocks(dims, causal, row_stats):
+    """fp16 heads, with and without row statistics, key and query counts that
+    are not multiples of the 64-key block or of the 128- and 256-row tiles
+    (four- and eight-wave workgroups), key padding with lengths down to 1:
+    the last K/V block reads past n_k (clamped rows, masked) and some rows
+    see a single allowed key."""
     d_h, d_vh = dims
     B, h, n = 3, 2, 301
     Qh, Kh, Vh = make_heads(B, h, n, n, d_h, d_vh, "f32", seed=23)
@@ -488,14 +492,24 @@ def test_attn_core_f16_ragged_blocks(dims, causal):
     Qh16, Kh16, Vh16 = (t.float().cpu().numpy() for t in (to16(Qh), to16(Kh), to16(Vh)))
     c = 1.0 / math.sqrt(d_h)
     allow = allowed_set(B, n, n, causal=causal, key_len=key_len)
-    ref = attn_core_ref(Qh16, Kh16, Vh16, c, allow)["Z"]
-    _say(f"[ragged blocks] d_h={d_h} d_vh={d_vh} causal={causal}")
+    full = attn_core_ref(Qh16, Kh16, Vh16, c, allow)
+    ref = full["Z"]
+    rm = rl = None
+    if row_stats:
+        rm = torch.empty((B, h, n), dtype=torch.float32, device=DEV)
+        rl = torch.empty_like(rm)
+    _say(f"[ragged blocks] d_h={d_h} d_vh={d_vh} causal={causal} row_stats={row_stats}")
     Z = mha.attn_core(to16(Qh), to16(Kh), to16(Vh), scale=c, causal=causal,
-                      key_len=torch.from_numpy(key_len).to(DEV))
+                      key_len=torch.from_numpy(key_len).to(DEV), row_m=rm, row_l=rl)
     torch.cuda.synchronize()
     err = _rel_err(Z.cpu().numpy(), ref)
     _say(f"  Z err {err:.3e}")
     assert err <= 1e-2
+    if row_stats:
+        # m from the scaled query rounded to fp16 once (2^-11 relative);
+        # l sums fp16-rounded weights
+        np.testing.assert_allclose(rm.cpu().numpy(), full["m"], rtol=2e-3, atol=2e-3)
+        np.testing.assert_allclose(rl.cpu().numpy(), full["l"], rtol=1e-2)
     # batch item 2 allows key 0 only: every row is exactly v_0 (weight 1)
     Zc = Z.float().cpu().numpy()
     for r in range(h):

@@ -501,8 +501,12 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       };
       raw_scores(shifted);
       // value fragments of this block, read ahead of the weights
-      vec vpre[DMA ? NKB : 1][2][DMA ? C::NDV : 1];
-      if constexpr (DMA) {
+      // (not in eight-wave workgroups with value rows of 96+ and heads of 128
+      // or the exact-shift merge: there the fragments do not fit the
+      // registers of two waves per SIMD)
+      constexpr bool VPRE = DMA && !(WAVES >= 8 && C::NDV > 2 && (DH >= 128 || !LAZY));
+      vec vpre[VPRE ? NKB : 1][2][VPRE ? C::NDV : 1];
+      if constexpr (VPRE) {
         #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           #pragma unroll
@@ -689,8 +693,14 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
           for (int st = 0; st < 2; ++st)
             #pragma unroll
             for (int d = 0; d < C::NDV; ++d) {
-              if constexpr (DMA) {
+              if constexpr (VPRE) {
                 mfma_chunk(o[d], vpre[kb][st][d], pb[kb][st]);
+              } else if constexpr (DMA) {
+                const unsigned v0 = vaddr[d] + (kb * 32 + 16 * st) * C::VRB;
+                const vec4 lo = lds_read_tr4_at<T>(v0);
+                const vec4 hi = lds_read_tr4_at<T>(v0 + 8 * C::VRB);
+                mfma_chunk(o[d], vec{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]},
+                           pb[kb][st]);
               } else {
                 const T* v0 = &vs[(kb * 32 + 16 * st + srow) * C::VROW + d * 32 + scol];
                 const vec4 lo = lds_read_tr4<T>(v0);

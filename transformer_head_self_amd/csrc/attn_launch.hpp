@@ -46,12 +46,42 @@ hipError_t launch_attn_fixed(AttnParams p, hipStream_t stream) {
   // Without requested row statistics the 2-byte deferred-shift variant
   // skips the running maximum (block-sum trigger).
   const bool stats = p.row_m != nullptr || p.row_l != nullptr;
+  // Eight waves per workgroup (256 query rows) for 2-byte heads of 64 or 128
+  // with at least one of the two widths 128: there a four-wave workgroup
+  // runs one wave per SIMD (its direct-load stages, 72-128 KB, or its
+  // registers leave room for no second one), and two waves per SIMD now
+  // share each K/V tile (each 1 KB load window owned by one wave).
+  // Measured in one process (causal; d = 128 at B = 1 with 16k tokens, the
+  // mixed widths at B = 2 with 8k): d = 128 fp16 heads 1172 -> 968 us
+  // without row statistics and 1358 -> 987 us with them, bf16 heads
+  // 1575 -> 1093 us; d_h = 64 with d_vh = 128 524 -> 401 us, d_h = 128
+  // with d_vh = 64 503 -> 403 us (fp16, no statistics); the other
+  // mixed-width cases within 2 % either way.
+  constexpr bool wide8 = sizeof(T) == 2 && (DH == 64 || DH == 128) &&
+                         (DV == 64 || DV == 128) && (DH == 128 || DV == 128);
+  if constexpr (wide8) {
+    if (fast) {
+      typedef AttnCfg<T, DH, DV, 8, 64> C8;
+      p.num_q_tiles = (p.n_q + C8::QT - 1) / C8::QT;
+      const long long g8 = (long long)p.num_q_tiles * p.B * p.h;
+      if constexpr (lazy) {
+        if (!stats) {
+          hipLaunchKernelGGL((attn_pipe_kernel<T, DH, DV, 4, 1, 8>), dim3((unsigned)g8),
+                             dim3(C8::NT), 0, stream, p);
+          return hipGetLastError();
+        }
+      }
+      hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, 8, 64, true, lazy, 1>), dim3((unsigned)g8),
+                         dim3(C8::NT), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
   if constexpr (lazy && sizeof(T) == 2) {
     if (fast && !stats) {
-      // The software-pipelined kernel (two waves per SIMD) wins where a block
-      // carries more matrix work per weight: value rows of 96+ or heads of
-      // 128 (measured 30 % and 10 % faster); for narrower heads three
-      // unpipelined waves per SIMD are faster (measured 7 %).
+      // The software-pipelined kernel wins where a block carries more matrix
+      // work per weight (value rows of 96: measured 30 % faster, two
+      // workgroups per CU); for narrower heads three unpipelined waves per
+      // SIMD are faster (measured 7 %).
       if constexpr (MHA_ATTN_PIPE && (DV >= 96 || DH >= 128)) {
         static_assert(WAVES == 4 && BN == 64, "the pipelined kernel's tile");
         hipLaunchKernelGGL((attn_pipe_kernel<T, DH, DV, MHA_PIPE_NS, MHA_PIPE_OCC>),

@@ -33,12 +33,16 @@ namespace mha {
 
 // NS: K/V stages in LDS (3 or 4); a block is loaded NS - 2 blocks ahead of
 // its scores.  OCC: waves per SIMD the register allocation must allow.
-template <typename T, int DH, int DV, int NS = 4, int OCC = 2>
-__global__ __launch_bounds__(256, OCC) void attn_pipe_kernel(AttnParams p) {
+// WAVES: waves per workgroup (4 or 8), 32 query rows each.
+template <typename T, int DH, int DV, int NS = 4, int OCC = 2, int WAVES = 4>
+__global__ __launch_bounds__(64 * WAVES, OCC) void attn_pipe_kernel(AttnParams p) {
   static_assert(sizeof(T) == 2, "2-byte heads");
   static_assert(NS == 3 || NS == 4, "three or four stages");
-  constexpr int WAVES = 4, BN = 64;
+  static_assert(WAVES == 4 || WAVES == 8, "four or eight waves");
+  constexpr int BN = 64;
   typedef AttnCfg<T, DH, DV, WAVES, BN> C;
+  static_assert(C::KTILE == C::K_WIN * WAVES * 1024 && C::VTILE == C::V_WIN * WAVES * 1024,
+                "every wave owns whole 1 KB load windows of both tiles");
   constexpr int NKB = C::NKB;   // 2 sub-blocks of 32 keys
   typedef typename Elem<T>::vec vec;
   typedef typename Elem<T>::vec4 vec4;

@@ -207,6 +207,56 @@ def test_attn_core_bool_mask_broadcast():
     assert _rel_err(Z.cpu().numpy(), ref) <= 1e-4
 
 
+BOOL_FAST_CASES = [
+    # dtype, B, h, n_q, n_k, d_h, d_vh, causal, key_len, batch-shared G
+    ("f16", 2, 2, 300, 300, 64, 64, True, None, False),
+    ("bf16", 2, 3, 200, 520, 64, 128, False, (520, 100), True),
+    ("f16", 1, 2, 257, 400, 128, 128, False, None, False),
+    ("bf16", 2, 2, 130, 256, 32, 96, False, (256, 3), False),
+]
+
+
+@pytest.mark.parametrize("case", BOOL_FAST_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_bool_mask_direct_load_path(case):
+    """Boolean masks on 2-byte heads of exact widths with n_k a multiple of 4
+    (the direct-load kernel reading four mask bytes per load), with row
+    statistics.  Even rows forbid their first 128 keys wherever a later key
+    is available, so their first two key blocks are empty and the running
+    summary starts from the empty state in a later block."""
+    dt, B, h, n_q, n_k, d_h, d_vh, causal, kl, shared = case
+    _say(f"[bool direct-load] {case}")
+    Qh, Kh, Vh = make_heads(B, h, n_q, n_k, d_h, d_vh, "f32" if dt == "f16" else dt,
+                            seed=60 + n_q)
+    dev, host = _heads_dev(Qh, Kh, Vh, dt)
+    rng = np.random.default_rng(61 + n_k)
+    Bm = 1 if shared else B
+    G = rng.random((Bm, n_q, n_k)) < 0.3
+    key_len = None if kl is None else np.array(kl[:B], dtype=np.int32)
+    for bm in range(Bm):
+        L = n_k if (key_len is None or shared) else int(key_len[bm])
+        if shared and key_len is not None:
+            L = int(key_len.min())
+        for i in range(n_q):
+            last = min(i if causal else n_k - 1, L - 1)
+            if i % 2 == 0 and last >= 128:
+                G[bm, i, :128] = False
+            G[bm, i, last] = True          # every row keeps an allowed key
+    allow = allowed_set(B, n_q, n_k, causal=causal, key_len=key_len, allowed=G)
+    c = 1.0 / math.sqrt(d_h)
+    ref = attn_core_ref(*host, c, allow)
+    rm = torch.empty((B, h, n_q), device=DEV)
+    rl = torch.empty_like(rm)
+    kl_dev = None if key_len is None else torch.from_numpy(key_len).to(DEV)
+    Z = mha.attn_core(*dev, scale=c, causal=causal, key_len=kl_dev,
+                      allowed=torch.from_numpy(G).to(DEV), row_m=rm, row_l=rl)
+    torch.cuda.synchronize()
+    err = _rel_err(Z.cpu().numpy(), ref["Z"])
+    _say(f"  Z err {err:.3e}")
+    assert err <= SPLIT_TOL[dt]
+    np.testing.assert_allclose(rm.cpu().numpy(), ref["m"], rtol=0, atol=1e-4)
+    np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=4e-3)
+
+
 # ---------------------------------------------------------------------------
 # closed forms and exact properties
 # ---------------------------------------------------------------------------

@@ -125,6 +125,8 @@ void fill_mask(mha::AttnParams& p, const mha_mask* m) {
     p.add = m->add;
     p.add_batch_stride = m->add_batch_stride;
   }
+  p.mask_vec = p.n_k % 4 == 0 && aligned(p.allowed, 4) && p.allowed_batch_stride % 4 == 0 &&
+               aligned(p.add, 16) && p.add_batch_stride % 4 == 0;
 }
 
 struct Workspace {

@@ -125,8 +125,9 @@ __device__ __forceinline__ int v_swizzle(int row) {
 }
 
 // FAST: every row of Q, K, V is exactly DH / DV wide with 16-byte aligned
-// rows, and there is no boolean mask; the host selects it when that holds.
-// The general variant predicates every column and reads the boolean mask.
+// rows, and there is no boolean mask or additive bias (MASKED: there may be,
+// with aligned mask rows, p.mask_vec); the host selects it when that holds.
+// The general variant predicates every column and reads the masks.
 //
 // LAZY (deferred shift): the running state of a row is kept as (m, l*, z*)
 // with l* = l e^(m - mu), z* = z e^(m - mu) for a reference shift mu <= m
@@ -154,11 +155,15 @@ static_assert(kLazyLimit == (float)(1 << (int)kLazyTau), "limit = 2^tau");
 // (p.part_m / part_l / part_z) instead of Z.  Uses the exact-shift merge: a
 // partition may hold no allowed key for some rows (empty state).
 template <typename T, int DH, int DV, int WAVES, int BN_, bool FAST, bool LAZY = false, int OCC = 1,
-          bool STATS = true, bool SPLIT = false>
+          bool STATS = true, bool SPLIT = false, bool MASKED = false>
 __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p) {
   typedef AttnCfg<T, DH, DV, WAVES, BN_> C;
   static_assert(!(SPLIT && LAZY), "a key partition may hold no allowed key for a row");
   static_assert(STATS || (LAZY && C::TR), "the block-sum trigger is for 2-byte elements");
+  static_assert(!(MASKED && (LAZY || !FAST)), "masked fast variant: exact-shift merge");
+  // GEN: boolean / additive masks are read (the general variant, or the
+  // fast variant with masks whose rows hold aligned groups of four keys)
+  constexpr bool GEN = !FAST || MASKED;
   constexpr int NKB = C::NKB;
   typedef typename Elem<T>::vec vec;
   typedef typename Elem<T>::vec4 vec4;
@@ -216,9 +221,9 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   const T* Kb = reinterpret_cast<const T*>(p.K) + (size_t)bh * p.n_k * p.ldk;
   const T* Vb = reinterpret_cast<const T*>(p.V) + (size_t)bh * p.n_k * p.ldv;
   const uint8_t* Gb =
-      (!FAST && p.allowed) ? p.allowed + (size_t)b * p.allowed_batch_stride : nullptr;
+      (GEN && p.allowed) ? p.allowed + (size_t)b * p.allowed_batch_stride : nullptr;
   // additive score bias M (general path only): added to the scaled score
-  const float* Ab = (!FAST && p.add) ? p.add + (size_t)b * p.add_batch_stride : nullptr;
+  const float* Ab = (GEN && p.add) ? p.add + (size_t)b * p.add_batch_stride : nullptr;
   const bool vq = FAST || p.vec_q, vk = FAST || p.vec_k, vv = FAST || p.vec_v;
   const int dh = FAST ? DH : p.d_h;
   const int dvh = FAST ? DV : p.d_vh;
@@ -472,6 +477,31 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
     // empty key set here: its summary is the empty state, a no-op merge.
     const bool active = (qw < p.n_q) && !(p.causal && k0 > qw + 31);
     if (active) {
+      // General path with aligned mask rows: this block's boolean / additive
+      // mask entries for this lane's keys, four consecutive keys per load
+      // (the keys k0 + 32 kb + 8 a + 4 g + j, j < 4, of score slots
+      // (kb, 4 a + j)), issued before the score products so that their
+      // latency runs under them.  Rows past n_q read nothing (forbidden,
+      // zero bias); groups lie wholly inside or past n_k (n_k % 4 == 0).
+      uint32_t gmv[GEN ? NKB : 1][4];
+      floatx4 amv[GEN ? NKB : 1][4];
+      const bool mvec = GEN && p.mask_vec;
+      if constexpr (GEN) {
+        if (mvec) {
+          #pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            #pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const int key = k0 + kb * 32 + 8 * a + 4 * g;
+              const bool in = qi < p.n_q && key < p.n_k;
+              const size_t at = (size_t)qi * p.n_k + key;
+              gmv[kb][a] = 0xffffffffu;
+              amv[kb][a] = floatx4{0.f, 0.f, 0.f, 0.f};
+              if (Gb != nullptr) gmv[kb][a] = in ? *reinterpret_cast<const uint32_t*>(Gb + at) : 0u;
+              if (Ab != nullptr && in) amv[kb][a] = *reinterpret_cast<const floatx4*>(Ab + at);
+            }
+        }
+      }
       // ---- raw products S^T (NKB sub-blocks of 32 keys) ----------------------
       floatx16 s[NKB];
       // LAZY: from the second block on every row has a finite mu (the first
@@ -525,19 +555,36 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       // off = 32 kb + 8 (i / 4) + i % 4.  Causal and key padding allow exactly
       // the keys j <= lim = min(qi, kvalid - 1): one compare per score.
       const bool need_mask = (k0 + BN > kvalid) || (p.causal && k0 + BN - 1 > qw) ||
-                             (!FAST && (Gb != nullptr || Ab != nullptr));
+                             (GEN && (Gb != nullptr || Ab != nullptr));
       auto apply_mask = [&]() {
         const int lim = p.causal ? min(qi, kvalid - 1) : kvalid - 1;
         const int t = lim - k0 - 4 * g;
+        if constexpr (GEN) {
+          if (mvec) {
+            #pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+              #pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int a = i >> 2, j = i & 3;
+                const int off = kb * 32 + 8 * a + j;
+                const bool ok = off <= t && ((gmv[kb][a] >> (8 * j)) & 0xffu) != 0u;
+                if (Ab != nullptr)
+                  s[kb][i] = ok ? fmaf(s[kb][i], cs0, amv[kb][a][j] * kLog2e) : -INFINITY;
+                else
+                  s[kb][i] = ok ? s[kb][i] : -INFINITY;
+              }
+            return;
+          }
+        }
         #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int off = kb * 32 + 8 * (i >> 2) + (i & 3);
             bool ok = off <= t;
-            if (!FAST && Gb != nullptr && ok)
+            if (GEN && Gb != nullptr && ok)
               ok = qi < p.n_q && Gb[(size_t)qi * p.n_k + k0 + off + 4 * g] != 0;
-            if (!FAST && Ab != nullptr) {
+            if (GEN && Ab != nullptr) {
               // an allowed key has index <= lim < n_k, and qi < n_q is checked
               const float mb =
                   (ok && qi < p.n_q) ? Ab[(size_t)qi * p.n_k + k0 + off + 4 * g] : 0.f;

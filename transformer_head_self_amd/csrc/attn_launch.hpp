@@ -46,6 +46,20 @@ hipError_t launch_attn_fixed(AttnParams p, hipStream_t stream) {
   // Without requested row statistics the 2-byte deferred-shift variant
   // skips the running maximum (block-sum trigger).
   const bool stats = p.row_m != nullptr || p.row_l != nullptr;
+  // Boolean masks and additive biases on exact-width 2-byte heads with
+  // aligned mask rows: the direct-load kernel with the exact-shift merge
+  // (a row's first key block may hold no allowed key, which the deferred
+  // shift's start assumes).
+  if constexpr (sizeof(T) == 2) {
+    const bool fast_masked = p.d_h == DH && p.d_vh == DV && p.vec_q && p.vec_k && p.vec_v &&
+                             (p.allowed != nullptr || p.add != nullptr) && p.mask_vec;
+    if (fast_masked) {
+      constexpr int occm = (DH <= 64 && DV <= 64) ? 2 : 1;
+      hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, false, occm, true, false, true>),
+                         dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
   // Eight waves per workgroup (256 query rows) for 2-byte heads of 64 or 128
   // with at least one of the two widths 128: there a four-wave workgroup
   // runs one wave per SIMD (its direct-load stages, 72-128 KB, or its

@@ -92,6 +92,10 @@ struct AttnParams {
   long long allowed_batch_stride;
   const float* add;         // optional additive score bias [Ba, n_q, n_k] (natural-log units)
   long long add_batch_stride;
+  // allowed / add rows hold whole aligned groups of four keys (n_k and the
+  // batch strides multiples of 4, allowed 4-byte and add 16-byte aligned):
+  // the mask step reads four keys per load
+  int mask_vec;
   int B, h, n_q, n_k, d_h, d_vh;
   int ldq, ldk, ldv, ldz;
   float scale_log2;  // c * log2(e)

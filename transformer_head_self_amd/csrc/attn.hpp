@@ -32,6 +32,8 @@
 // convex combination of the values the product used.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 #include "lds_dma.hpp"
@@ -554,25 +556,33 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       // Score slot (kb, i) of this lane is key k0 + off(kb, i) + 4 g with
       // off = 32 kb + 8 (i / 4) + i % 4.  Causal and key padding allow exactly
       // the keys j <= lim = min(qi, kvalid - 1): one compare per score.
-      const bool need_mask = (k0 + BN > kvalid) || (p.causal && k0 + BN - 1 > qw) ||
-                             (GEN && (Gb != nullptr || Ab != nullptr));
+      // causal / padding thresholds bite only on boundary blocks
+      const bool need_cp = (k0 + BN > kvalid) || (p.causal && k0 + BN - 1 > qw);
+      const bool need_mask = need_cp || (GEN && (Gb != nullptr || Ab != nullptr));
       auto apply_mask = [&]() {
         const int lim = p.causal ? min(qi, kvalid - 1) : kvalid - 1;
         const int t = lim - k0 - 4 * g;
         if constexpr (GEN) {
           if (mvec) {
-            #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+            auto grouped = [&](auto cp) {
+              constexpr bool CP = decltype(cp)::value;   // threshold compare needed
               #pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                const int a = i >> 2, j = i & 3;
-                const int off = kb * 32 + 8 * a + j;
-                const bool ok = off <= t && ((gmv[kb][a] >> (8 * j)) & 0xffu) != 0u;
-                if (Ab != nullptr)
-                  s[kb][i] = ok ? fmaf(s[kb][i], cs0, amv[kb][a][j] * kLog2e) : -INFINITY;
-                else
-                  s[kb][i] = ok ? s[kb][i] : -INFINITY;
-              }
+              for (int kb = 0; kb < NKB; ++kb)
+                #pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                  const int a = i >> 2, j = i & 3;
+                  const int off = kb * 32 + 8 * a + j;
+                  const bool ok = (!CP || off <= t) && ((gmv[kb][a] >> (8 * j)) & 0xffu) != 0u;
+                  if (Ab != nullptr)
+                    s[kb][i] = ok ? fmaf(s[kb][i], cs0, amv[kb][a][j] * kLog2e) : -INFINITY;
+                  else
+                    s[kb][i] = ok ? s[kb][i] : -INFINITY;
+                }
+            };
+            if (need_cp)
+              grouped(std::true_type());
+            else
+              grouped(std::false_type());
             return;
           }
         }
@@ -669,9 +679,10 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
         m_run = m_new;
         if (__any(alpha != 1.0f)) rescale(alpha);   // some row's maximum moved
-        if (need_mask) {
-          // a forbidden score is -inf; with c = 0 the product -inf * 0 would
-          // be NaN, so its weight is set to 0 explicitly
+        if (need_mask && !(cs > 0.f)) {
+          // a forbidden score is -inf, whose weight 2^(-inf) is 0; with c = 0
+          // the product -inf * 0 would be NaN, so there the weight is set to
+          // 0 explicitly
           #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
             #pragma unroll

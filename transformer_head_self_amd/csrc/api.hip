@@ -127,6 +127,8 @@ void fill_mask(mha::AttnParams& p, const mha_mask* m) {
   }
   p.mask_vec = p.n_k % 4 == 0 && aligned(p.allowed, 4) && p.allowed_batch_stride % 4 == 0 &&
                aligned(p.add, 16) && p.add_batch_stride % 4 == 0;
+  p.mask_g16 = p.mask_vec && p.n_k % 16 == 0 && aligned(p.allowed, 16) &&
+               p.allowed_batch_stride % 16 == 0 && (int64_t)p.n_q * p.n_k < (int64_t(1) << 31);
 }
 
 struct Workspace {

@@ -157,7 +157,7 @@ static_assert(kLazyLimit == (float)(1 << (int)kLazyTau), "limit = 2^tau");
 // (p.part_m / part_l / part_z) instead of Z.  Uses the exact-shift merge: a
 // partition may hold no allowed key for some rows (empty state).
 template <typename T, int DH, int DV, int WAVES, int BN_, bool FAST, bool LAZY = false, int OCC = 1,
-          bool STATS = true, bool SPLIT = false, bool MASKED = false>
+          bool STATS = true, bool SPLIT = false, int MASKED = 0>
 __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p) {
   typedef AttnCfg<T, DH, DV, WAVES, BN_> C;
   static_assert(!(SPLIT && LAZY), "a key partition may hold no allowed key for a row");
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   static_assert(!(MASKED && (LAZY || !FAST)), "masked fast variant: exact-shift merge");
   // GEN: boolean / additive masks are read (the general variant, or the
   // fast variant with masks whose rows hold aligned groups of four keys)
-  constexpr bool GEN = !FAST || MASKED;
+  constexpr bool GEN = !FAST || MASKED != 0;
   constexpr int NKB = C::NKB;
   typedef typename Elem<T>::vec vec;
   typedef typename Elem<T>::vec4 vec4;
@@ -175,7 +175,14 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   // DMA: K/V tiles move from global memory straight into LDS (three stages in
   // flight); otherwise they are staged through registers (two buffers).
   constexpr bool DMA = C::TR && FAST && BN_ == 64;
-  constexpr int LDS_BYTES = DMA ? C::DMA_LDS : C::REG_LDS;
+  // MASKED == 2: the boolean mask's tile (QT rows x 64 key bytes) is loaded
+  // straight into LDS with each block's K/V tiles, after the stages
+  constexpr bool MLDS = MASKED == 2;
+  static_assert(!MLDS || DMA, "the mask tile travels with the direct loads");
+  constexpr int MT = MLDS ? C::QT * BN : 0;
+  constexpr int M_WIN = MT / 1024 / WAVES;
+  static_assert(M_WIN * 1024 * WAVES == MT, "whole 1 KB mask windows per wave");
+  constexpr int LDS_BYTES = DMA ? C::DMA_LDS + C::NS * MT : C::REG_LDS;
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   T* Ks = reinterpret_cast<T*>(smem);
   T* Vs = Ks + 2 * C::KBUF;
@@ -381,11 +388,34 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       voff[q] = tile_row(win, C::VRB) * C::VRB + v_chunk_of(win) * 16;
     }
   }
+  // Mask tile windows: window w holds tile rows 16 w .. 16 w + 15, 64 bytes
+  // each; lane i fills row 16 w + i / 4, slot i % 4, from the row's 16-byte
+  // chunk (i % 4) ^ ((row / 4) % 4) (so the reads below, 32 rows at one
+  // chunk, spread over the banks).  Rows past n_q read row n_q - 1 and
+  // chunks past n_k the last chunk (n_k % 16 == 0): both are never used
+  // (rows not stored; keys >= n_k fail the key-count threshold).
+  unsigned mrow[MLDS ? M_WIN : 1], mchk[MLDS ? M_WIN : 1];
+  if constexpr (MLDS) {
+    #pragma unroll
+    for (int q = 0; q < M_WIN; ++q) {
+      const int t = (wave * M_WIN + q) * 1024 + 16 * lane;
+      const int row = t / 64, slot = (t % 64) / 16;
+      mrow[q] = (unsigned)min(q0 + row, p.n_q - 1) * (unsigned)p.n_k;
+      mchk[q] = (unsigned)((slot ^ ((row >> 2) & 3)) * 16);
+    }
+  }
   // block blk into stage blk % 3; in the last block, rows past n_k read the
   // last key (masked out, weight 0)
   auto issue_kv = [&](int blk) {
     const int k0 = blk * BN;
     const unsigned st = lds_base + (unsigned)((blk % C::NS) * C::STAGE);
+    if constexpr (MLDS) {
+      const unsigned mst = lds_base + (unsigned)(C::DMA_LDS + (blk % C::NS) * MT);
+      #pragma unroll
+      for (int q = 0; q < M_WIN; ++q)
+        lds_dma16(Gb, mrow[q] + min((unsigned)k0 + mchk[q], (unsigned)(p.n_k - 16)),
+                  mst + (wave * M_WIN + q) * 1024);
+    }
     const char* kg = reinterpret_cast<const char*>(Kb) + (size_t)k0 * C::KRB;
     const char* vg = reinterpret_cast<const char*>(Vb) + (size_t)k0 * C::VRB;
     if (k0 + BN <= p.n_k) {
@@ -446,7 +476,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
     if constexpr (DMA) {
       // block blk has landed once only block blk+1's loads are outstanding;
       // after the barrier no wave reads block blk-1, whose stage is refilled
-      if (blk + 1 < nblk) wait_vm_lds<C::K_WIN + C::V_WIN>();
+      if (blk + 1 < nblk) wait_vm_lds<C::K_WIN + C::V_WIN + M_WIN>();
       else wait_vm_lds<0>();
       __builtin_amdgcn_s_barrier();
       compiler_fence();
@@ -487,8 +517,23 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       // zero bias); groups lie wholly inside or past n_k (n_k % 4 == 0).
       uint32_t gmv[GEN ? NKB : 1][4];
       floatx4 amv[GEN ? NKB : 1][4];
-      const bool mvec = GEN && p.mask_vec;
-      if constexpr (GEN) {
+      const bool mvec = GEN && (MLDS || p.mask_vec);
+      if constexpr (MLDS) {
+        // this lane's row of the block's mask tile: dword (kb, a) holds keys
+        // k0 + 32 kb + 8 a + 4 g .. + 3, in chunk 2 kb + a / 2 of the row
+        const int mr = wave * 32 + l32, sw = (mr >> 2) & 3;
+        unsigned mb = lds_base + (unsigned)(C::DMA_LDS + (blk % C::NS) * MT);
+        asm("" : "+s"(mb));
+        #pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          #pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int c = 2 * kb + (a >> 1);
+            gmv[kb][a] = lds_load_at<uint32_t>(mb + (unsigned)(mr * 64 + ((c ^ sw) * 16) +
+                                                               8 * (a & 1) + 4 * g));
+            amv[kb][a] = floatx4{0.f, 0.f, 0.f, 0.f};
+          }
+      } else if constexpr (GEN) {
         if (mvec) {
           #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)

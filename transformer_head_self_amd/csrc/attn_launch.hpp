@@ -55,8 +55,14 @@ hipError_t launch_attn_fixed(AttnParams p, hipStream_t stream) {
                              (p.allowed != nullptr || p.add != nullptr) && p.mask_vec;
     if (fast_masked) {
       constexpr int occm = (DH <= 64 && DV <= 64) ? 2 : 1;
-      hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, false, occm, true, false, true>),
-                         dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
+      // a boolean mask alone with 16-byte aligned rows travels into LDS with
+      // the K/V tiles; otherwise each lane loads its mask entries
+      if (p.allowed != nullptr && p.add == nullptr && p.mask_g16)
+        hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, false, occm, true, false, 2>),
+                           dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
+      else
+        hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, false, occm, true, false, 1>),
+                           dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
       return hipGetLastError();
     }
   }

@@ -96,6 +96,10 @@ struct AttnParams {
   // batch strides multiples of 4, allowed 4-byte and add 16-byte aligned):
   // the mask step reads four keys per load
   int mask_vec;
+  // boolean rows also 16-byte aligned (n_k and the batch stride multiples
+  // of 16) and n_q * n_k below 2^31: the direct-load kernel can move the
+  // mask tile into LDS with the K/V tiles
+  int mask_g16;
   int B, h, n_q, n_k, d_h, d_vh;
   int ldq, ldk, ldv, ldz;
   float scale_log2;  // c * log2(e)

@@ -103,6 +103,10 @@ def parse():
                          "(one query row per item and head against 32768 cached keys)")
     ap.add_argument("--backward", action="store_true",
                     help="time the attention-core backward pass on the headline shape instead")
+    ap.add_argument("--mask", choices=["bool", "additive"], default=None,
+                    help="time the attention core on the headline shape with the causal rule "
+                         "also given as a boolean mask [B, T, T] or an additive bias (0 / -inf) "
+                         "instead, next to the causal flag alone")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters (optional)")
     return ap.parse_args()
@@ -200,6 +204,51 @@ def decode_bench(args, torch):
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": nbytes},
         "unsplit_ms": round(ms_plain, 5),
         "unsplit_gbs": round(nbytes / (ms_plain * 1e-3) / 1e9, 1),
+    }), flush=True)
+
+
+def mask_bench(args, torch):
+    """Attention core at the headline shape (fp16 heads): causal flag alone,
+    then the causal flag with the same rule as a boolean mask or an additive
+    bias, which sends every key block through the mask step."""
+    import transformer_head_self_amd as mha
+    from transformer_head_self_amd.inputs import HEADLINE, WORKLOADS
+    w = WORKLOADS[HEADLINE]
+    B, h, T, d = w.B, w.h, w.n_q, w.d_h
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    Qh, Kh, Vh = (torch.randn(B, h, T, d, generator=gen).to(dev).half() for _ in range(3))
+    Z = torch.empty((B, T, h * d), dtype=torch.float16, device=dev)
+    tri = torch.tril(torch.ones(T, T, dtype=torch.bool, device=dev))
+    G = tri.expand(B, T, T).contiguous() if args.mask == "bool" else None
+    A = (torch.zeros(B, T, T, device=dev).masked_fill(~tri, float("-inf"))
+         if args.mask == "additive" else None)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_flag = timed(lambda: mha.attn_core(Qh, Kh, Vh, scale=w.scale, causal=True,
+                                          out_dtype=torch.float16, Z=Z, stream=stream))
+    ms_mask = timed(lambda: mha.attn_core(Qh, Kh, Vh, scale=w.scale, causal=True, allowed=G,
+                                          add=A, out_dtype=torch.float16, Z=Z, stream=stream))
+    flops = 2.0 * B * h * T * T * (2 * d) * 0.5
+    print(json.dumps({
+        "metric": f"attention core with a {args.mask} mask, causal rule, TFLOP/s",
+        "value": round(flops / (ms_mask * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+        "ms_masked": round(ms_mask, 5), "ms_causal_flag_only": round(ms_flag, 5),
+        "steps": args.steps, "warmup": args.warmup, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"{HEADLINE} heads, attn_core, {args.mask} mask [B, T, T]",
+                   "B": B, "h": h, "n_q": T, "n_k": T, "d_h": d, "d_vh": d},
     }), flush=True)
 
 
@@ -328,6 +377,9 @@ def main():
         return
     if args.backward:
         backward_bench(args, torch)
+        return
+    if args.mask:
+        mask_bench(args, torch)
         return
 
     import transformer_head_self_amd as mha

@@ -159,7 +159,9 @@ def _mask(B, n_q, n_k, causal, key_len, allowed, device, add=None):
         m.flags |= MHA_MASK_KEY_PADDING
         m.key_len = kl.data_ptr()
     if allowed is not None:
-        G = torch.as_tensor(allowed, device=device).to(torch.uint8).contiguous()
+        G = torch.as_tensor(allowed, device=device)
+        # a bool tensor is one byte per entry (0 / 1): reinterpreted, not copied
+        G = (G.view(torch.uint8) if G.dtype == torch.bool else G.to(torch.uint8)).contiguous()
         if G.dim() != 3 or G.shape[1:] != (n_q, n_k) or G.shape[0] not in (1, B):
             raise ValueError("allowed must have shape [B or 1, n_q, n_k]")
         keep.append(G)

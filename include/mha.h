@@ -95,6 +95,14 @@ typedef struct mha_mask {
   const float* add;             /* [Ba][n_q][n_k] fp32 (ADDITIVE), device, 4-byte aligned   */
   int64_t add_batch_stride;     /* elements between items; 0 = one bias for the batch       */
 } mha_mask;
+/* Speed (not correctness) of the BOOL and ADDITIVE rules depends on layout:
+ * with n_k and the batch strides multiples of 4 (and `add` 16-byte
+ * aligned) the attention forward reads four keys' entries per load; a BOOL
+ * mask alone with n_k and its batch stride multiples of 16, `allowed`
+ * 16-byte aligned and n_q * n_k below 2^31 is moved into on-chip memory
+ * with the key/value tiles (fastest).  Other layouts are read entry by
+ * entry.  The causal and key-padding rules cost almost nothing: prefer them
+ * to an equivalent BOOL mask. */
 
 /* Projection biases (review page "Multi-Head Attention", "Parameter and
  * Work Conventions" and "Audit Order": the bias convention is stated, not

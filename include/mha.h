@@ -30,7 +30,8 @@
  *   magnitude (projected values of order one are far inside that range).
  * - The library allocates nothing, keeps no state between calls, never
  *   synchronises, and enqueues its kernels on `stream` (a hipStream_t; NULL
- *   means the null stream).  The caller owns every buffer.
+ *   means the null stream).  The caller owns every buffer; the one exception
+ *   is the static scratch array of attn_core_split_noalloc (see there).
  * - Every argument that the host can check is checked before anything is
  *   launched; on error nothing is launched and nothing is written.
  * - Pointers must be aligned to their element size; 16-byte alignment and
@@ -63,7 +64,9 @@ typedef enum {
   MHA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the *_workspace_bytes() */
   MHA_ERR_UNSUPPORTED = -7, /* d_h or d_vh above the largest instantiated head width */
   MHA_ERR_LAUNCH = -8,      /* the HIP runtime reported an error at launch           */
-  MHA_ERR_SCALE = -9        /* scale is not a finite number                          */
+  MHA_ERR_SCALE = -9,       /* scale is not a finite number                          */
+  MHA_ERR_SCRATCH = -10     /* attn_core_split_noalloc: the request exceeds the
+                               library's static scratch (MHA_STATIC_SCRATCH_BYTES)    */
 } mha_status;
 
 typedef enum { MHA_F32 = 0, MHA_BF16 = 1, MHA_F16 = 2 } mha_dtype;
@@ -197,6 +200,24 @@ mha_status attn_core_split(const mha_dims* d, const mha_mask* m,
                            const void* Qh, const void* Kh, const void* Vh, void* Z,
                            float* row_m, float* row_l, int32_t splits,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* attn_core_split without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The partitions' summaries go to a
+ * scratch array the library holds in each GPU's memory for the life of the
+ * process (MHA_STATIC_SCRATCH_BYTES, 16 MiB); this call allocates nothing.
+ * Same arguments, masks, layouts and results as attn_core_split (same
+ * kernels, so bit for bit the same outputs), without workspace.  Errors as
+ * there, plus MHA_ERR_SCRATCH when attn_split_workspace_bytes(d, splits)
+ * exceeds MHA_STATIC_SCRATCH_BYTES (nothing is launched).  Every call on one
+ * GPU shares that GPU's scratch: calls that overlap in time on one GPU (two
+ * streams, or two host threads) race and may return wrong results; calls
+ * ordered on one stream are safe.  Nothing in the scratch needs clearing:
+ * each call writes every summary it reads. */
+#define MHA_STATIC_SCRATCH_BYTES (16u << 20)
+mha_status attn_core_split_noalloc(const mha_dims* d, const mha_mask* m,
+                                   const void* Qh, const void* Kh, const void* Vh, void* Z,
+                                   float* row_m, float* row_l, int32_t splits, void* stream);
 
 /* Backward pass of attn_core: gradients of a scalar loss with respect to
  * Qh, Kh and Vh, given dZ, its gradient with respect to Z.  The pages define

@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
 * ``attn_core_split``  the same with the key axis cut into partitions whose
   summaries are merged afterwards (few query rows, many keys).
 * ``attn_split_workspace_bytes``.
+* ``attn_core_split_noalloc``  the key-split form with the library's static
+  scratch instead of a workspace (for callers that cannot allocate).
 * ``attn_core_backward``  gradients of the attention core from the forward's
   row statistics; ``attn_backward_workspace_bytes``.
 * ``mha_backward``  gradients of the whole layer (inputs, weights, biases)
@@ -29,7 +31,7 @@ import os
 __all__ = [
     "MhaError", "MhaDims", "MhaMask", "MhaBias", "MhaBiasGrad", "lib", "mha_backward",
     "mha_backward_workspace_bytes", "mha_forward", "attn_core", "attn_core_split",
-    "attn_split_workspace_bytes", "attn_core_backward", "attn_backward_workspace_bytes",
+    "attn_split_workspace_bytes", "attn_core_split_noalloc", "attn_core_backward", "attn_backward_workspace_bytes",
     "mha_workspace_bytes", "mha_status_string", "MHA_F32", "MHA_BF16", "MHA_F16",
     "MHA_MASK_CAUSAL", "MHA_MASK_KEY_PADDING", "MHA_MASK_BOOL", "MHA_MASK_ADDITIVE",
 ]
@@ -37,6 +39,8 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmha.so")
 
 MHA_F32, MHA_BF16, MHA_F16 = 0, 1, 2
+MHA_ERR_SCRATCH = -10
+MHA_STATIC_SCRATCH_BYTES = 16 << 20   # the static scratch of attn_core_split_noalloc
 MHA_MASK_CAUSAL, MHA_MASK_KEY_PADDING, MHA_MASK_BOOL, MHA_MASK_ADDITIVE = 1, 2, 4, 8
 
 
@@ -94,6 +98,9 @@ def lib():
         L.attn_core_split.argtypes = [P(MhaDims), P(MhaMask), vp, vp, vp, vp, vp, vp,
                                       ctypes.c_int32, vp, ctypes.c_size_t, vp]
         L.attn_core_split.restype = ctypes.c_int
+        L.attn_core_split_noalloc.argtypes = [P(MhaDims), P(MhaMask), vp, vp, vp, vp, vp, vp,
+                                              ctypes.c_int32, vp]
+        L.attn_core_split_noalloc.restype = ctypes.c_int
         L.attn_backward_workspace_bytes.argtypes = [P(MhaDims)]
         L.attn_backward_workspace_bytes.restype = ctypes.c_size_t
         L.attn_core_backward.argtypes = [P(MhaDims), P(MhaMask)] + [vp] * 11 + [ctypes.c_size_t,
@@ -296,6 +303,29 @@ def attn_core_split(Qh, Kh, Vh, *, splits=0, scale=None, causal=False, key_len=N
     del keep
     if st != 0:
         raise MhaError(st, "attn_core_split")
+    return Z
+
+
+def attn_core_split_noalloc(Qh, Kh, Vh, *, splits=0, scale=None, causal=False, key_len=None,
+                            allowed=None, add=None, out_dtype=None, Z=None, row_m=None,
+                            row_l=None, stream=None):
+    """attn_core_split with the partitions' summaries in the library's static
+    scratch (MHA_STATIC_SCRATCH_BYTES per GPU) instead of a workspace: the C
+    call allocates nothing.  Calls that overlap in time on one GPU share that
+    scratch and race; calls ordered on one stream are safe."""
+    torch = _torch()
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    dims = _core_dims(Qh, Kh, Vh, scale, out_dtype)
+    B, h, n_q, n_k, d_vh = dims.B, dims.h, dims.n_q, dims.n_k, dims.d_vh
+    m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Qh.device, add)
+    if Z is None:
+        Z = torch.empty((B, n_q, h * d_vh), dtype=out_dtype, device=Qh.device)
+    st = lib().attn_core_split_noalloc(ctypes.byref(dims), ctypes.byref(m), _ptr(Qh), _ptr(Kh),
+                                       _ptr(Vh), _ptr(Z), _ptr(row_m), _ptr(row_l), int(splits),
+                                       _stream(stream))
+    del keep
+    if st != 0:
+        raise MhaError(st, "attn_core_split_noalloc")
     return Z
 
 

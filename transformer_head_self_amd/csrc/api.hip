@@ -9,6 +9,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <stdint.h>
 #include <string.h>
 
@@ -268,6 +270,87 @@ BwdWorkspace carve_bwd(const mha_dims* d) {
   return w;
 }
 
+// Library-owned scratch for attn_core_split_noalloc: the partitions'
+// summaries of the key-split form, for callers that cannot allocate.  Every
+// GPU the library runs on holds its own copy until the process ends.  In host
+// code this name is only a stand-in for the array: the device address comes
+// from hipGetSymbolAddress, once per device with that device current, and
+// only that address is ever passed to a kernel.
+static __device__ __align__(256) char scratch[MHA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<char*> g_scratch_addr[kMaxScratchDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream), looked up on the first call for that device.
+mha_status device_scratch(hipStream_t stream, char** out) {
+  int cur = -1, dev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return MHA_ERR_LAUNCH;
+  dev = cur;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return MHA_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxScratchDevices) return MHA_ERR_LAUNCH;
+  char* a = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (a == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    a = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (a == nullptr) {
+      if (dev != cur && hipSetDevice(dev) != hipSuccess) return MHA_ERR_LAUNCH;
+      void* sym = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch));
+      if (dev != cur && hipSetDevice(cur) != hipSuccess) return MHA_ERR_LAUNCH;
+      if (e != hipSuccess || sym == nullptr) return MHA_ERR_LAUNCH;
+      a = static_cast<char*>(sym);
+      g_scratch_addr[dev].store(a, std::memory_order_release);
+    }
+  }
+  *out = a;
+  return MHA_OK;
+}
+
+// Shared body of attn_core_split and attn_core_split_noalloc: checks, then
+// the partition and merge launches with the summaries at `ws`.  `ws` is
+// NULL for the no-allocation form, which takes the static scratch instead.
+mha_status split_forward(const mha_dims* d, const mha_mask* m, const void* Qh, const void* Kh,
+                         const void* Vh, void* Z, float* row_m, float* row_l, int32_t splits,
+                         void* workspace, size_t workspace_bytes, bool use_scratch,
+                         void* stream) {
+  mha_status s = check_core_dims(d);
+  if (s != MHA_OK) return s;
+  if ((s = check_mask(d, m)) != MHA_OK) return s;
+  if (splits < 0) return MHA_ERR_DIM;
+  if (!Qh || !Kh || !Vh || !Z) return MHA_ERR_NULL;
+  const size_t ei = esize(d->in_dtype), eo = esize(d->out_dtype);
+  if (!aligned(Qh, ei) || !aligned(Kh, ei) || !aligned(Vh, ei) || !aligned(Z, eo) ||
+      !aligned(row_m, 4) || !aligned(row_l, 4))
+    return MHA_ERR_ALIGN;
+  const SplitPlan sp = split_plan(d, splits);
+  if (!split_plan_fits(d, sp)) return MHA_ERR_DIM;
+  char* ws = nullptr;
+  if (use_scratch) {
+    if (sp.total > (size_t)MHA_STATIC_SCRATCH_BYTES) return MHA_ERR_SCRATCH;
+    if ((s = device_scratch((hipStream_t)stream, &ws)) != MHA_OK) return s;
+  } else {
+    if (!workspace || workspace_bytes < sp.total) return MHA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MHA_ERR_ALIGN;
+    ws = static_cast<char*>(workspace);
+  }
+  mha::AttnParams p;
+  memset(&p, 0, sizeof(p));
+  attn_params(p, d, d->in_dtype, Qh, Kh, Vh, Z, d->out_dtype, row_m, row_l);
+  fill_mask(p, m);
+  // every (partition, row) summary is written before the merge reads it, so
+  // nothing in the scratch needs clearing between calls
+  p.splits = sp.splits;
+  p.split_keys = sp.split_keys;
+  p.part_m = reinterpret_cast<float*>(ws + sp.m);
+  p.part_l = reinterpret_cast<float*>(ws + sp.l);
+  p.part_z = reinterpret_cast<float*>(ws + sp.z);
+  if (mha::launch_attention_split(p, d->in_dtype, (hipStream_t)stream) != hipSuccess)
+    return MHA_ERR_LAUNCH;
+  return MHA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -291,6 +374,9 @@ const char* mha_status_string(int s) {
     case MHA_ERR_UNSUPPORTED: return "MHA_ERR_UNSUPPORTED: head width above the instantiated maximum";
     case MHA_ERR_LAUNCH: return "MHA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
     case MHA_ERR_SCALE: return "MHA_ERR_SCALE: the score scale is not finite";
+    case MHA_ERR_SCRATCH:
+      return "MHA_ERR_SCRATCH: the partitions' summaries need more than the library's static "
+             "scratch (MHA_STATIC_SCRATCH_BYTES); use fewer splits or attn_core_split";
     default: return "unknown mha_status";
   }
 }
@@ -324,32 +410,14 @@ size_t attn_split_workspace_bytes(const mha_dims* d, int32_t splits) {
 mha_status attn_core_split(const mha_dims* d, const mha_mask* m, const void* Qh, const void* Kh,
                            const void* Vh, void* Z, float* row_m, float* row_l, int32_t splits,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  mha_status s = check_core_dims(d);
-  if (s != MHA_OK) return s;
-  if ((s = check_mask(d, m)) != MHA_OK) return s;
-  if (splits < 0) return MHA_ERR_DIM;
-  if (!Qh || !Kh || !Vh || !Z) return MHA_ERR_NULL;
-  const size_t ei = esize(d->in_dtype), eo = esize(d->out_dtype);
-  if (!aligned(Qh, ei) || !aligned(Kh, ei) || !aligned(Vh, ei) || !aligned(Z, eo) ||
-      !aligned(row_m, 4) || !aligned(row_l, 4))
-    return MHA_ERR_ALIGN;
-  const SplitPlan sp = split_plan(d, splits);
-  if (!split_plan_fits(d, sp)) return MHA_ERR_DIM;
-  if (!workspace || workspace_bytes < sp.total) return MHA_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return MHA_ERR_ALIGN;
-  mha::AttnParams p;
-  memset(&p, 0, sizeof(p));
-  attn_params(p, d, d->in_dtype, Qh, Kh, Vh, Z, d->out_dtype, row_m, row_l);
-  fill_mask(p, m);
-  char* ws = static_cast<char*>(workspace);
-  p.splits = sp.splits;
-  p.split_keys = sp.split_keys;
-  p.part_m = reinterpret_cast<float*>(ws + sp.m);
-  p.part_l = reinterpret_cast<float*>(ws + sp.l);
-  p.part_z = reinterpret_cast<float*>(ws + sp.z);
-  if (mha::launch_attention_split(p, d->in_dtype, (hipStream_t)stream) != hipSuccess)
-    return MHA_ERR_LAUNCH;
-  return MHA_OK;
+  return split_forward(d, m, Qh, Kh, Vh, Z, row_m, row_l, splits, workspace, workspace_bytes,
+                       false, stream);
+}
+
+mha_status attn_core_split_noalloc(const mha_dims* d, const mha_mask* m, const void* Qh,
+                                   const void* Kh, const void* Vh, void* Z, float* row_m,
+                                   float* row_l, int32_t splits, void* stream) {
+  return split_forward(d, m, Qh, Kh, Vh, Z, row_m, row_l, splits, nullptr, 0, true, stream);
 }
 
 size_t attn_backward_workspace_bytes(const mha_dims* d) {

@@ -192,6 +192,26 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _launch_stream(stream):
+    """The torch stream the kernels will run on (torch's current stream by
+    default)."""
+    torch = _torch()
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _used_on(stream, tensors):
+    """Mark tensors allocated here (outputs, workspace, converted masks) as
+    used by the launches on ``stream``: torch's caching allocator then keeps
+    their memory out of reuse until that stream's work has finished, also
+    when ``stream`` is not the stream they were allocated on."""
+    torch = _torch()
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None and t.is_cuda:
+            t.record_stream(stream)
+
+
 def default_work_dtype(in_dtype):
     """Intermediate element type used when the caller does not choose one."""
     torch = _torch()
@@ -241,6 +261,7 @@ def mha_forward(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, *, scale=None, causal
                            _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_O), ctypes.byref(bias),
                            _ptr(Y), _ptr(row_m),
                            _ptr(row_l), _ptr(workspace), workspace.numel(), _stream(stream))
+    _used_on(stream, keep + [Y, workspace])
     del keep
     if st != 0:
         raise MhaError(st, "mha_forward")
@@ -271,6 +292,7 @@ def attn_core(Qh, Kh, Vh, *, scale=None, causal=False, key_len=None, allowed=Non
         Z = torch.empty((B, n_q, h * d_vh), dtype=out_dtype, device=Qh.device)
     st = lib().attn_core(ctypes.byref(dims), ctypes.byref(m), _ptr(Qh), _ptr(Kh), _ptr(Vh),
                          _ptr(Z), _ptr(row_m), _ptr(row_l), _stream(stream))
+    _used_on(stream, keep + [Z])
     del keep
     if st != 0:
         raise MhaError(st, "attn_core")
@@ -300,6 +322,7 @@ def attn_core_split(Qh, Kh, Vh, *, splits=0, scale=None, causal=False, key_len=N
     st = lib().attn_core_split(ctypes.byref(dims), ctypes.byref(m), _ptr(Qh), _ptr(Kh),
                                _ptr(Vh), _ptr(Z), _ptr(row_m), _ptr(row_l), int(splits),
                                _ptr(workspace), workspace.numel(), _stream(stream))
+    _used_on(stream, keep + [Z, workspace])
     del keep
     if st != 0:
         raise MhaError(st, "attn_core_split")
@@ -323,6 +346,7 @@ def attn_core_split_noalloc(Qh, Kh, Vh, *, splits=0, scale=None, causal=False, k
     st = lib().attn_core_split_noalloc(ctypes.byref(dims), ctypes.byref(m), _ptr(Qh), _ptr(Kh),
                                        _ptr(Vh), _ptr(Z), _ptr(row_m), _ptr(row_l), int(splits),
                                        _stream(stream))
+    _used_on(stream, keep + [Z])
     del keep
     if st != 0:
         raise MhaError(st, "attn_core_split_noalloc")
@@ -359,6 +383,7 @@ def attn_core_backward(Qh, Kh, Vh, Z, dZ, row_m, row_l, *, scale=None, causal=Fa
                                   _ptr(Vh), _ptr(Z), _ptr(dZ), _ptr(row_m), _ptr(row_l),
                                   _ptr(dQh), _ptr(dKh), _ptr(dVh), _ptr(workspace),
                                   workspace.numel(), _stream(stream))
+    _used_on(stream, keep + [dQh, dKh, dVh, workspace])
     del keep
     if st != 0:
         raise MhaError(st, "attn_core_backward")
@@ -412,6 +437,7 @@ def mha_backward(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, dY, row_m, row_l, fw
                             _ptr(out["dW_K"]), _ptr(out["dW_V"]), _ptr(out["dW_O"]),
                             ctypes.byref(db), _ptr(workspace), workspace.numel(),
                             _stream(stream))
+    _used_on(stream, keep + list(out.values()) + [workspace])
     del keep
     if st != 0:
         raise MhaError(st, "mha_backward")

@@ -576,6 +576,83 @@ def test_attn_core_f16_ragged_blocks(dims, causal, row_stats):
                                       np.broadcast_to(Vh16[2, r, 0], (n, d_vh)))
 
 
+@pytest.mark.parametrize("key_len", [(700, 517), (640, 64)])
+def test_pipelined_core_noncausal_with_jumps(key_len):
+    """fp16 heads of 64 without row statistics and without the causal rule
+    run the three-stage pipelined kernel.  Ragged sizes (300 query rows: two
+    full 128-row tiles and a tail; 700 keys: a partial last block), key
+    padding (a partial block walked first, or lengths that are whole
+    blocks), and score jumps placed so that every path of the deferred
+    shift runs: key 640 in the first block walked (exact maximum), key 130
+    and key 300 in the steady iterations (the second overflows a weight:
+    redo from the raw scores, with the next block's scores moved), key 600
+    in the last block walked (redo without a next block)."""
+    B, h, n_q, n_k, d = 2, 2, 300, 700, 64
+    Qh, Kh, Vh = make_heads(B, h, n_q, n_k, d, d, "f32", seed=81)
+    Qh[..., 0] = 4.0
+    Kh[..., 0] *= 0.1
+    for key, val in ((130, 40.0), (300, 300.0), (600, 60.0), (640, 45.0)):
+        Kh[:, :, key, 0] = val
+    to16 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(torch.float16)
+    Qh16, Kh16, Vh16 = (t.float().cpu().numpy() for t in (to16(Qh), to16(Kh), to16(Vh)))
+    kl = np.array(key_len, dtype=np.int32)
+    c = 1.0 / math.sqrt(d)
+    ref = attn_core_ref(Qh16, Kh16, Vh16, c, allowed_set(B, n_q, n_k, key_len=kl))["Z"]
+    _say(f"[pipelined non-causal] key_len={key_len}")
+    Z = mha.attn_core(to16(Qh), to16(Kh), to16(Vh), scale=c, key_len=torch.from_numpy(kl).to(DEV),
+                      out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Zc = Z.cpu().numpy()
+    assert np.isfinite(Zc).all()
+    err = _rel_err(Zc, ref)
+    _say(f"  Z err {err:.3e}")
+    assert err <= 1e-2
+    # a second call writes the same bits (deterministic)
+    Z2 = mha.attn_core(to16(Qh), to16(Kh), to16(Vh), scale=c, key_len=torch.from_numpy(kl).to(DEV),
+                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(Z2.cpu().numpy(), Zc)
+
+
+def test_calls_on_a_side_stream():
+    """The binding launches on the stream it is given; outputs, workspace and
+    converted masks it allocates are kept from reuse until that stream's
+    work is done.  mha_forward and attn_core on a non-current stream, with
+    masks the binding converts (a list of key lengths, a float64 additive
+    bias), then fresh allocations on the current stream, match the oracle."""
+    w = custom_workload(name="side-stream", dtype="bf16", B=2, n_q=200, n_k=200, d_q=128,
+                        d_k=128, d_v=128, h=2, d_h=64, d_vh=64, d_o=128, seed=83)
+    x = make_inputs(w)
+    key_len = [200, 77]
+    allow = allowed_set(w.B, w.n_q, w.n_k, key_len=np.array(key_len, np.int32))
+    side = torch.cuda.Stream()
+    Q = _to_dev(x["Q"], "bf16")
+    Ws = {k: _to_dev(x[k], "bf16") for k in ("W_Q", "W_K", "W_V", "W_O")}
+    torch.cuda.synchronize()
+    with torch.cuda.stream(torch.cuda.current_stream()):
+        Y = mha.mha_forward(Q, Q, Q, Ws["W_Q"], Ws["W_K"], Ws["W_V"], Ws["W_O"], w.h, w.d_h,
+                            w.d_vh, key_len=key_len, stream=side)
+        junk = [torch.full((1 << 20,), 7.0, device=DEV) for _ in range(8)]   # reuse pressure
+    side.synchronize()
+    ref = mha_ref(x["Q"], x["K"], x["V"], x["W_Q"], x["W_K"], x["W_V"], x["W_O"], w.h, w.d_h,
+                  w.d_vh, w.scale, allow)["Y"]
+    err = _rel_err(Y.cpu().numpy(), ref)
+    _say(f"[side stream] mha_forward Y err {err:.3e}")
+    assert err <= TOL["bf16"]
+    Qh, Kh, Vh = make_heads(2, 2, 150, 150, 64, 64, "f32", seed=84)
+    M = np.where(np.random.default_rng(85).random((1, 150, 150)) < 0.3, -np.inf, 0.0)
+    M[..., 0] = 0.0
+    Zs = mha.attn_core(_to_dev(Qh, "f32"), _to_dev(Kh, "f32"), _to_dev(Vh, "f32"), scale=0.125,
+                       add=torch.from_numpy(M).to(DEV), stream=side)
+    junk += [torch.full((1 << 20,), 7.0, device=DEV) for _ in range(8)]
+    side.synchronize()
+    refz = attn_core_ref(Qh, Kh, Vh, 0.125, allowed_set(2, 150, 150, allowed=np.isfinite(M)))["Z"]
+    errz = _rel_err(Zs.cpu().numpy(), refz)
+    _say(f"  attn_core Z err {errz:.3e}")
+    assert errz <= TOL["f32"]
+    del junk
+
+
 # ---------------------------------------------------------------------------
 # key-split form (partitions of the key axis merged afterwards)
 # ---------------------------------------------------------------------------

@@ -13,7 +13,12 @@ Printed JSON line (rank 0):
   events around its own launches on the stream it runs on, against the
   bf16 dense matrix-core peak;
 * cpu_baseline: the float64 CPU oracle on a bounded sample (one batch item)
-  of the same workload, in the same unit.
+  of the same workload, in the same unit; that leg also compares the timed
+  output's rows of that item with the oracle's (``parity``);
+* ms_median / ms_min: per-step times from events around every timed step;
+* settled: the same forward timed again after about 0.2 s of back-to-back
+  steps (the GPU clock rises over the first milliseconds of sustained load;
+  ``value`` keeps the requested warm-up and steps).
 """
 
 from __future__ import annotations
@@ -33,6 +38,7 @@ METRIC = "MHA fwd TFLOP/s and % bf16 MFMA peak (T=4096, h=16, d_k=64, causal)"
 # sources that define the attention kernel; a traffic measurement is only
 # reported while their hash matches the one recorded with it
 ATTN_SOURCES = ["transformer_head_self_amd/csrc/attn.hpp", "transformer_head_self_amd/csrc/attn_pipe.hpp",
+                "transformer_head_self_amd/csrc/attn_pipe3.hpp",
                 "transformer_head_self_amd/csrc/attn_launch.hpp", "transformer_head_self_amd/csrc/common.hpp",
                 "transformer_head_self_amd/csrc/internal.hpp", "transformer_head_self_amd/csrc/lds_dma.hpp"]
 
@@ -65,20 +71,9 @@ def core_kernel_name(w):
         return "attn_pipe_kernel, eight waves (attention core)"
     if fast and (dv >= 96 or dh >= 128):
         return "attn_pipe_kernel (attention core)"
+    if fast and dh == 64 and dv == 64 and not w.causal:
+        return "attn_fwd3_kernel (attention core)"
     return "attn_fwd_kernel (attention core)"
-
-
-def gpu_sclk_mhz():
-    """Current shader clock from the driver's DPM table (sysfs), or None."""
-    import glob
-    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-        try:
-            for line in open(path):
-                if line.rstrip().endswith("*"):
-                    return int(line.split(":")[1].strip().lower().split("mhz")[0])
-        except (OSError, ValueError, IndexError):
-            continue
-    return None
 
 
 def parse():
@@ -128,8 +123,9 @@ def workspace_views(ws, w, torch, work):
     return out
 
 
-def cpu_baseline(w, x):
-    """Time the float64 oracle on one batch item of the workload."""
+def cpu_baseline(w, x, Y_gpu):
+    """Time the float64 oracle on one batch item of the workload, and compare
+    the timed forward's output rows of that item with it."""
     import numpy as np
     from oracle import allowed_set, mha_ref
     try:
@@ -142,14 +138,35 @@ def cpu_baseline(w, x):
     Ws = {k: x[k].astype(np.float64) for k in ("W_Q", "W_K", "W_V", "W_O")}
     allow = allowed_set(1, w.n_q, w.n_k, causal=w.causal, key_len=kl)
     t0 = time.perf_counter()
-    mha_ref(sub["Q"], sub["K"], sub["V"], Ws["W_Q"], Ws["W_K"], Ws["W_V"], Ws["W_O"], w.h,
-            w.d_h, w.d_vh, w.scale, allow)
+    ref = mha_ref(sub["Q"], sub["K"], sub["V"], Ws["W_Q"], Ws["W_K"], Ws["W_V"], Ws["W_O"], w.h,
+                  w.d_h, w.d_vh, w.scale, allow)["Y"][0]
     dt = time.perf_counter() - t0
     flops = (w.core_flops_effective(kl) + w.proj_flops()) / w.B
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
+    y = np.asarray(Y_gpu[0], dtype=np.float64)
+    err = float(np.max(np.abs(y - ref)) / np.sqrt(np.mean(ref * ref)))
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s",
+            "cores": len(os.sched_getaffinity(0)), "blas_threads": int(blas_threads),
             "kind": "oracle", "seconds": dt,
             "sample": f"1 of {w.B} batch items of {w.name}: dense float64 oracle (full score "
                       f"matrix per head, no causal skipping), FLOPs counted as for the GPU"}
+    parity = {"metric": "max|Y - Y_oracle| / RMS(Y_oracle)", "value": err,
+              "bar": 1e-4 if w.dtype == "f32" else 2e-2,
+              "rows": f"all {w.n_q} query rows of batch item 0 of the timed output"}
+    return base, parity
+
+
+def timed_steps(fn, steps, stream, torch):
+    """Run fn `steps` times between events on `stream`: the total time of the
+    region and each step's time (ms)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return ev[0].elapsed_time(ev[-1]) / steps, per
 
 
 DECODE = dict(B=8, h=16, n_k=32768, d=64)
@@ -412,19 +429,11 @@ def main():
                         stream=stream)
 
     # ---- whole forward --------------------------------------------------------
-    ms_step = float("nan")
     steps_fwd = args.steps if args.only != "core" else 1
     for _ in range(args.warmup if args.only != "core" else 1):
         step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps_fwd):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / steps_fwd
+    ms_step, per_step = timed_steps(step, steps_fwd, stream, torch)
+    Y_timed = Y.float().cpu().numpy()
     if args.only == "forward":
         print(json.dumps({"ms_per_step": ms_step}), flush=True)
         return
@@ -440,15 +449,21 @@ def main():
 
     for _ in range(args.warmup):
         core()
-    torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(args.steps):
-        core()
-    c1.record(stream)
-    sclk = gpu_sclk_mhz()   # read while the timed launches run
-    torch.cuda.synchronize()
-    ms_core = c0.elapsed_time(c1) / args.steps
+    ms_core, per_core = timed_steps(core, args.steps, stream, torch)
+
+    # ---- the forward again after about 0.2 s of sustained load -------------------
+    settled = None
+    if args.only == "all":
+        t_end = time.perf_counter() + 0.2
+        n_settle = 0
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                step()
+            torch.cuda.synchronize()
+            n_settle += 20
+        ms_settled, per_settled = timed_steps(step, args.steps, stream, torch)
+        settled = {"settle_steps": n_settle, "ms_per_step": round(ms_settled, 5),
+                   "ms_median": round(per_settled[len(per_settled) // 2], 5)}
 
     core_flops = w.core_flops_effective(x["key_len"])
     total_flops = core_flops + w.proj_flops()
@@ -467,6 +482,9 @@ def main():
         except Exception:
             traffic = None
 
+    nominal = w.core_flops() + w.proj_flops()
+    if settled is not None:
+        settled["value"] = round(total_flops / (settled["ms_per_step"] * 1e-3) / 1e12, 3)
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -475,6 +493,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_median": round(per_step[len(per_step) // 2], 5),
+        "ms_min": round(per_step[0], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -487,10 +507,15 @@ def main():
                    "h": w.h, "d_h": w.d_h, "d_vh": w.d_vh, "d_o": w.d_o,
                    "mask": "causal" if w.causal else ("key_padding" if w.pad_range else "none"),
                    "parallelism": "single-gpu"},
+        # value counts the effective work (padded keys excluded); nominal counts
+        # every key of n_k (the two differ for key-padding workloads)
+        "flops_per_step": {"effective": total_flops, "nominal": nominal},
         "e2e_frac_of_peak": round(value / peak, 4),
-        "attn_core": {"ms": round(ms_core, 5), "tflops": round(core_tflops, 3),
+        "attn_core": {"ms": round(ms_core, 5), "ms_median": round(per_core[len(per_core) // 2], 5),
+                      "ms_min": round(per_core[0], 5), "tflops": round(core_tflops, 3),
                       "frac_of_peak": round(core_tflops / peak, 4),
-                      "gflop": round(core_flops / 1e9, 3)},
+                      "gflop": round(core_flops / 1e9, 3),
+                      "gflop_nominal": round(w.core_flops() / 1e9, 3)},
         "roofline": {"bound": "mfma", "kernel": core_kernel_name(w),
                      "achieved": round(core_tflops, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(core_tflops / peak, 4), "traffic": traffic},
@@ -500,10 +525,11 @@ def main():
                         "achieved": round(exps / (ms_core * 1e-3) / 1e12, 3),
                         "peak": round(EXP_PEAK_T_PER_S, 2), "unit": "T exp/s",
                         "frac": round(exps / (ms_core * 1e-3) / 1e12 / EXP_PEAK_T_PER_S, 4)},
-        "sclk_mhz": sclk,
     }
+    if settled is not None:
+        out["settled"] = settled
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, x)
+        out["cpu_baseline"], out["parity"] = cpu_baseline(w, x, Y_timed)
     print(json.dumps(out), flush=True)
 
 

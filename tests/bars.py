@@ -1,0 +1,21 @@
+"""Tolerance bars of the fp16-intermediate GPU tests, each set from the
+error that tests/rounding_model.py (a float64 model of exactly the roundings
+the fp16 path makes) shows on the same inputs.  tests/test_rounding_model.py
+recomputes every emulated error below on the CPU and checks that each bar
+is about twice it (between 1.5 and 3 times).  The smaller fp16 tests need no
+constant: they compute twice the model's error on their own inputs
+(rounding_model.core_bar).
+
+Metric: max |out - ref| / RMS(ref) against the float64 oracle.
+"""
+
+# mha_forward, bf16 inputs, fp16 intermediates, at B=4, T=4096,
+# d_model=1024, h=16, d_h=64, causal: the model's error on batch item 0.
+HEADLINE_MODEL_ERR_ITEM0 = 1.490e-2
+
+# attn_core on the headline's fp16 heads with fp16 Z (the benchmark's launch
+# configuration): the model's largest error over the four batch items, and
+# the bar.
+HEADLINE_CORE_MODEL_ERR = 1.364e-2
+F16_CORE_HEADLINE_BAR = 2.8e-2
+

@@ -2,15 +2,18 @@
 
 Metric: max |out - ref| / RMS(ref) over every element (padded query rows
 included).  Bars: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs with fp32
-accumulation.  Small problems are compared in full; the large workloads are
-compared on sampled query rows that the oracle computes one by one, in the
-same launch configuration the benchmark times.  Exact (==) checks cover the
+accumulation; fp16-intermediate bars come from tests/bars.py (each about
+twice the error of a float64 model of the fp16 roundings).  Every workload
+is compared in every output, except the 16384-token one, compared on whole
+256-row query tiles and every 64th row that the oracle computes row by row;
+the benchmark's workload and kernel are compared exactly as it runs them.  Exact (==) checks cover the
 properties that must hold bit for bit: forbidden keys do not influence the
 result, batch items do not mix, W_O = 0 gives 0, W_V leaves (m, l) alone,
 a row with one allowed key returns that key's value, runs are deterministic.
 """
 
 import math
+import os
 import sys
 
 import numpy as np
@@ -28,6 +31,10 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 DEV = "cuda:0"
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from bars import F16_CORE_HEADLINE_BAR, HEADLINE_MODEL_ERR_ITEM0  # noqa: E402
+from rounding_model import core_bar  # noqa: E402
 
 
 def _say(msg):
@@ -119,30 +126,68 @@ def test_workload_full_parity(name):
     np.testing.assert_allclose(rl, ref["l"], rtol=3e-2 if w.dtype == "bf16" else 1e-4)
 
 
-SAMPLE_ROWS = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, 255, 256, 1000, 2047, 2048, 4095]
-
-
-@pytest.mark.parametrize("name", [
-    "self-bf16-B4-T4096-dm1024-h16-dh64-causal",
-    "self-bf16-B1-T16384-dm2048-h16-dh128-causal",
-])
-def test_workload_sampled_parity(name):
-    w = WORKLOADS[name]
-    _say(f"[parity sampled] {name}")
+def test_headline_workload_every_output():
+    """B=4, T=4096, d_model=1024, h=16, d_h=64, causal, bf16 inputs (the
+    benchmark's workload, run exactly as the benchmark runs it): every element
+    of Y against the oracle, under the 2e-2 bar; and the same check tighter,
+    against the error a float64 model of the library's fp16 roundings makes
+    on batch item 0 (tests/rounding_model.py; 1.49e-2 there): the GPU may not
+    exceed it by more than a quarter."""
+    w = WORKLOADS["self-bf16-B4-T4096-dm1024-h16-dh64-causal"]
+    _say(f"[parity every output] {w.name}")
     x = make_inputs(w)
     Y = _run_forward(w, x)
-    rng = np.random.default_rng(99)
-    rows = sorted(set([r for r in SAMPLE_ROWS if r < w.n_q] + [w.n_q - 1] +
-                      list(rng.integers(0, w.n_q, 16))))
-    allow = _allow(w, x)
-    outs, refs = [], []
-    for b in sorted({0, w.B - 1}):
-        Yr, _, _, _ = mha_ref_rows(x["Q"], x["K"], x["V"], x["W_Q"], x["W_K"], x["W_V"],
-                                   x["W_O"], w.h, w.d_h, w.d_vh, w.scale, allow, b, rows)
-        outs.append(Y[b, rows])
-        refs.append(Yr)
-    err = _rel_err(np.concatenate(outs), np.concatenate(refs))
-    _say(f"  Y err on {len(rows)} rows x {len(outs)} items: {err:.3e}")
+    ref = mha_ref(x["Q"], x["K"], x["V"], x["W_Q"], x["W_K"], x["W_V"], x["W_O"], w.h, w.d_h,
+                  w.d_vh, w.scale, _allow(w, x))["Y"]
+    err = _rel_err(Y, ref)
+    err0 = _rel_err(Y[0], ref[0])
+    _say(f"  Y err over all {Y.size} outputs {err:.3e}; item 0 {err0:.3e}")
+    assert err <= TOL["bf16"]
+    assert err0 <= 1.25 * HEADLINE_MODEL_ERR_ITEM0
+
+
+def test_headline_core_every_output():
+    """The attention kernel alone in the benchmark's launch configuration
+    (fp16 heads taken from the forward's workspace, fp16 Z, no row
+    statistics): every element of Z against the oracle run on the same fp16
+    heads (their values converted exactly to float64)."""
+    w = WORKLOADS["self-bf16-B4-T4096-dm1024-h16-dh64-causal"]
+    _say(f"[core every output] {w.name}")
+    x = make_inputs(w)
+    dims = mha.MhaDims(B=w.B, h=w.h, n_q=w.n_q, n_k=w.n_k, d_q=w.d_q, d_k=w.d_k, d_v=w.d_v,
+                       d_h=w.d_h, d_vh=w.d_vh, d_o=w.d_o, scale=w.scale, in_dtype=1,
+                       out_dtype=0, work_dtype=2)
+    ws = torch.empty(mha.mha_workspace_bytes(dims), dtype=torch.uint8, device=DEV)
+    Q = _to_dev(x["Q"], "bf16")
+    Wd = {k: _to_dev(x[k], "bf16") for k in ("W_Q", "W_K", "W_V", "W_O")}
+    mha.mha_forward(Q, Q, Q, Wd["W_Q"], Wd["W_K"], Wd["W_V"], Wd["W_O"], w.h, w.d_h, w.d_vh,
+                    causal=True, workspace=ws)
+    n = w.B * w.h * w.n_q * w.d_h
+    heads = [ws[i * 2 * n:(i + 1) * 2 * n].view(torch.float16).view(w.B, w.h, w.n_q, w.d_h)
+             for i in range(3)]   # Qh, Kh, Vh: equal sizes, 256-byte multiples
+    Z = mha.attn_core(*heads, scale=w.scale, causal=True, out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    h64 = [t.float().cpu().numpy() for t in heads]
+    ref = attn_core_ref(*h64, w.scale, allowed_set(w.B, w.n_q, w.n_k, causal=True))["Z"]
+    err = _rel_err(Z.float().cpu().numpy(), ref)
+    _say(f"  Z err over all {Z.numel()} outputs {err:.3e} (bar {F16_CORE_HEADLINE_BAR})")
+    assert err <= F16_CORE_HEADLINE_BAR
+
+
+def test_long_sequence_workload_whole_tiles():
+    """B=1, T=16384, d_model=2048, h=16, d_h=128, causal: whole 256-row
+    query tiles (the first, one in the middle, the last) and every 64th row
+    besides, against the oracle computed row by row."""
+    w = WORKLOADS["self-bf16-B1-T16384-dm2048-h16-dh128-causal"]
+    _say(f"[parity tiles] {w.name}")
+    x = make_inputs(w)
+    Y = _run_forward(w, x)
+    rows = sorted(set(range(0, 256)) | set(range(8192, 8448)) |
+                  set(range(w.n_q - 256, w.n_q)) | set(range(0, w.n_q, 64)))
+    Yr, _, _, _ = mha_ref_rows(x["Q"], x["K"], x["V"], x["W_Q"], x["W_K"], x["W_V"], x["W_O"],
+                               w.h, w.d_h, w.d_vh, w.scale, _allow(w, x), 0, rows)
+    err = _rel_err(Y[0, rows], Yr)
+    _say(f"  Y err on {len(rows)} rows: {err:.3e}")
     assert err <= TOL[w.dtype]
 
 
@@ -256,8 +301,9 @@ def test_bool_mask_direct_load_path(case, row_stats):
     Zc = Z.cpu().numpy()
     assert np.isfinite(Zc).all()
     err = _rel_err(Zc, ref["Z"])
-    _say(f"  Z err {err:.3e}")
-    assert err <= SPLIT_TOL[dt]
+    bar = SPLIT_TOL[dt] if dt != "f16" else core_bar(*host, c, allow, ref["Z"])
+    _say(f"  Z err {err:.3e} (bar {bar:.2e})")
+    assert err <= bar
     if row_stats:
         np.testing.assert_allclose(rm.cpu().numpy(), ref["m"], rtol=0, atol=1e-4)
         np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=4e-3)
@@ -416,18 +462,21 @@ def test_bf16_intermediates_option():
 
 def test_attn_core_f16_heads():
     """fp16 heads: the fast path scales the query by c log2(e) and rounds it to
-    fp16 once, and rounds the weights to fp16: two 2^-11 roundings on N(0,1)
-    data; max over ~600k outputs stays below 1e-2 of the RMS."""
+    fp16 once, and rounds the weights to fp16.  The bar is twice the error
+    of a float64 model of those roundings on the same inputs
+    (tests/rounding_model.py)."""
     B, h, n = 2, 4, 300
     Qh, Kh, Vh = make_heads(B, h, n, n, 64, 64, "f32", seed=12)
     to16 = lambda a: torch.from_numpy(a).to(DEV).to(torch.float16)
     Qh16, Kh16, Vh16 = (t.float().cpu().numpy() for t in (to16(Qh), to16(Kh), to16(Vh)))
-    ref = attn_core_ref(Qh16, Kh16, Vh16, 0.125, allowed_set(B, n, n, causal=True))["Z"]
+    allow = allowed_set(B, n, n, causal=True)
+    ref = attn_core_ref(Qh16, Kh16, Vh16, 0.125, allow)["Z"]
     Z = mha.attn_core(to16(Qh), to16(Kh), to16(Vh), scale=0.125, causal=True)
     torch.cuda.synchronize()
     err = _rel_err(Z.cpu().numpy(), ref)
-    _say(f"  f16 heads: Z err {err:.3e}")
-    assert err <= 1e-2
+    bar = core_bar(Qh16, Kh16, Vh16, 0.125, allow, ref)
+    _say(f"  f16 heads: Z err {err:.3e} (bar {bar:.2e})")
+    assert err <= bar
 
 
 def test_negative_and_zero_scale_match_oracle():
@@ -511,7 +560,8 @@ def test_attn_core_f16_late_score_jumps(row_stats, d, as_mask):
     to16 = lambda a: torch.from_numpy(a).to(DEV).to(torch.float16)
     Qh16, Kh16, Vh16 = (t.float().cpu().numpy() for t in (to16(Qh), to16(Kh), to16(Vh)))
     c = 1.0 / math.sqrt(d)
-    ref = attn_core_ref(Qh16, Kh16, Vh16, c, allowed_set(B, n, n, causal=True))
+    allow = allowed_set(B, n, n, causal=True)
+    ref = attn_core_ref(Qh16, Kh16, Vh16, c, allow)
     rm = rl = None
     if row_stats:
         rm = torch.empty((B, h, n), dtype=torch.float32, device=DEV)
@@ -524,8 +574,9 @@ def test_attn_core_f16_late_score_jumps(row_stats, d, as_mask):
     Zc = Z.cpu().numpy()
     assert np.isfinite(Zc).all()
     err = _rel_err(Zc, ref["Z"])
-    _say(f"  Z err {err:.3e}")
-    assert err <= 1e-2
+    bar = core_bar(Qh16, Kh16, Vh16, c, allow, ref["Z"])
+    _say(f"  Z err {err:.3e} (bar {bar:.2e})")
+    assert err <= bar
     # rows past key 450 attend almost only to it: Z is close to v_450 there
     np.testing.assert_allclose(Zc[0, 451:, :d], np.broadcast_to(Vh16[0, 0, 450], (n - 451, d)),
                                atol=2e-3)
@@ -562,8 +613,9 @@ def test_attn_core_f16_ragged_blocks(dims, causal, row_stats):
                       key_len=torch.from_numpy(key_len).to(DEV), row_m=rm, row_l=rl)
     torch.cuda.synchronize()
     err = _rel_err(Z.cpu().numpy(), ref)
-    _say(f"  Z err {err:.3e}")
-    assert err <= 1e-2
+    bar = core_bar(Qh16, Kh16, Vh16, c, allow, ref)
+    _say(f"  Z err {err:.3e} (bar {bar:.2e})")
+    assert err <= bar
     if row_stats:
         # m from the scaled query rounded to fp16 once (2^-11 relative);
         # l sums fp16-rounded weights
@@ -576,6 +628,22 @@ def test_attn_core_f16_ragged_blocks(dims, causal, row_stats):
                                       np.broadcast_to(Vh16[2, r, 0], (n, d_vh)))
 
 
+PIPE_JUMPS = ((130, 18.0), (300, 30.0), (600, 20.0), (640, 18.0))
+
+
+def pipelined_case_inputs():
+    """Heads of the pipelined-kernel test: feature 0 of the queries is +4 on
+    even rows and -4 on odd rows, so the score jumps planted on four keys
+    reach only the even rows (about 9, 15, 10 and 9 nats above the rest)."""
+    B, h, n_q, n_k, d = 2, 2, 300, 700, 64
+    Qh, Kh, Vh = make_heads(B, h, n_q, n_k, d, d, "f32", seed=81)
+    Qh[..., 0] = 4.0 * np.where(np.arange(n_q) % 2 == 0, 1.0, -1.0)[None, None, :]
+    Kh[..., 0] *= 0.1
+    for key, val in PIPE_JUMPS:
+        Kh[:, :, key, 0] = val
+    return Qh, Kh, Vh
+
+
 @pytest.mark.parametrize("key_len", [(700, 517), (640, 64)])
 def test_pipelined_core_noncausal_with_jumps(key_len):
     """fp16 heads of 64 without row statistics and without the causal rule
@@ -583,30 +651,31 @@ def test_pipelined_core_noncausal_with_jumps(key_len):
     full 128-row tiles and a tail; 700 keys: a partial last block), key
     padding (a partial block walked first, or lengths that are whole
     blocks), and score jumps placed so that every path of the deferred
-    shift runs: key 640 in the first block walked (exact maximum), key 130
-    and key 300 in the steady iterations (the second overflows a weight:
-    redo from the raw scores, with the next block's scores moved), key 600
-    in the last block walked (redo without a next block)."""
-    B, h, n_q, n_k, d = 2, 2, 300, 700, 64
-    Qh, Kh, Vh = make_heads(B, h, n_q, n_k, d, d, "f32", seed=81)
-    Qh[..., 0] = 4.0
-    Kh[..., 0] *= 0.1
-    for key, val in ((130, 40.0), (300, 300.0), (600, 60.0), (640, 45.0)):
-        Kh[:, :, key, 0] = val
+    shift runs on the even rows: key 640 in the first block walked (its
+    exact maximum), keys 130 and 300 in the steady iterations (the second
+    overflows a weight: redo from the raw scores, with the next block's
+    scores moved), key 600 in the last block walked (redo with no next
+    block).  The odd rows see no jump."""
+    Qh, Kh, Vh = pipelined_case_inputs()
+    B, h, n_q, n_k, d = Qh.shape[0], Qh.shape[1], Qh.shape[2], Kh.shape[2], Qh.shape[3]
     to16 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(torch.float16)
     Qh16, Kh16, Vh16 = (t.float().cpu().numpy() for t in (to16(Qh), to16(Kh), to16(Vh)))
     kl = np.array(key_len, dtype=np.int32)
     c = 1.0 / math.sqrt(d)
-    ref = attn_core_ref(Qh16, Kh16, Vh16, c, allowed_set(B, n_q, n_k, key_len=kl))["Z"]
-    _say(f"[pipelined non-causal] key_len={key_len}")
+    allow = allowed_set(B, n_q, n_k, key_len=kl)
+    ref = attn_core_ref(Qh16, Kh16, Vh16, c, allow)["Z"]
+    bar = core_bar(Qh16, Kh16, Vh16, c, allow, ref)
+    _say(f"[pipelined non-causal] key_len={key_len} (bar {bar:.2e})")
     Z = mha.attn_core(to16(Qh), to16(Kh), to16(Vh), scale=c, key_len=torch.from_numpy(kl).to(DEV),
                       out_dtype=torch.float32)
     torch.cuda.synchronize()
     Zc = Z.cpu().numpy()
     assert np.isfinite(Zc).all()
     err = _rel_err(Zc, ref)
-    _say(f"  Z err {err:.3e}")
-    assert err <= 1e-2
+    err_odd = _rel_err(Zc[:, 1::2], ref[:, 1::2])
+    _say(f"  Z err {err:.3e} (rows without jumps {err_odd:.3e})")
+    assert err <= bar
+    assert err_odd <= bar
     # a second call writes the same bits (deterministic)
     Z2 = mha.attn_core(to16(Qh), to16(Kh), to16(Vh), scale=c, key_len=torch.from_numpy(kl).to(DEV),
                        out_dtype=torch.float32)
@@ -666,7 +735,7 @@ def _heads_dev(Qh, Kh, Vh, dt):
     return t, [Qh, Kh, Vh]
 
 
-SPLIT_TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 1e-2}
+SPLIT_TOL = {"f32": 1e-4, "bf16": 2e-2}   # fp16 heads: twice the rounding model's error
 
 SPLIT_CASES = [
     # dtype, B, h, n_q, n_k, d_h, d_vh, key_len, splits
@@ -691,7 +760,8 @@ def test_split_decode_matches_oracle(case):
     dev, host = _heads_dev(Qh, Kh, Vh, dt)
     key_len = None if kl is None else np.array(kl[:B], dtype=np.int32)
     c = 1.0 / math.sqrt(d_h)
-    ref = attn_core_ref(*host, c, allowed_set(B, n_q, n_k, key_len=key_len))
+    allow = allowed_set(B, n_q, n_k, key_len=key_len)
+    ref = attn_core_ref(*host, c, allow)
     rm = torch.empty((B, h, n_q), device=DEV)
     rl = torch.empty_like(rm)
     Z = mha.attn_core_split(*dev, splits=splits, scale=c,
@@ -699,8 +769,9 @@ def test_split_decode_matches_oracle(case):
                             row_m=rm, row_l=rl)
     torch.cuda.synchronize()
     err = _rel_err(Z.cpu().numpy(), ref["Z"])
-    _say(f"  Z err {err:.3e}")
-    assert err <= SPLIT_TOL[dt]
+    bar = core_bar(*host, c, allow, ref["Z"]) if dt == "f16" else SPLIT_TOL[dt]
+    _say(f"  Z err {err:.3e} (bar {bar:.2e})")
+    assert err <= bar
     np.testing.assert_allclose(rm.cpu().numpy(), ref["m"], rtol=0, atol=2e-3)
     np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-5 if dt == "f32" else 4e-3)
     if key_len is not None and 1 in kl[:B]:
@@ -815,15 +886,16 @@ def test_additive_bias_core_matches_oracle(case):
                       add=torch.from_numpy(M).to(DEV), row_m=rm, row_l=rl)
     torch.cuda.synchronize()
     err = _rel_err(Z.cpu().numpy(), ref["Z"])
-    _say(f"  Z err {err:.3e}")
-    assert err <= SPLIT_TOL[dt]
+    bar = core_bar(*host, c, allow, ref["Z"], add=M) if dt == "f16" else SPLIT_TOL[dt]
+    _say(f"  Z err {err:.3e} (bar {bar:.2e})")
+    assert err <= bar
     np.testing.assert_allclose(rm.cpu().numpy(), ref["m"], rtol=0, atol=1e-4)
     np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-5 if dt == "f32" else 4e-3)
     # the key-split form takes the same bias
     Zs = mha.attn_core_split(*dev, splits=3, scale=c, causal=causal, key_len=kl_dev,
                              add=torch.from_numpy(M).to(DEV))
     torch.cuda.synchronize()
-    assert _rel_err(Zs.cpu().numpy(), ref["Z"]) <= SPLIT_TOL[dt]
+    assert _rel_err(Zs.cpu().numpy(), ref["Z"]) <= bar
 
 
 def test_additive_bias_single_finite_entry_returns_that_value_exactly():
@@ -888,9 +960,9 @@ def test_forward_with_projection_biases(case):
                                       d_vh, 1.0 / math.sqrt(d_h), allow, add=M)["Y"]) > 10 * TOL[dt]
 
 
-def test_forward_biases_at_headline_size_sampled():
+def test_forward_biases_at_headline_size():
     """Projection biases on the 4 x 4096-token causal bf16 workload (fast
-    attention path, 256x256 GEMM tiles), checked on sampled query rows."""
+    attention path, 256x256 GEMM tiles): every element of Y."""
     w = WORKLOADS["self-bf16-B4-T4096-dm1024-h16-dh64-causal"]
     _say("[forward biases, full size] " + w.name)
     x = make_inputs(w)
@@ -903,14 +975,11 @@ def test_forward_biases_at_headline_size_sampled():
     Y = mha.mha_forward(Q, Q, Q, Wd["W_Q"], Wd["W_K"], Wd["W_V"], Wd["W_O"], w.h, w.d_h, w.d_vh,
                         causal=True, **{k: _to_dev(v, "bf16") for k, v in bs.items()})
     torch.cuda.synchronize()
-    Y = Y.cpu().numpy()
-    allow = _allow(w, x)
-    for b, rows in ((0, [0, 1, 777, 4095]), (3, [63, 64, 2048, 4000])):
-        Yr, _, _, _ = mha_ref_rows(x["Q"], x["Q"], x["Q"], x["W_Q"], x["W_K"], x["W_V"], x["W_O"],
-                                   w.h, w.d_h, w.d_vh, w.scale, allow, b, rows, biases=bs)
-        err = _rel_err(Y[b, rows], Yr)
-        _say(f"  item {b} rows {rows}: err {err:.3e}")
-        assert err <= TOL["bf16"]
+    ref = mha_ref(x["Q"], x["Q"], x["Q"], x["W_Q"], x["W_K"], x["W_V"], x["W_O"], w.h, w.d_h,
+                  w.d_vh, w.scale, _allow(w, x), biases=bs)["Y"]
+    err = _rel_err(Y.cpu().numpy(), ref)
+    _say(f"  Y err over every output {err:.3e}")
+    assert err <= TOL["bf16"]
 
 
 # ---------------------------------------------------------------------------

@@ -1,0 +1,97 @@
+"""CPU tests of tests/rounding_model.py, the float64 model of the roundings
+of the library's fp16 and bf16 paths from which the GPU tests' fp16 bars are
+set.
+
+* With every rounding turned off the model's block-by-block bookkeeping (the
+  deferred shift with its redo, the exact-shift merge) reproduces the plain
+  definition (the oracle) to float64 rounding: the model computes what the
+  page "Stable summary of an attention key block" (Definition) computes, in
+  another order.
+* A row with a single allowed key gets that key's value, rounded once to the
+  output type: the weight 2^0 = 1 is exact in every format.
+* Coarser weights (bf16 instead of fp16) give a larger error.
+* The headline constants in tests/bars.py are what the model computes, and
+  the headline bar is about twice the modelled error.
+"""
+
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+import bars  # noqa: E402
+import rounding_model as RM  # noqa: E402
+from oracle import allowed_set, attn_core_ref, mha_ref  # noqa: E402
+from transformer_head_self_amd.inputs import WORKLOADS, make_heads, make_inputs  # noqa: E402
+
+
+def _jump_heads(n, d, seed):
+    Qh, Kh, Vh = make_heads(1, 2, n, n, d, d, "f32", seed=seed)
+    Qh[..., 0] = 4.0
+    Kh[..., 0] *= 0.1
+    Kh[:, :, 200, 0] = 40.0
+    Kh[:, :, 450, 0] = 300.0
+    return RM.rnd16(Qh), RM.rnd16(Kh), RM.rnd16(Vh)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_model_without_rounding_is_the_definition(causal):
+    """Score jumps of 20 and 150 nats late in the rows make the deferred
+    shift move and redo blocks; key padding empties whole blocks of some
+    rows."""
+    n, d = 600, 64
+    Qh, Kh, Vh = _jump_heads(n, d, 91)
+    kl = None if causal else np.array([333], np.int32)
+    allow = allowed_set(1, n, n, causal=causal, key_len=kl)
+    ref = attn_core_ref(Qh, Kh, Vh, 1 / math.sqrt(d), allow)["Z"]
+    Zd = RM.attn_core_f16_model(Qh, Kh, Vh, 1 / math.sqrt(d), allow, exact=True)
+    Ze = RM.attn_core_exact_shift_model(Qh, Kh, Vh, 1 / math.sqrt(d), allow, exact=True)
+    assert RM.rel_err(Zd, ref) < 1e-12
+    assert RM.rel_err(Ze, ref) < 1e-12
+
+
+def test_single_allowed_key_is_its_value_rounded_once():
+    Qh, Kh, Vh = make_heads(1, 1, 3, 3, 16, 16, "f32", seed=92)
+    Qh, Kh, Vh = RM.rnd16(Qh), RM.rnd16(Kh), RM.rnd16(Vh)
+    allow = allowed_set(1, 3, 3, causal=True)   # row 0 allows key 0 only
+    for Z in (RM.attn_core_f16_model(Qh, Kh, Vh, 0.25, allow, out_dtype="f16"),
+              RM.attn_core_exact_shift_model(Qh, Kh, Vh, 0.25, allow, out_dtype="f16")):
+        np.testing.assert_array_equal(Z[0, 0], RM.rnd16(Vh[0, 0, 0]))
+
+
+def test_coarser_weights_give_a_larger_error():
+    Qh, Kh, Vh = make_heads(1, 2, 300, 300, 64, 64, "bf16", seed=93)
+    allow = allowed_set(1, 300, 300, causal=True)
+    ref = attn_core_ref(Qh, Kh, Vh, 0.125, allow)["Z"]
+    e16 = RM.rel_err(RM.attn_core_exact_shift_model(Qh, Kh, Vh, 0.125, allow, "f16"), ref)
+    eb16 = RM.rel_err(RM.attn_core_exact_shift_model(Qh, Kh, Vh, 0.125, allow, "bf16"), ref)
+    assert 4.0 < eb16 / e16 < 16.0    # unit roundoff 2^-8 against 2^-11 per weight
+
+
+def test_headline_constants_are_the_models_errors():
+    """The benchmark's workload (B=4, T=4096, d_model=1024, h=16, d_h=64,
+    causal, bf16 inputs): the forward's modelled error on batch item 0, and
+    the core's on the item with the largest one (item 3), as stored in
+    tests/bars.py; the headline core bar is about twice the latter, and the
+    modelled forward stays inside the 2e-2 bar."""
+    w = WORKLOADS["self-bf16-B4-T4096-dm1024-h16-dh64-causal"]
+    x = make_inputs(w)
+    allow = allowed_set(1, w.n_q, w.n_k, causal=True)
+    X0 = x["Q"][:1]
+    ref = mha_ref(X0, X0, X0, x["W_Q"], x["W_K"], x["W_V"], x["W_O"], w.h, w.d_h, w.d_vh,
+                  w.scale, allow)["Y"]
+    Ym = RM.mha_forward_f16_model(X0, X0, X0, x["W_Q"], x["W_K"], x["W_V"], x["W_O"], w.h,
+                                  w.d_h, w.d_vh, w.scale, allow)
+    e_fwd = RM.rel_err(Ym, ref)
+    assert abs(e_fwd / bars.HEADLINE_MODEL_ERR_ITEM0 - 1) < 0.02
+    assert e_fwd < 2e-2
+    X3 = x["Q"][3:4]
+    heads = [RM.heads_f16(X3, x[k], w.h, w.d_h) for k in ("W_Q", "W_K", "W_V")]
+    refz = attn_core_ref(*heads, w.scale, allow)["Z"]
+    e_core = RM.rel_err(RM.attn_core_f16_model(*heads, w.scale, allow, out_dtype="f16"), refz)
+    assert abs(e_core / bars.HEADLINE_CORE_MODEL_ERR - 1) < 0.02
+    assert 1.5 <= bars.F16_CORE_HEADLINE_BAR / bars.HEADLINE_CORE_MODEL_ERR <= 3.0

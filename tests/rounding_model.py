@@ -181,6 +181,58 @@ def core_bar(Qh, Kh, Vh, scale, allow, ref_Z, elem="f16", out_dtype="f32", floor
     return max(2.0 * max(errs), floor)
 
 
+def attn_core_grad_model(Qh, Kh, Vh, scale, allow, dZ, Z, elem="f16", grad_dtype="f32",
+                         add=None, exact=False):
+    """Gradients (dQh, dKh, dVh) of the attention core under the backward
+    kernels' roundings: with A the row softmax (fp32, modelled exactly), the
+    kernels round dZ, A (the dV product's operand) and dS = A o (dA - D) once
+    to the heads' type `elem`; every sum is fp32 (modelled exactly); the
+    gradients are stored in `grad_dtype` (the type of Z and dZ).  D_i =
+    sum_e dZ_ie Z_ie uses the rounded dZ and the stored Z.  exact=True turns
+    every rounding off."""
+    re = _ident if exact else (rnd16 if elem == "f16" else rnd_bf16)
+    rg = _ident if exact else {"f32": rnd32, "f16": rnd16, "bf16": rnd_bf16}[grad_dtype]
+    Qh, Kh, Vh = (np.asarray(t, np.float64) for t in (Qh, Kh, Vh))
+    dZ = re(np.asarray(dZ, np.float64))
+    Z = np.asarray(Z, np.float64)
+    B, h, n_q, _ = Qh.shape
+    n_k, d_vh = Kh.shape[2], Vh.shape[3]
+    M = None if add is None else np.broadcast_to(np.asarray(add, np.float64), (B, n_q, n_k))
+    dQ, dK, dV = np.zeros_like(Qh), np.zeros_like(Kh), np.zeros_like(Vh)
+    for b in range(B):
+        A_ok = np.asarray(allow[b], bool)
+        if M is not None:
+            A_ok = A_ok & (M[b] > -np.inf)
+        for r in range(h):
+            S = scale * (Qh[b, r] @ Kh[b, r].T)
+            if M is not None:
+                S = S + np.where(A_ok, M[b], 0.0)
+            S = np.where(A_ok, S, -np.inf)
+            mx = S.max(axis=1, keepdims=True)
+            mx = np.where(np.isfinite(mx), mx, 0.0)
+            E = np.where(A_ok, np.exp(S - mx), 0.0)
+            den = E.sum(axis=1, keepdims=True)
+            A = np.divide(E, den, out=np.zeros_like(E), where=den > 0)
+            dZr = dZ[b, :, r * d_vh:(r + 1) * d_vh]
+            D = np.sum(dZr * Z[b, :, r * d_vh:(r + 1) * d_vh], axis=1, keepdims=True)
+            dA = dZr @ Vh[b, r].T
+            dS = re(A * (dA - D))
+            dV[b, r] = re(A).T @ dZr
+            dQ[b, r] = scale * (dS @ Kh[b, r])
+            dK[b, r] = scale * (dS.T @ Qh[b, r])
+    return {"dQh": rg(dQ), "dKh": rg(dK), "dVh": rg(dV)}
+
+
+def grad_err(out, ref):
+    """(||out - ref|| / ||ref||, max|out - ref| / max|ref|), the metrics of
+    the gradient bars."""
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = out - ref
+    return (float(np.linalg.norm(d) / np.linalg.norm(ref)),
+            float(np.abs(d).max() / np.abs(ref).max()))
+
+
 def heads_f16(X, W, h, d):
     """A projection of bf16 X by bf16 W, accumulated exactly and rounded to
     fp16, in the head-major layout [B, h, n, d]."""

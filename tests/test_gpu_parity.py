@@ -33,8 +33,9 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 DEV = "cuda:0"
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-from bars import F16_CORE_HEADLINE_BAR, HEADLINE_MODEL_ERR_ITEM0  # noqa: E402
+from bars import BWD_TOL, F16_CORE_HEADLINE_BAR, HEADLINE_MODEL_ERR_ITEM0  # noqa: E402
 from rounding_model import core_bar  # noqa: E402
+from bwd_cases import BWD_CASES, additive_bias, bwd_case_inputs  # noqa: E402
 
 
 def _say(msg):
@@ -849,11 +850,7 @@ def test_split_decode_full_size_sampled():
 # additive score bias M and projection biases
 # ---------------------------------------------------------------------------
 
-def _additive(rng, Bm, n_q, n_k, frac_forbidden=0.1):
-    M = rng.normal(size=(Bm, n_q, n_k)) * 2.0
-    M[rng.random(M.shape) < frac_forbidden] = -np.inf
-    M[:, :, 0] = rng.normal(size=(Bm, n_q))  # key 0 stays allowed in every row
-    return M.astype(np.float32)
+_additive = additive_bias
 
 
 ADD_CASES = [
@@ -989,13 +986,9 @@ def test_forward_biases_at_headline_size():
 from oracle import attn_core_grad_ref  # noqa: E402
 
 # Gradient bars (normwise ||out - ref|| / ||ref||, and max|out - ref| /
-# max|ref|): the kernels round A, dS and dZ once to the element type
-# (u = 2^-9 for bf16, 2^-11 for fp16) before fp32 sums; a CPU emulation of
-# exactly those roundings on these cases gives normwise 2.4e-3 (bf16) and
-# 3e-4 (fp16), max-normalised at most 3.7e-3 and 6.2e-4.  The bars are about
-# twice that.  (max|err| / RMS, the forward's metric, is dominated by the
-# heavy tail of the gradients: a few keys with large weights.)
-BWD_TOL = {"bf16": (5e-3, 1e-2), "f16": (1e-3, 2e-3)}
+# max|ref|): tests/bars.py, each 1.5 to 3.5 times the error of the backward's
+# rounding model on these cases.  (max|err| / RMS, the forward's metric, is
+# dominated by the heavy tail of the gradients: a few keys with large weights.)
 
 
 def _grad_err(out, ref):
@@ -1029,40 +1022,13 @@ def _bwd_run(dt, zdt, Qh, Kh, Vh, dZ, c, causal=False, key_len=None, allowed=Non
             dZt.float().cpu().numpy().astype(np.float64))
 
 
-BWD_CASES = [
-    # dtype, grad dtype, B, h, n_q, n_k, d_h, d_vh, causal, key_len, bool, additive
-    ("bf16", "f32", 2, 3, 100, 333, 64, 64, False, None, False, False),
-    ("f16", "f32", 2, 2, 200, 200, 64, 64, True, None, False, False),
-    ("bf16", "bf16", 2, 2, 130, 257, 64, 96, False, (257, 100), False, False),
-    ("f16", "f32", 1, 2, 300, 300, 128, 128, True, (300,), False, False),
-    ("f16", "f16", 3, 2, 65, 65, 40, 24, True, (65, 10, 1), False, False),
-    ("bf16", "f32", 2, 2, 96, 160, 32, 32, False, None, True, False),
-    ("f16", "f32", 2, 2, 150, 150, 64, 64, True, None, False, True),
-    ("f16", "f32", 2, 2, 1, 700, 64, 64, False, (700, 300), False, False),
-    # dZ in the heads' type, n_q a multiple of 4: the direct-load dK/dV kernel
-    # (ragged query and key tiles, causal, padding, both widths, 4 rows)
-    ("f16", "f16", 2, 3, 100, 333, 64, 64, False, None, False, False),
-    ("bf16", "bf16", 2, 2, 200, 200, 64, 64, True, (200, 77), False, False),
-    ("f16", "f16", 1, 2, 300, 300, 128, 128, True, (300,), False, False),
-    ("f16", "f16", 2, 2, 4, 700, 64, 64, False, (700, 300), False, False),
-    ("bf16", "bf16", 2, 2, 132, 90, 128, 128, False, (90, 45), False, False),
-]
 
 
 @pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_backward_matches_oracle(case):
     dt, zdt, B, h, n_q, n_k, d_h, d_vh, causal, kl, use_bool, use_add = case
     _say(f"[backward] {case}")
-    Qh, Kh, Vh = make_heads(B, h, n_q, n_k, d_h, d_vh, "f32", seed=60 + n_q + n_k)
-    rng = np.random.default_rng(61 + n_k)
-    dZ = rng.standard_normal((B, n_q, h * d_vh)).astype(np.float32)
-    key_len = None if kl is None else np.array(kl[:B], dtype=np.int32)
-    G = None
-    if use_bool:
-        G = rng.random((B, n_q, n_k)) < 0.5
-        G[:, :, 0] = True
-    M = _additive(rng, B, n_q, n_k) if use_add else None
-    c = 1.0 / math.sqrt(d_h)
+    Qh, Kh, Vh, dZ, key_len, G, M, c = bwd_case_inputs(case)
     grads, host, dZh = _bwd_run(dt, zdt, Qh, Kh, Vh, dZ, c, causal, key_len, G, M)
     allow = allowed_set(B, n_q, n_k, causal=causal, key_len=key_len, allowed=G)
     ref = attn_core_grad_ref(*host, c, allow, dZh, add=M)

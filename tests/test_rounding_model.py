@@ -95,3 +95,45 @@ def test_headline_constants_are_the_models_errors():
     e_core = RM.rel_err(RM.attn_core_f16_model(*heads, w.scale, allow, out_dtype="f16"), refz)
     assert abs(e_core / bars.HEADLINE_CORE_MODEL_ERR - 1) < 0.02
     assert 1.5 <= bars.F16_CORE_HEADLINE_BAR / bars.HEADLINE_CORE_MODEL_ERR <= 3.0
+
+
+def test_intermediate_precision_choice():
+    """Why bf16 inputs get fp16 intermediates: on the cross-attention workload
+    (all 16 items), rounding only the projected heads to bf16 already misses
+    the 2e-2 bar, while rounding heads, weights, concatenation and W^O to
+    fp16 stays near 5e-3.  Weights at the row's exact maximum; every sum
+    exact.  Expected errors (max |dY| / RMS): heads to bf16 3.1e-2, weights to
+    bf16 1.2e-2, concatenation to bf16 1.7e-2, all to fp16 4.7e-3."""
+    w = WORKLOADS["cross-bf16-B16-nq512-nk2048-h12-dh64-dvh96-keypad"]
+    x = make_inputs(w)
+    Q, K, V = (x[k].astype(np.float64) for k in "QKV")
+    allow = allowed_set(w.B, w.n_q, w.n_k, key_len=x["key_len"])
+    ref = mha_ref(Q, K, V, x["W_Q"], x["W_K"], x["W_V"], x["W_O"], w.h, w.d_h, w.d_vh,
+                  w.scale, allow)["Y"]
+    ident = lambda a: np.asarray(a, np.float64)  # noqa: E731
+    sl = w.scale * RM.LOG2E
+
+    def forward(r_heads, r_weights, r_concat, r_wo):
+        def heads(X, W, d):
+            P = r_heads(X @ np.asarray(W, np.float64))
+            return P.reshape(w.B, X.shape[1], w.h, d).transpose(0, 2, 1, 3)
+        Qh, Kh, Vh = heads(Q, x["W_Q"], w.d_h), heads(K, x["W_K"], w.d_h), heads(V, x["W_V"], w.d_vh)
+        Z = np.empty((w.B, w.n_q, w.h * w.d_vh))
+        for b in range(w.B):
+            for r in range(w.h):
+                S = np.where(allow[b], sl * (Qh[b, r] @ Kh[b, r].T), -np.inf)
+                P = np.where(allow[b], r_weights(np.exp2(S - S.max(axis=1, keepdims=True))), 0.0)
+                Z[b, :, r * w.d_vh:(r + 1) * w.d_vh] = (P @ Vh[b, r]) / P.sum(axis=1, keepdims=True)
+        return r_concat(Z) @ r_wo(np.asarray(x["W_O"], np.float64))
+
+    got = {
+        "heads_bf16": RM.rel_err(forward(RM.rnd_bf16, ident, ident, ident), ref),
+        "weights_bf16": RM.rel_err(forward(ident, RM.rnd_bf16, ident, ident), ref),
+        "concat_bf16": RM.rel_err(forward(ident, ident, RM.rnd_bf16, ident), ref),
+        "all_fp16": RM.rel_err(forward(RM.rnd16, RM.rnd16, RM.rnd16, RM.rnd16), ref),
+    }
+    expect = {"heads_bf16": 3.1e-2, "weights_bf16": 1.2e-2, "concat_bf16": 1.7e-2,
+              "all_fp16": 4.7e-3}
+    for k, v in expect.items():
+        assert abs(got[k] / v - 1) < 0.05, (k, got[k])
+    assert got["heads_bf16"] > 2e-2 > 4 * got["all_fp16"]

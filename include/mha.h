@@ -28,6 +28,9 @@
  *   inputs: fp16 keeps three more mantissa bits than bf16 at the same
  *   matrix-core rate, provided every intermediate stays below 65504 in
  *   magnitude (projected values of order one are far inside that range).
+ *   Beyond it an fp16 intermediate becomes inf and the output is not
+ *   finite; the call still returns MHA_OK (the library does not scan its
+ *   intermediates).  Choose work_dtype = MHA_BF16 where range matters.
  * - The library allocates nothing, keeps no state between calls, never
  *   synchronises, and enqueues its kernels on `stream` (a hipStream_t; NULL
  *   means the null stream).  The caller owns every buffer; the one exception

@@ -147,13 +147,11 @@ def test_headline_workload_every_output():
     assert err0 <= 1.25 * HEADLINE_MODEL_ERR_ITEM0
 
 
-def test_headline_core_every_output():
-    """The attention kernel alone in the benchmark's launch configuration
-    (fp16 heads taken from the forward's workspace, fp16 Z, no row
-    statistics): every element of Z against the oracle run on the same fp16
-    heads (their values converted exactly to float64)."""
+@pytest.fixture(scope="module")
+def headline_heads():
+    """The benchmark's fp16 heads (from the forward's workspace, bf16 inputs
+    B=4, T=4096, d_model=1024, h=16, d_h=64) and the oracle's Z on them."""
     w = WORKLOADS["self-bf16-B4-T4096-dm1024-h16-dh64-causal"]
-    _say(f"[core every output] {w.name}")
     x = make_inputs(w)
     dims = mha.MhaDims(B=w.B, h=w.h, n_q=w.n_q, n_k=w.n_k, d_q=w.d_q, d_k=w.d_k, d_v=w.d_v,
                        d_h=w.d_h, d_vh=w.d_vh, d_o=w.d_o, scale=w.scale, in_dtype=1,
@@ -166,10 +164,33 @@ def test_headline_core_every_output():
     n = w.B * w.h * w.n_q * w.d_h
     heads = [ws[i * 2 * n:(i + 1) * 2 * n].view(torch.float16).view(w.B, w.h, w.n_q, w.d_h)
              for i in range(3)]   # Qh, Kh, Vh: equal sizes, 256-byte multiples
-    Z = mha.attn_core(*heads, scale=w.scale, causal=True, out_dtype=torch.float16)
     torch.cuda.synchronize()
     h64 = [t.float().cpu().numpy() for t in heads]
     ref = attn_core_ref(*h64, w.scale, allowed_set(w.B, w.n_q, w.n_k, causal=True))["Z"]
+    return w, [t.clone() for t in heads], ref
+
+
+@pytest.mark.parametrize("mask", [None, "bool", "additive"])
+def test_headline_core_every_output(headline_heads, mask):
+    """The attention kernel alone in the benchmark's launch configuration
+    (fp16 heads taken from the forward's workspace, fp16 Z, no row
+    statistics): every element of Z against the oracle run on the same fp16
+    heads (their values converted exactly to float64).  mask: the causal
+    rule given again as a boolean mask [B, T, T] or an additive bias (0 /
+    -inf), as the mask benchmark times it (the exact-shift kernels)."""
+    w, heads, ref = headline_heads
+    _say(f"[core every output] {w.name} mask={mask}")
+    T = w.n_q
+    G = M = None
+    if mask is not None:
+        tri = torch.tril(torch.ones(T, T, dtype=torch.bool, device=DEV))
+        if mask == "bool":
+            G = tri.expand(w.B, T, T).contiguous()
+        else:
+            M = torch.zeros(w.B, T, T, device=DEV).masked_fill(~tri, float("-inf"))
+    Z = mha.attn_core(*heads, scale=w.scale, causal=True, allowed=G, add=M,
+                      out_dtype=torch.float16)
+    torch.cuda.synchronize()
     err = _rel_err(Z.float().cpu().numpy(), ref)
     _say(f"  Z err over all {Z.numel()} outputs {err:.3e} (bar {F16_CORE_HEADLINE_BAR})")
     assert err <= F16_CORE_HEADLINE_BAR
@@ -259,6 +280,11 @@ BOOL_FAST_CASES = [
     ("bf16", 2, 3, 200, 520, 64, 128, False, (520, 100), True),
     ("f16", 1, 2, 257, 400, 128, 128, False, None, False),
     ("bf16", 2, 2, 130, 256, 32, 96, False, (256, 3), False),
+    # causal with the mask tile in LDS (n_k a multiple of 16): reversed tile
+    # order and diagonal blocks, per-item and batch-shared masks, query tails
+    ("f16", 2, 2, 400, 400, 64, 64, True, None, False),
+    ("bf16", 2, 2, 336, 336, 64, 64, True, (336, 200), True),
+    ("f16", 1, 3, 272, 272, 128, 128, True, None, True),
 ]
 
 
@@ -327,6 +353,73 @@ def test_zero_scale_prefix_mean_at_full_size():
         for r in (0, h - 1):
             ref = np.cumsum(Vh[b, r].astype(np.float64), axis=0) / np.arange(1, T + 1)[:, None]
             assert _rel_err(Z[b, :, r], ref) < 1e-5
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_key_padding_mean_at_full_size(causal):
+    """c = 0 with key padding at B=4, T=4096, h=16, d=64 (every item and
+    head, every row): all allowed weights are e^0 = 1 (page "Stable summary
+    of an attention key block", Definition), so row i returns the mean of
+    v_0 .. v_(last) with last = L_b - 1 (and at most i when causal).  fp16
+    heads (non-causal: the benchmark's pipelined kernel).  Bound, elementwise:
+    the fp32 sum of n exact values is off by at most (n - 1) 2^-24 sum |v|,
+    and the division adds at most 2 ulps; a row with one key returns it
+    exactly."""
+    B, h, T, d = 4, 16, 4096, 64
+    key_len = np.array([T, 1, 2049, 777], np.int32)
+    _say(f"[zero scale padding] B={B} h={h} T={T} d={d} causal={causal} L={key_len.tolist()}")
+    Qh, Kh, Vh = make_heads(B, h, T, T, d, d, "f32", seed=9)
+    dev = [torch.from_numpy(a).to(DEV).half() for a in (Qh, Kh, Vh)]
+    V16 = dev[2].float().cpu().numpy().astype(np.float64)
+    Z = mha.attn_core(*dev, scale=0.0, causal=causal, key_len=torch.from_numpy(key_len).to(DEV),
+                      out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Z = Z.cpu().numpy().reshape(B, T, h, d).astype(np.float64)
+    u = 2.0 ** -24
+    for b in range(B):
+        L = int(key_len[b])
+        rows = np.arange(T)
+        n = np.minimum(rows + 1, L) if causal else np.full(T, L)
+        for r in range(h):
+            v = V16[b, r]
+            csum = np.cumsum(v, axis=0)
+            cabs = np.cumsum(np.abs(v), axis=0)
+            mean = csum[n - 1] / n[:, None]
+            bound = (n[:, None] - 1) * u * cabs[n - 1] / n[:, None] + 3 * u * np.abs(mean)
+            err = np.abs(Z[b, :, r] - mean)
+            assert np.all(err <= bound), (b, r, float((err - bound).max()))
+            one = n == 1
+            assert np.array_equal(Z[b, one, r], v[np.zeros(int(one.sum()), int)])
+
+
+def test_fp16_intermediates_overflow_is_not_reported():
+    """The fp16 intermediates of bf16 inputs hold |x| < 65504.  Heads beyond
+    that (here W_V scaled by 2^16, exact in bf16, so the value heads reach
+    about 2^16 times N(0, 1)) become inf in fp16 and the output is not
+    finite; the library returns MHA_OK all the same (it does not scan for
+    overflow).  The same inputs with bf16 intermediates stay finite and
+    within that path's 6e-2 bar; W_V scaled by 2^8 stays inside fp16's range
+    and within the 2e-2 bar."""
+    w = custom_workload(name="wide-range", kind="self", dtype="bf16", B=2, n_q=256, n_k=256,
+                        d_q=256, d_k=256, d_v=256, h=4, d_h=64, d_vh=64, d_o=256, causal=True,
+                        seed=21)
+    x = make_inputs(w)
+    allow = _allow(w, x)
+    for shift, wdt, bar in ((16, torch.float16, None), (16, torch.bfloat16, 6e-2),
+                            (8, torch.float16, TOL["bf16"])):
+        xs = dict(x)
+        xs["W_V"] = (x["W_V"].astype(np.float64) * 2.0 ** shift).astype(np.float32)
+        _say(f"[wide range] W_V * 2^{shift} work={wdt}")
+        Y = _run_forward(w, xs, work_dtype=wdt)
+        if bar is None:
+            assert not np.isfinite(Y).all()
+            continue
+        ref = mha_ref(xs["Q"], xs["K"], xs["V"], xs["W_Q"], xs["W_K"], xs["W_V"], xs["W_O"],
+                      w.h, w.d_h, w.d_vh, w.scale, allow)["Y"]
+        assert np.isfinite(Y).all()
+        err = _rel_err(Y, ref)
+        _say(f"  Y err {err:.3e} (bar {bar:.0e})")
+        assert err <= bar
 
 
 def test_single_allowed_key_returns_value_exactly():

@@ -107,3 +107,71 @@ def test_random_backward_core(case):
         fro, mx = _grad_err(got, r)
         _say(f"  {name} normwise {fro:.3e} max {mx:.3e}")
         assert fro <= BWD_TOL[dt][0] and mx <= BWD_TOL[dt][1], name
+
+
+def _draw_masked(seed, n):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dt = ("f16", "bf16")[i % 2]
+        kind = ("bool", "additive")[(i // 2) % 2]
+        d_h = d_vh = int(rng.choice([32, 64, 128]))
+        if i % 4 == 3:
+            d_vh = int(rng.choice([32, 64, 96, 128]))
+        B, h = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        mult = 16 if i % 3 != 2 else 4          # mask tile through LDS, or 4-byte loads
+        n_q = int(rng.integers(1, 400))
+        n_k = int(rng.integers(1, 400 // mult + 1)) * mult
+        causal = bool(rng.integers(0, 2))
+        if causal:
+            n_q = n_k
+        kl = tuple(int(v) for v in rng.integers(1, n_k + 1, size=B)) if rng.integers(0, 2) else None
+        shared = bool(rng.integers(0, 2))
+        density = float(rng.choice([0.1, 0.5, 0.9]))
+        cases.append((dt, kind, B, h, n_q, n_k, d_h, d_vh, causal, kl, shared, density))
+    return cases
+
+
+MASK_CASES = _draw_masked(999, 14)
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_random_masked_core(case):
+    """Random boolean masks and additive biases ([B or 1, n_q, n_k]) on top of
+    random causal / padding rules; every row keeps one allowed key."""
+    dt, kind, B, h, n_q, n_k, d_h, d_vh, causal, kl, shared, density = case
+    _say(f"[random masked] {case}")
+    Qh, Kh, Vh = make_heads(B, h, n_q, n_k, d_h, d_vh, "f32" if dt == "f16" else dt,
+                            seed=900 + n_q + n_k)
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    dev = [torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(tdt) for a in (Qh, Kh, Vh)]
+    host = [t.float().cpu().numpy().astype(np.float64) for t in dev]
+    rng = np.random.default_rng(901 + n_k)
+    key_len = None if kl is None else np.array(kl, dtype=np.int32)
+    Bm = 1 if shared else B
+    ok = rng.random((Bm, n_q, n_k)) < density
+    for bm in range(Bm):
+        L = n_k if key_len is None else int(key_len.min() if shared else key_len[bm])
+        for i in range(n_q):
+            top = min(i if causal else n_k - 1, L - 1)
+            ok[bm, i, int(rng.integers(0, top + 1))] = True
+    G = M = None
+    if kind == "bool":
+        G = ok
+    else:
+        M = np.where(ok, rng.normal(size=ok.shape) * 2.0, -np.inf).astype(np.float32)
+    c = 1.0 / math.sqrt(d_h)
+    Z = mha.attn_core(*dev, scale=c, causal=causal,
+                      key_len=None if key_len is None else torch.from_numpy(key_len).to(DEV),
+                      allowed=None if G is None else torch.from_numpy(G).to(DEV),
+                      add=None if M is None else torch.from_numpy(M).to(DEV),
+                      out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    allow = allowed_set(B, n_q, n_k, causal=causal, key_len=key_len, allowed=G)
+    ref = attn_core_ref(*host, c, allow, add=M)
+    err = _rel_err(Z.cpu().numpy(), ref["Z"])
+    bar = core_bar(*host, c, allow, ref["Z"], elem=dt, add=M)
+    if dt == "bf16":
+        bar = min(bar, TOL["bf16"])
+    _say(f"  Z err {err:.3e} (bar {bar:.2e})")
+    assert err <= bar

@@ -74,10 +74,10 @@ def test_coarser_weights_give_a_larger_error():
 
 def test_headline_constants_are_the_models_errors():
     """The benchmark's workload (B=4, T=4096, d_model=1024, h=16, d_h=64,
-    causal, bf16 inputs): the forward's modelled error on batch item 0, and
-    the core's on the item with the largest one (item 3), as stored in
-    tests/bars.py; the headline core bar is about twice the latter, and the
-    modelled forward stays inside the 2e-2 bar."""
+    causal, bf16 inputs): the forward's modelled error on batch item 0, the
+    core's on the item with the largest one (item 3, deferred shift; item 0,
+    exact shift), as stored in tests/bars.py; the headline core bar is about
+    twice the core's, and the modelled forward stays inside the 2e-2 bar."""
     w = WORKLOADS["self-bf16-B4-T4096-dm1024-h16-dh64-causal"]
     x = make_inputs(w)
     allow = allowed_set(1, w.n_q, w.n_k, causal=True)
@@ -95,6 +95,12 @@ def test_headline_constants_are_the_models_errors():
     e_core = RM.rel_err(RM.attn_core_f16_model(*heads, w.scale, allow, out_dtype="f16"), refz)
     assert abs(e_core / bars.HEADLINE_CORE_MODEL_ERR - 1) < 0.02
     assert 1.5 <= bars.F16_CORE_HEADLINE_BAR / bars.HEADLINE_CORE_MODEL_ERR <= 3.0
+    heads0 = [RM.heads_f16(X0, x[k], w.h, w.d_h) for k in ("W_Q", "W_K", "W_V")]
+    refz0 = attn_core_ref(*heads0, w.scale, allow)["Z"]
+    e_exact = RM.rel_err(RM.attn_core_exact_shift_model(*heads0, w.scale, allow, elem="f16",
+                                                        out_dtype="f16"), refz0)
+    assert abs(e_exact / bars.HEADLINE_CORE_EXACT_MODEL_ERR - 1) < 0.02
+    assert 1.5 <= bars.F16_CORE_HEADLINE_BAR / bars.HEADLINE_CORE_EXACT_MODEL_ERR <= 3.0
 
 
 def test_intermediate_precision_choice():

@@ -36,7 +36,10 @@ __all__ = [
     "MHA_MASK_CAUSAL", "MHA_MASK_KEY_PADDING", "MHA_MASK_BOOL", "MHA_MASK_ADDITIVE",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmha.so")
+# The library to load: the in-tree build, or the file named by
+# TRANSFORMER_HEAD_SELF_AMD_LIB (an instrumented build of the same sources).
+LIB_PATH = (os.environ.get("TRANSFORMER_HEAD_SELF_AMD_LIB") or
+            os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmha.so"))
 
 MHA_F32, MHA_BF16, MHA_F16 = 0, 1, 2
 MHA_ERR_SCRATCH = -10

@@ -247,7 +247,8 @@ def attn_core_grad_ref(Qh, Kh, Vh, scale, allow, dZ, add=None):
 
     Same arguments as ``attn_core_ref`` plus dZ [B, n_q, h*d_vh] (the
     gradient of a scalar loss with respect to the concatenated output Z).
-    Returns dict with dQh, dKh, dVh (shapes of Qh, Kh, Vh).
+    Returns dict with dQh, dKh, dVh (shapes of Qh, Kh, Vh), and with an
+    additive bias also dM (the shape of ``add``: [B or 1, n_q, n_k]).
 
     Derivation (calculus on the definitions the forward follows; the pages
     give no backward pass): for one head, with scores S = c Q K^T (+ M) and
@@ -259,6 +260,9 @@ def attn_core_grad_ref(Qh, Kh, Vh, scale, allow, dZ, add=None):
                                                 A_ij = 0, so dS_ij = 0);
       dQ = c dS K,  dK = c dS^T Q.
     The row term sum_k A_ik dA_ik equals sum_e dZ_ie Z_ie.
+    M enters every head's scores with coefficient 1 (S = c Q K^T + M), so
+    dM is dS summed over the heads, and over the batch items when one M
+    serves them all; a forbidden entry (masked, or M = -inf) gets 0.
     """
     Qh, Kh, Vh = _f64(Qh), _f64(Kh), _f64(Vh)
     dZ = _f64(dZ)
@@ -270,6 +274,7 @@ def attn_core_grad_ref(Qh, Kh, Vh, scale, allow, dZ, add=None):
     dQ = np.zeros_like(Qh)
     dK = np.zeros_like(Kh)
     dV = np.zeros_like(Vh)
+    dM = None if add is None else np.zeros((B, n_q, n_k))
     for b in range(B):
         for r in range(h):
             A = A_all[b, r]                                   # [n_q, n_k]
@@ -280,7 +285,12 @@ def attn_core_grad_ref(Qh, Kh, Vh, scale, allow, dZ, add=None):
             dS = A * (dA - rowdot)
             dQ[b, r] = scale * (dS @ Kh[b, r])
             dK[b, r] = scale * (dS.T @ Qh[b, r])
-    return {"dQh": dQ, "dKh": dK, "dVh": dV}
+            if dM is not None:
+                dM[b] += dS
+    res = {"dQh": dQ, "dKh": dK, "dVh": dV}
+    if dM is not None:
+        res["dM"] = dM if np.shape(add)[0] == B else dM.sum(axis=0, keepdims=True)
+    return res
 
 
 def mha_grad_ref(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, scale, allow, dY, add=None,
@@ -288,7 +298,8 @@ def mha_grad_ref(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, scale, allow, dY, ad
     """Gradients of the full layer for an upstream gradient dY [B, n_q, d_o].
 
     Returns dict with dQ, dK, dV (input gradients; for self-attention the
-    gradient with respect to X is their sum), dW_Q, dW_K, dW_V, dW_O,
+    gradient with respect to X is their sum), dM (with an additive bias, as
+    in attn_core_grad_ref), dW_Q, dW_K, dW_V, dW_O,
     db_Q, db_K, db_V, db_O (the bias gradients, whether or not the forward
     used biases: a bias enters additively, so its gradient does not depend
     on its value) and dQ_cat, dK_cat, dV_cat (the heads' gradients side by
@@ -318,4 +329,6 @@ def mha_grad_ref(Q, K, V, W_Q, W_K, W_V, W_O, h, d_h, d_vh, scale, allow, dY, ad
         out["db_" + name] = flat.sum(axis=(0, 1))
         out["d" + name + "_cat"] = flat
         out["d" + name] = flat @ W.T
+    if "dM" in g:
+        out["dM"] = g["dM"]
     return out

@@ -844,6 +844,61 @@ def test_core_gradient_matches_central_differences(mask):
         np.testing.assert_allclose(g[key], num, rtol=1e-6, atol=1e-8)
 
 
+@pytest.mark.parametrize("shared", [False, True])
+def test_bias_gradient_matches_central_differences(shared):
+    """dM, the gradient with respect to the additive score bias: every finite
+    entry against the central difference of the forward oracle; entries that
+    are -inf or masked get exactly 0.  A batch-shared M ([1, n_q, n_k])
+    collects both items' contributions."""
+    n_q, n_k = 5, 6
+    Qh, Kh, Vh, dZ = _grad_case(84, n_q=n_q, n_k=n_k)
+    rng = _rng(85)
+    allow = allowed_set(2, n_q, n_k, key_len=np.array([6, 4]))
+    M = rng.normal(size=(1 if shared else 2, n_q, n_k))
+    M[:, 1, 2] = -np.inf
+    c = 0.6
+    g = attn_core_grad_ref(Qh, Kh, Vh, c, allow, dZ, add=M)
+    assert g["dM"].shape == M.shape
+
+    def loss(Mx):
+        return float(np.sum(attn_core_ref(Qh, Kh, Vh, c, allow, add=Mx)["Z"] * dZ))
+
+    eps = 1e-5
+    for idx in np.ndindex(M.shape):
+        if not np.isfinite(M[idx]):
+            assert g["dM"][idx] == 0.0
+            continue
+        Mp = M.copy(); Mp[idx] += eps
+        Mm = M.copy(); Mm[idx] -= eps
+        num = (loss(Mp) - loss(Mm)) / (2 * eps)
+        assert abs(g["dM"][idx] - num) <= 1e-8 + 1e-6 * abs(num), idx
+    # keys past an item's length get nothing
+    if not shared:
+        assert np.all(g["dM"][1, :, 4:] == 0.0)
+    # the rows of dS sum to zero (adding a constant to a row of M changes nothing)
+    np.testing.assert_allclose(g["dM"].sum(axis=2), 0.0, atol=1e-12)
+
+
+def test_planted_bias_gradient_mistake_fails_central_differences():
+    """dM from head 0 alone (the sum over heads dropped) is caught."""
+    Qh, Kh, Vh, dZ = _grad_case(86, B=1, h=2, n_q=3, n_k=3, d_h=2, d_vh=2)
+    allow = np.ones((1, 3, 3), bool)
+    M = _rng(87).normal(size=(1, 3, 3))
+    out = attn_core_ref(Qh, Kh, Vh, 0.8, allow, keep_A=True, add=M)
+    A = out["A"][0, 0]
+    dZr = dZ[0, :, 0:2]
+    dA = dZr @ Vh[0, 0].T
+    wrong = A * (dA - np.sum(A * dA, axis=1, keepdims=True))
+    eps = 1e-5
+    Mp = M.copy(); Mp[0, 0, 1] += eps
+    Mm = M.copy(); Mm[0, 0, 1] -= eps
+    num = (np.sum(attn_core_ref(Qh, Kh, Vh, 0.8, allow, add=Mp)["Z"] * dZ) -
+           np.sum(attn_core_ref(Qh, Kh, Vh, 0.8, allow, add=Mm)["Z"] * dZ)) / (2 * eps)
+    assert abs(wrong[0, 1] - num) > 1e-4
+    g = attn_core_grad_ref(Qh, Kh, Vh, 0.8, allow, dZ, add=M)
+    assert abs(g["dM"][0, 0, 1] - num) < 1e-8
+
+
 def test_core_gradient_invariants():
     """Adding one vector to every key leaves each row's softmax unchanged, so
     the key gradients of a (batch, head) sum to zero over the allowed keys;
@@ -919,6 +974,16 @@ def test_layer_gradient_matches_central_differences():
     g = mha_grad_ref(P["Q"], P["K"], P["V"], P["W_Q"], P["W_K"], P["W_V"], P["W_O"], h, d_h,
                      d_vh, c, allow, dY, add=M,
                      biases={k: P[k] for k in ("b_Q", "b_K", "b_V", "b_O")})
+    bs = {k: P[k] for k in ("b_Q", "b_K", "b_V", "b_O")}
+    for idx in np.ndindex(M.shape):
+        lo = []
+        for sgn in (1, -1):
+            Mx = M.copy(); Mx[idx] += sgn * 1e-6
+            Y = mha_ref(P["Q"], P["K"], P["V"], P["W_Q"], P["W_K"], P["W_V"], P["W_O"], h, d_h,
+                        d_vh, c, allow, add=Mx, biases=bs)["Y"]
+            lo.append(float(np.sum(Y * dY)))
+        num = (lo[0] - lo[1]) / 2e-6
+        assert abs(g["dM"][idx] - num) <= 1e-7 + 1e-6 * abs(num), idx
     eps = 1e-6
     for name in P:
         num = np.zeros_like(P[name])

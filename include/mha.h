@@ -232,8 +232,10 @@ mha_status attn_core_split_noalloc(const mha_dims* d, const mha_mask* m,
  * "Stable summary of an attention key block", Definition: the weights are
  * e^(s - m) / l for the final (m, l) of each row); nothing of size n_q x n_k
  * is stored.  Same dims and mask as the forward call (an additive bias M is
- * applied; no gradient with respect to M is formed).
- *   in_dtype   BF16 or F16 (Qh, Kh, Vh); F32 gives MHA_ERR_DTYPE.
+ * applied; its gradient is attn_bias_backward's).
+ *   in_dtype   BF16 or F16 (Qh, Kh, Vh: matrix-core kernels, operands
+ *              rounded to that type, fp32 sums) or F32 (vector-ALU
+ *              kernels, fp32 throughout).
  *   out_dtype  element type of Z, dZ and of the gradients written.
  *   Qh, Kh, Vh as for attn_core; Z [B, n_q, h*d_vh] the forward's output,
  *   dZ of the same shape; row_m, row_l [B, h, n_q] fp32 from the same
@@ -250,6 +252,29 @@ mha_status attn_core_backward(const mha_dims* d, const mha_mask* m,
                               const void* Z, const void* dZ,
                               const float* row_m, const float* row_l,
                               void* dQh, void* dKh, void* dVh,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Gradient of the same loss with respect to the additive score bias M of
+ * attn_core (mask flag MHA_MASK_ADDITIVE required, else MHA_ERR_MASK).  M
+ * enters every head's scores with coefficient 1 (page "Multi-Head Attention"
+ * review, "The Complete Multi-Head Operation": softmax(Q K^T / sqrt(d_k) + M)
+ * per head), so
+ *   dM = sum over heads r of dS_r   (dS_r as in attn_core_backward),
+ * summed over the batch items as well when one M serves them all
+ * (add_batch_stride 0).  Arguments as for attn_core_backward (any in_dtype;
+ * operands as the products of attn_core_backward see them: dZ rounded to
+ * a 2-byte in_dtype), plus:
+ *   dM  fp32 [B, n_q, n_k], or [1, n_q, n_k] for a shared M (written in
+ *       full: entries that are forbidden, -inf in M, masked or past the
+ *       keys of an item get 0), device memory, 4-byte aligned.
+ *   workspace as for attn_core_backward (the row terms are formed again).
+ * Two launches on `stream`: row terms, then one vector-ALU kernel that walks
+ * the heads (and items) of each 64 x 64 tile of dM in order: deterministic,
+ * no atomics, no scratch of size n_q x n_k per head. */
+mha_status attn_bias_backward(const mha_dims* d, const mha_mask* m,
+                              const void* Qh, const void* Kh, const void* Vh,
+                              const void* Z, const void* dZ,
+                              const float* row_m, const float* row_l, float* dM,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Gradient outputs for the projection biases of mha_backward: each pointer
@@ -289,8 +314,8 @@ size_t mha_backward_workspace_bytes(const mha_dims* d);
  *   accumulated: for self-attention the gradient of X is dQ + dK + dV),
  *   dW_Q, dW_K, dW_V, dW_O (shapes of the weights), dbias (may be NULL).
  *   workspace: mha_backward_workspace_bytes(d) bytes, 256-byte aligned.
- * work_dtype must be BF16 or F16 (the core backward's element types); with
- * F32 the call returns MHA_ERR_DTYPE.  All products accumulate in fp32;
+ * work_dtype BF16 or F16 (matrix-core core backward) or F32 (vector-ALU
+ * core backward, fp32 operands).  All products accumulate in fp32;
  * operands are rounded to work_dtype.  Deterministic. */
 mha_status mha_backward(const mha_dims* d, const mha_mask* m,
                         const void* Q, const void* K, const void* V,

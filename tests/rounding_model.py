@@ -123,12 +123,14 @@ def attn_core_f16_model(Qh, Kh, Vh, scale, allow, out_dtype="f16", block=64, tau
 
 
 def attn_core_exact_shift_model(Qh, Kh, Vh, scale, allow, elem="f16", out_dtype="f32",
-                                block=64, exact=False, add=None):
+                                block=64, exact=False, add=None, stats=False):
     """Z of the exact-shift form: weights 2^(c log2(e) s + M log2(e) - m), m
-    the running exact maximum, rounded to `elem` ("f16" or "bf16"); `add`: an
-    optional additive score bias M [B or 1, n_q, n_k] in natural-log units
-    (-inf forbids a key); exact=True turns every rounding off."""
-    rw = _ident if exact else (rnd16 if elem == "f16" else rnd_bf16)
+    the running exact maximum, rounded to `elem` ("f16", "bf16", or "f32":
+    no rounding); `add`: an optional additive score bias M [B or 1, n_q, n_k]
+    in natural-log units (-inf forbids a key); exact=True turns every
+    rounding off.  stats=True also returns the rows' final (m, l): m in
+    base-2 units, l the sum of the rounded weights at that shift."""
+    rw = _ident if (exact or elem == "f32") else (rnd16 if elem == "f16" else rnd_bf16)
     rout = _ident if exact else {"f32": rnd32, "f16": rnd16, "bf16": rnd_bf16}[out_dtype]
     Qh, Kh, Vh = (np.asarray(t, np.float64) for t in (Qh, Kh, Vh))
     B, h, n_q, _ = Qh.shape
@@ -136,6 +138,8 @@ def attn_core_exact_shift_model(Qh, Kh, Vh, scale, allow, elem="f16", out_dtype=
     sl = abs(scale) * LOG2E if exact else float(np.float32(abs(scale)) * np.float32(LOG2E))
     sg = -1.0 if scale < 0 else 1.0
     Z = np.empty((B, n_q, h * d_vh))
+    m_out = np.empty((B, h, n_q))
+    l_out = np.empty((B, h, n_q))
     nblk = (n_k + block - 1) // block
     M = None if add is None else np.broadcast_to(np.asarray(add, np.float64), (B, n_q, n_k))
     for b in range(B):
@@ -162,7 +166,11 @@ def attn_core_exact_shift_model(Qh, Kh, Vh, scale, allow, elem="f16", out_dtype=
                 l += p.sum(axis=1)
                 z += p @ Vh[b, r, k * block:(k + 1) * block]
                 m = m_new
-            Z[b, :, r * d_vh:(r + 1) * d_vh] = rout(z / l[:, None])
+            with np.errstate(invalid="ignore", divide="ignore"):
+                Z[b, :, r * d_vh:(r + 1) * d_vh] = rout(z / l[:, None])
+            m_out[b, r], l_out[b, r] = m, l
+    if stats:
+        return Z, m_out, l_out
     return Z
 
 
@@ -182,15 +190,18 @@ def core_bar(Qh, Kh, Vh, scale, allow, ref_Z, elem="f16", out_dtype="f32", floor
 
 
 def attn_core_grad_model(Qh, Kh, Vh, scale, allow, dZ, Z, elem="f16", grad_dtype="f32",
-                         add=None, exact=False):
-    """Gradients (dQh, dKh, dVh) of the attention core under the backward
-    kernels' roundings: with A the row softmax (fp32, modelled exactly), the
-    kernels round dZ, A (the dV product's operand) and dS = A o (dA - D) once
-    to the heads' type `elem`; every sum is fp32 (modelled exactly); the
-    gradients are stored in `grad_dtype` (the type of Z and dZ).  D_i =
-    sum_e dZ_ie Z_ie uses the rounded dZ and the stored Z.  exact=True turns
-    every rounding off."""
-    re = _ident if exact else (rnd16 if elem == "f16" else rnd_bf16)
+                         add=None, exact=False, stats=None):
+    """Gradients (dQh, dKh, dVh, and dM with `add`) of the attention core under
+    the backward kernels' roundings: with A the weights recomputed from the
+    row statistics (fp32, modelled exactly; `stats` = (m in base-2 units, l)
+    from the forward, else the exact softmax), the matrix-core kernels round
+    dZ, A (the dV product's operand) and dS = A o (dA - D) once to the heads'
+    type `elem` ("f32": no rounding); every sum is fp32 (modelled exactly);
+    the gradients are stored in `grad_dtype` (the type of Z and dZ).  D_i =
+    sum_e dZ_ie Z_ie uses the rounded dZ and the stored Z.  dM (fp32, shape of
+    `add`) sums the unrounded dS over heads (and items for a shared bias), as
+    the bias-gradient kernel does.  exact=True turns every rounding off."""
+    re = _ident if (exact or elem == "f32") else (rnd16 if elem == "f16" else rnd_bf16)
     rg = _ident if exact else {"f32": rnd32, "f16": rnd16, "bf16": rnd_bf16}[grad_dtype]
     Qh, Kh, Vh = (np.asarray(t, np.float64) for t in (Qh, Kh, Vh))
     dZ = re(np.asarray(dZ, np.float64))
@@ -199,6 +210,7 @@ def attn_core_grad_model(Qh, Kh, Vh, scale, allow, dZ, Z, elem="f16", grad_dtype
     n_k, d_vh = Kh.shape[2], Vh.shape[3]
     M = None if add is None else np.broadcast_to(np.asarray(add, np.float64), (B, n_q, n_k))
     dQ, dK, dV = np.zeros_like(Qh), np.zeros_like(Kh), np.zeros_like(Vh)
+    dM = None if M is None else np.zeros((B, n_q, n_k))
     for b in range(B):
         A_ok = np.asarray(allow[b], bool)
         if M is not None:
@@ -208,19 +220,31 @@ def attn_core_grad_model(Qh, Kh, Vh, scale, allow, dZ, Z, elem="f16", grad_dtype
             if M is not None:
                 S = S + np.where(A_ok, M[b], 0.0)
             S = np.where(A_ok, S, -np.inf)
-            mx = S.max(axis=1, keepdims=True)
-            mx = np.where(np.isfinite(mx), mx, 0.0)
-            E = np.where(A_ok, np.exp(S - mx), 0.0)
-            den = E.sum(axis=1, keepdims=True)
-            A = np.divide(E, den, out=np.zeros_like(E), where=den > 0)
+            if stats is None:
+                mx = S.max(axis=1, keepdims=True)
+                mx = np.where(np.isfinite(mx), mx, 0.0)
+                E = np.where(A_ok, np.exp(S - mx), 0.0)
+                den = E.sum(axis=1, keepdims=True)
+                A = np.divide(E, den, out=np.zeros_like(E), where=den > 0)
+            else:
+                m2, l = stats[0][b, r][:, None], stats[1][b, r][:, None]
+                with np.errstate(divide="ignore", invalid="ignore"):
+                    L2 = np.where((l > 0) & np.isfinite(m2), m2 + np.log2(l), np.inf)
+                    A = np.where(A_ok, np.exp2(S * LOG2E - L2), 0.0)
             dZr = dZ[b, :, r * d_vh:(r + 1) * d_vh]
             D = np.sum(dZr * Z[b, :, r * d_vh:(r + 1) * d_vh], axis=1, keepdims=True)
             dA = dZr @ Vh[b, r].T
-            dS = re(A * (dA - D))
+            dS32 = A * (dA - D)
+            dS = re(dS32)
             dV[b, r] = re(A).T @ dZr
             dQ[b, r] = scale * (dS @ Kh[b, r])
             dK[b, r] = scale * (dS.T @ Qh[b, r])
-    return {"dQh": rg(dQ), "dKh": rg(dK), "dVh": rg(dV)}
+            if dM is not None:
+                dM[b] += dS32
+    out = {"dQh": rg(dQ), "dKh": rg(dK), "dVh": rg(dV)}
+    if dM is not None:
+        out["dM"] = dM if np.shape(add)[0] == B else dM.sum(axis=0, keepdims=True)
+    return out
 
 
 def grad_err(out, ref):

@@ -313,7 +313,7 @@ def test_backward_workspace_and_errors():
     assert need == 2 * ((3 * 5 * 37 * 4 + 255) // 256 * 256)
     assert mha.attn_backward_workspace_bytes(None) == 0
     assert _bwd(None) == -1
-    assert _bwd(_dims()) == -3                       # fp32 heads: no backward kernels
+    assert _bwd(_dims(), ws=None) == -6              # fp32 heads pass the type checks
     for i in range(10):
         p = [FAKE] * 10
         p[i] = None
@@ -326,6 +326,30 @@ def test_backward_workspace_and_errors():
     assert _bwd(d, ws=FAKE + 128, ws_bytes=need) == -5
     assert _bwd(d, MhaMask(flags=mha.MHA_MASK_CAUSAL)) == -4   # n_q != n_k
     assert _bwd(_dims(in_dtype=mha.MHA_F16, out_dtype=mha.MHA_F32, d_h=200)) == -7
+
+
+def _bias_bwd(d, m, ptrs=None, dM=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    p = [FAKE] * 7 if ptrs is None else ptrs
+    return mha.lib().attn_bias_backward(
+        ctypes.byref(d) if d is not None else None, ctypes.byref(m) if m is not None else None,
+        *p, dM, ws, ws_bytes, None)
+
+
+def test_bias_backward_errors():
+    d = _dims(in_dtype=mha.MHA_BF16, out_dtype=mha.MHA_BF16, B=3, h=5, n_q=37)
+    add = MhaMask(flags=mha.MHA_MASK_ADDITIVE, add=FAKE, add_batch_stride=0)
+    assert _bias_bwd(None, add) == -1
+    assert _bias_bwd(d, None) == -4                  # the additive bias is required
+    assert _bias_bwd(d, MhaMask(flags=0)) == -4
+    for i in range(7):
+        p = [FAKE] * 7
+        p[i] = None
+        assert _bias_bwd(d, add, ptrs=p) == -1
+    assert _bias_bwd(d, add, dM=None) == -1
+    assert _bias_bwd(d, add, dM=FAKE + 2) == -5      # fp32 output
+    assert _bias_bwd(d, add, ws=None) == -6
+    assert _bias_bwd(d, MhaMask(flags=mha.MHA_MASK_ADDITIVE, add=FAKE, add_batch_stride=5)) == -4
+    assert _bias_bwd(_dims(), add, ws=None) == -6    # fp32 heads too
 
 
 def test_layer_backward_workspace_and_errors():
@@ -341,7 +365,7 @@ def test_layer_backward_workspace_and_errors():
         return L.mha_backward(ctypes.byref(dd) if dd is not None else None, None, *p, fws, fwb,
                               *([FAKE] * 7), None, ws, wsb, None)
     assert call(None) == -1
-    assert call(_dims()) == -3                         # fp32 intermediates: no core backward
+    assert call(_dims(), wsb=0) == -6                  # fp32 intermediates pass the type checks
     for i in range(10):
         p = [FAKE] * 10
         p[i] = None

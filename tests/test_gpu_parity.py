@@ -34,6 +34,8 @@ DEV = "cuda:0"
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 from bars import BWD_TOL, F16_CORE_HEADLINE_BAR, HEADLINE_MODEL_ERR_ITEM0  # noqa: E402
+from rounding_model import attn_core_exact_shift_model as exact_shift_model  # noqa: E402
+from rounding_model import attn_core_grad_model as grad_model  # noqa: E402
 from rounding_model import core_bar  # noqa: E402
 from bwd_cases import BWD_CASES, additive_bias, bwd_case_inputs  # noqa: E402
 
@@ -1095,7 +1097,7 @@ def _grad_err(out, ref):
 def _bwd_run(dt, zdt, Qh, Kh, Vh, dZ, c, causal=False, key_len=None, allowed=None, add=None):
     """GPU forward (for Z, row_m, row_l) then backward; returns numpy grads,
     the exact values the GPU consumed (heads and dZ), and Z."""
-    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dt]
     zt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[zdt]
     dev = [torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(tdt) for a in (Qh, Kh, Vh)]
     B, h, n_q, _ = Qh.shape
@@ -1175,6 +1177,112 @@ def test_backward_full_size_two_heads(zdt):
             assert fro <= BWD_TOL["f16"][0] and mx <= BWD_TOL["f16"][1]
 
 
+FP32_BWD_CASES = [
+    # B, h, n_q, n_k, d_h, d_vh, causal, key_len, bool, additive
+    (2, 4, 64, 64, 16, 16, True, None, False, False),          # the fp32 causal workload's heads
+    (8, 8, 512, 512, 64, 64, False, (512, 128, 300, 511, 200, 129, 400, 256), False, False),
+    (2, 3, 100, 333, 40, 24, False, (333, 100), True, False),
+    (2, 2, 130, 130, 128, 96, True, None, False, True),
+]
+
+
+@pytest.mark.parametrize("case", FP32_BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_backward_fp32_heads(case):
+    """fp32 heads, Z, dZ and gradients (the vector-ALU backward kernels):
+    against the oracle's gradients under the fp32 bar."""
+    B, h, n_q, n_k, d_h, d_vh, causal, kl, use_bool, use_add = case
+    _say(f"[backward fp32] {case}")
+    Qh, Kh, Vh = make_heads(B, h, n_q, n_k, d_h, d_vh, "f32", seed=66 + n_q + n_k)
+    rng = np.random.default_rng(67 + n_k)
+    dZ = rng.standard_normal((B, n_q, h * d_vh)).astype(np.float32)
+    key_len = None if kl is None else np.array(kl[:B], dtype=np.int32)
+    G = None
+    if use_bool:
+        G = rng.random((B, n_q, n_k)) < 0.5
+        G[:, :, 0] = True
+    M = additive_bias(rng, B, n_q, n_k) if use_add else None
+    c = 1.0 / math.sqrt(d_h)
+    grads, host, dZh = _bwd_run("f32", "f32", Qh, Kh, Vh, dZ, c, causal, key_len, G, M)
+    allow = allowed_set(B, n_q, n_k, causal=causal, key_len=key_len, allowed=G)
+    ref = attn_core_grad_ref(*host, c, allow, dZh, add=M)
+    for name, got in zip(("dQh", "dKh", "dVh"), grads):
+        fro, mx = _grad_err(got, ref[name])
+        _say(f"  {name} normwise {fro:.3e} max {mx:.3e}")
+        assert fro <= BWD_TOL["f32"][0] and mx <= BWD_TOL["f32"][1], name
+    if key_len is not None:
+        for b in range(B):
+            assert np.all(grads[1][b, :, key_len[b]:] == 0)
+            assert np.all(grads[2][b, :, key_len[b]:] == 0)
+
+
+DM_CASES = [
+    # heads, Z/dZ type, B, h, n_q, n_k, d_h, d_vh, causal, key_len, bool, batch-shared M
+    ("f16", "f32", 2, 3, 100, 333, 64, 64, False, None, False, False),
+    ("bf16", "bf16", 2, 2, 200, 200, 64, 64, True, (200, 77), False, True),
+    ("f32", "f32", 2, 2, 96, 160, 32, 32, False, None, True, False),
+    ("f16", "f16", 1, 4, 65, 65, 40, 24, True, None, False, False),
+    ("bf16", "f32", 3, 2, 70, 130, 128, 96, False, (130, 64, 1), True, True),
+    ("f32", "f32", 2, 2, 64, 64, 16, 16, True, None, False, True),
+]
+
+
+@pytest.mark.parametrize("case", DM_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_bias_gradient_matches_oracle(case):
+    """dM (attn_bias_backward): the gradient with respect to the additive
+    score bias, summed over heads (and items for a shared bias), against the
+    oracle's.  Bars: twice the error of the backward's rounding model (the
+    weights recomputed from the forward's row statistics, dZ rounded to the
+    heads' type, the stored Z), at least the fp32 bar.  Entries no query may
+    use are exactly 0; two runs agree bit for bit."""
+    dt, zdt, B, h, n_q, n_k, d_h, d_vh, causal, kl, use_bool, shared = case
+    _say(f"[bias gradient] {case}")
+    Qh, Kh, Vh = make_heads(B, h, n_q, n_k, d_h, d_vh, "f32", seed=68 + n_q + n_k)
+    rng = np.random.default_rng(69 + n_k)
+    dZ = rng.standard_normal((B, n_q, h * d_vh)).astype(np.float32)
+    key_len = None if kl is None else np.array(kl[:B], dtype=np.int32)
+    G = None
+    if use_bool:
+        G = rng.random((B, n_q, n_k)) < 0.5
+        G[:, :, 0] = True
+    M = additive_bias(rng, 1 if shared else B, n_q, n_k)
+    c = 1.0 / math.sqrt(d_h)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    zt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[zdt]
+    dev = [torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(tdt) for a in (Qh, Kh, Vh)]
+    kl_dev = None if key_len is None else torch.from_numpy(key_len).to(DEV)
+    G_dev = None if G is None else torch.from_numpy(G).to(DEV)
+    M_dev = torch.from_numpy(M).to(DEV)
+    rm = torch.empty((B, h, n_q), device=DEV)
+    rl = torch.empty_like(rm)
+    Z = mha.attn_core(*dev, scale=c, causal=causal, key_len=kl_dev, allowed=G_dev, add=M_dev,
+                      out_dtype=zt, row_m=rm, row_l=rl)
+    dZt = torch.from_numpy(dZ).to(DEV).to(zt)
+    dM = mha.attn_bias_backward(*dev, Z, dZt, rm, rl, M_dev, scale=c, causal=causal,
+                                key_len=kl_dev, allowed=G_dev)
+    dM2 = mha.attn_bias_backward(*dev, Z, dZt, rm, rl, M_dev, scale=c, causal=causal,
+                                 key_len=kl_dev, allowed=G_dev)
+    torch.cuda.synchronize()
+    got = dM.cpu().numpy()
+    assert np.array_equal(got, dM2.cpu().numpy())
+    host = [t.float().cpu().numpy().astype(np.float64) for t in dev]
+    dZh = dZt.float().cpu().numpy().astype(np.float64)
+    allow = allowed_set(B, n_q, n_k, causal=causal, key_len=key_len, allowed=G)
+    ref = attn_core_grad_ref(*host, c, allow, dZh, add=M)["dM"]
+    assert got.shape == ref.shape
+    Zm, m2, lm = exact_shift_model(*host, c, allow, elem=dt, out_dtype=zdt, add=M, stats=True)
+    model = grad_model(*host, c, allow, dZh, np.nan_to_num(Zm), elem=dt, grad_dtype=zdt, add=M,
+                       stats=(m2, lm))["dM"]
+    mfro, mmx = _grad_err(model, ref)
+    bar = (max(2 * mfro, BWD_TOL["f32"][0]), max(2 * mmx, BWD_TOL["f32"][1]))
+    fro, mx = _grad_err(got, ref)
+    _say(f"  dM normwise {fro:.3e} max {mx:.3e} (model {mfro:.2e} / {mmx:.2e})")
+    assert fro <= bar[0] and mx <= bar[1]
+    # entries no query may use: forbidden for every item the bias serves
+    usable = allow & (np.broadcast_to(M, allow.shape) > -np.inf)
+    dead = ~usable.any(axis=0, keepdims=True) if shared else ~usable
+    assert np.all(got[dead] == 0.0)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_split_decode_kernel_masks(dt):
     """The decode-shaped partition kernel (one to four query rows) with a
@@ -1238,6 +1346,65 @@ LAYER_BWD_CASES = [
 
 # bf16 intermediates: each rounding is 2^-8 instead of fp16's 2^-11
 LAYER_TOL_BF16 = (8 * LAYER_TOL[0], 8 * LAYER_TOL[1])
+
+
+LAYER_F32_CASES = [
+    # kind, B, n_q, n_k, d_q, d_k, d_v, h, d_h, d_vh, d_o, causal, key_len, additive
+    ("self", 2, 64, 64, 64, 64, 64, 4, 16, 16, 64, True, None, False),
+    ("cross", 2, 70, 150, 96, 80, 112, 3, 32, 48, 72, False, (150, 40), True),
+]
+
+
+@pytest.mark.parametrize("case", LAYER_F32_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_layer_backward_fp32(case):
+    """fp32 inputs, weights, intermediates and gradients (the fp32 GEMMs and
+    the vector-ALU core backward), with projection biases: every gradient of
+    the layer against the oracle under the fp32 bar."""
+    kind, B, n_q, n_k, d_q, d_k, d_v, h, d_h, d_vh, d_o, causal, kl, use_add = case
+    _say(f"[layer backward fp32] {case}")
+    rng = np.random.default_rng(98 + n_q)
+    Q = rng.standard_normal((B, n_q, d_q)).astype(np.float32)
+    K = V = Q
+    if kind == "cross":
+        K = rng.standard_normal((B, n_k, d_k)).astype(np.float32)
+        V = rng.standard_normal((B, n_k, d_v)).astype(np.float32)
+    W = {k: (rng.standard_normal(s) / math.sqrt(s[0])).astype(np.float32) for k, s in
+         (("W_Q", (d_q, h * d_h)), ("W_K", (d_k, h * d_h)), ("W_V", (d_v, h * d_vh)),
+          ("W_O", (h * d_vh, d_o)))}
+    bs = {k: (rng.standard_normal(n) * 0.5).astype(np.float32) for k, n in
+          (("b_Q", h * d_h), ("b_K", h * d_h), ("b_V", h * d_vh), ("b_O", d_o))}
+    key_len = None if kl is None else np.array(kl[:B], dtype=np.int32)
+    M = _additive(rng, B, n_q, n_k) if use_add else None
+    dY = rng.standard_normal((B, n_q, d_o)).astype(np.float32)
+    c = 1.0 / math.sqrt(d_h)
+    allow = allowed_set(B, n_q, n_k, causal=causal, key_len=key_len)
+    ref = mha_grad_ref(Q, K, V, W["W_Q"], W["W_K"], W["W_V"], W["W_O"], h, d_h, d_vh, c, allow,
+                       dY, add=M, biases=bs)
+    tQ = _to_dev(Q, "f32")
+    tK, tV = (tQ, tQ) if kind == "self" else (_to_dev(K, "f32"), _to_dev(V, "f32"))
+    tW = {k: _to_dev(v, "f32") for k, v in W.items()}
+    kl_dev = None if key_len is None else torch.from_numpy(key_len).to(DEV)
+    M_dev = None if M is None else torch.from_numpy(M).to(DEV)
+    dims = mha.MhaDims(B=B, h=h, n_q=n_q, n_k=n_k, d_q=d_q, d_k=d_k, d_v=d_v, d_h=d_h,
+                       d_vh=d_vh, d_o=d_o, scale=c, in_dtype=0, out_dtype=0, work_dtype=0)
+    fws = torch.empty(mha.mha_workspace_bytes(dims), dtype=torch.uint8, device=DEV)
+    rm = torch.empty((B, h, n_q), device=DEV)
+    rl = torch.empty_like(rm)
+    mha.mha_forward(tQ, tK, tV, tW["W_Q"], tW["W_K"], tW["W_V"], tW["W_O"], h, d_h, d_vh,
+                    scale=c, causal=causal, key_len=kl_dev, add=M_dev, row_m=rm, row_l=rl,
+                    workspace=fws, **{k: _to_dev(v, "f32") for k, v in bs.items()})
+    g = mha.mha_backward(tQ, tK, tV, tW["W_Q"], tW["W_K"], tW["W_V"], tW["W_O"], h, d_h, d_vh,
+                         torch.from_numpy(dY).to(DEV), rm, rl, fws, scale=c, causal=causal,
+                         key_len=kl_dev, add=M_dev, bias_grads=True)
+    torch.cuda.synchronize()
+    for name in ("dQ", "dK", "dV", "dW_Q", "dW_K", "dW_V", "dW_O"):
+        fro, mx = _grad_err(g[name].cpu().numpy(), ref[name])
+        _say(f"  {name} normwise {fro:.3e} max {mx:.3e}")
+        assert fro <= BWD_TOL["f32"][0] and mx <= BWD_TOL["f32"][1], name
+    for name in ("db_Q", "db_V", "db_O"):
+        fro, mx = _grad_err(g[name].cpu().numpy(), ref[name])
+        _say(f"  {name} normwise {fro:.3e} max {mx:.3e}")
+        assert fro <= BWD_TOL["f32"][0] and mx <= BWD_TOL["f32"][1], name
 
 
 @pytest.mark.parametrize("case", LAYER_BWD_CASES, ids=lambda c: "-".join(map(str, c)))

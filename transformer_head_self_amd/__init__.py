@@ -31,7 +31,8 @@ import os
 __all__ = [
     "MhaError", "MhaDims", "MhaMask", "MhaBias", "MhaBiasGrad", "lib", "mha_backward",
     "mha_backward_workspace_bytes", "mha_forward", "attn_core", "attn_core_split",
-    "attn_split_workspace_bytes", "attn_core_split_noalloc", "attn_core_backward", "attn_backward_workspace_bytes",
+    "attn_split_workspace_bytes", "attn_core_split_noalloc", "attn_core_backward",
+    "attn_bias_backward", "attn_backward_workspace_bytes",
     "mha_workspace_bytes", "mha_status_string", "MHA_F32", "MHA_BF16", "MHA_F16",
     "MHA_MASK_CAUSAL", "MHA_MASK_KEY_PADDING", "MHA_MASK_BOOL", "MHA_MASK_ADDITIVE",
 ]
@@ -109,6 +110,9 @@ def lib():
         L.attn_core_backward.argtypes = [P(MhaDims), P(MhaMask)] + [vp] * 11 + [ctypes.c_size_t,
                                                                                 vp]
         L.attn_core_backward.restype = ctypes.c_int
+        L.attn_bias_backward.argtypes = [P(MhaDims), P(MhaMask)] + [vp] * 9 + [ctypes.c_size_t,
+                                                                               vp]
+        L.attn_bias_backward.restype = ctypes.c_int
         L.mha_backward_workspace_bytes.argtypes = [P(MhaDims)]
         L.mha_backward_workspace_bytes.restype = ctypes.c_size_t
         L.mha_backward.argtypes = ([P(MhaDims), P(MhaMask)] + [vp] * 11 + [ctypes.c_size_t] +
@@ -366,7 +370,8 @@ def attn_core_backward(Qh, Kh, Vh, Z, dZ, row_m, row_l, *, scale=None, causal=Fa
                        workspace=None, stream=None):
     """Gradients (dQh, dKh, dVh) of a loss with upstream gradient dZ for the
     attention core; Z, row_m and row_l come from the same forward call (same
-    masks and scale).  Gradients have the element type of Z and dZ."""
+    masks and scale).  Gradients have the element type of Z and dZ.  Heads
+    may be bf16, fp16 or fp32."""
     torch = _torch()
     if dZ.dtype != Z.dtype:
         raise TypeError("Z and dZ must share one element type")
@@ -391,6 +396,36 @@ def attn_core_backward(Qh, Kh, Vh, Z, dZ, row_m, row_l, *, scale=None, causal=Fa
     if st != 0:
         raise MhaError(st, "attn_core_backward")
     return dQh, dKh, dVh
+
+
+def attn_bias_backward(Qh, Kh, Vh, Z, dZ, row_m, row_l, add, *, scale=None, causal=False,
+                       key_len=None, allowed=None, dM=None, workspace=None, stream=None):
+    """Gradient dM (fp32, the shape of ``add``: [B or 1, n_q, n_k]) of a loss
+    with upstream gradient dZ with respect to the additive score bias of
+    the attention core: dS summed over heads (and items for a shared bias).
+    Same arguments as ``attn_core_backward``."""
+    torch = _torch()
+    if dZ.dtype != Z.dtype:
+        raise TypeError("Z and dZ must share one element type")
+    dims = _core_dims(Qh, Kh, Vh, scale, Z.dtype)
+    B, n_q, n_k = dims.B, dims.n_q, dims.n_k
+    m, keep = _mask(B, n_q, n_k, causal, key_len, allowed, Qh.device, add)
+    Bo = 1 if m.add_batch_stride == 0 else B
+    if dM is None:
+        dM = torch.empty((Bo, n_q, n_k), dtype=torch.float32, device=Qh.device)
+    if dM.dtype != torch.float32 or not dM.is_contiguous() or tuple(dM.shape) != (Bo, n_q, n_k):
+        raise ValueError(f"dM must be a contiguous float32 [{Bo}, {n_q}, {n_k}] tensor")
+    if workspace is None:
+        workspace = torch.empty(max(attn_backward_workspace_bytes(dims), 1), dtype=torch.uint8,
+                                device=Qh.device)
+    st = lib().attn_bias_backward(ctypes.byref(dims), ctypes.byref(m), _ptr(Qh), _ptr(Kh),
+                                  _ptr(Vh), _ptr(Z), _ptr(dZ), _ptr(row_m), _ptr(row_l),
+                                  _ptr(dM), _ptr(workspace), workspace.numel(), _stream(stream))
+    _used_on(stream, keep + [dM, workspace])
+    del keep
+    if st != 0:
+        raise MhaError(st, "attn_bias_backward")
+    return dM
 
 
 def mha_backward_workspace_bytes(dims: MhaDims):

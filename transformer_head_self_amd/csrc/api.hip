@@ -425,25 +425,23 @@ size_t attn_backward_workspace_bytes(const mha_dims* d) {
   return 2 * round256((size_t)d->B * d->h * d->n_q * 4);
 }
 
-mha_status attn_core_backward(const mha_dims* d, const mha_mask* m, const void* Qh,
-                              const void* Kh, const void* Vh, const void* Z, const void* dZ,
-                              const float* row_m, const float* row_l, void* dQh, void* dKh,
-                              void* dVh, void* workspace, size_t workspace_bytes, void* stream) {
+// Checks shared by attn_core_backward and attn_bias_backward, and the
+// kernels' parameters (dQ, dK, dV left NULL).
+mha_status core_backward_params(const mha_dims* d, const mha_mask* m, const void* Qh,
+                                const void* Kh, const void* Vh, const void* Z, const void* dZ,
+                                const float* row_m, const float* row_l, void* workspace,
+                                size_t workspace_bytes, mha::AttnBwdParams& p) {
   mha_status s = check_core_dims(d);
   if (s != MHA_OK) return s;
-  if (d->in_dtype == MHA_F32) return MHA_ERR_DTYPE;
   if ((s = check_mask(d, m)) != MHA_OK) return s;
-  if (!Qh || !Kh || !Vh || !Z || !dZ || !row_m || !row_l || !dQh || !dKh || !dVh)
-    return MHA_ERR_NULL;
+  if (!Qh || !Kh || !Vh || !Z || !dZ || !row_m || !row_l) return MHA_ERR_NULL;
   const size_t ei = esize(d->in_dtype), eo = esize(d->out_dtype);
   if (!aligned(Qh, ei) || !aligned(Kh, ei) || !aligned(Vh, ei) || !aligned(Z, eo) ||
-      !aligned(dZ, eo) || !aligned(row_m, 4) || !aligned(row_l, 4) || !aligned(dQh, eo) ||
-      !aligned(dKh, eo) || !aligned(dVh, eo))
+      !aligned(dZ, eo) || !aligned(row_m, 4) || !aligned(row_l, 4))
     return MHA_ERR_ALIGN;
   const size_t rows = (size_t)d->B * d->h * d->n_q;
   if (!workspace || workspace_bytes < attn_backward_workspace_bytes(d)) return MHA_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return MHA_ERR_ALIGN;
-  mha::AttnBwdParams p;
   memset(&p, 0, sizeof(p));
   p.Q = Qh;
   p.K = Kh;
@@ -452,9 +450,6 @@ mha_status attn_core_backward(const mha_dims* d, const mha_mask* m, const void* 
   p.dZ = dZ;
   p.row_m = row_m;
   p.row_l = row_l;
-  p.dQ = dQh;
-  p.dK = dKh;
-  p.dV = dVh;
   p.lse2 = static_cast<float*>(workspace);
   p.dsum = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(rows * 4));
   p.B = d->B;
@@ -475,12 +470,47 @@ mha_status attn_core_backward(const mha_dims* d, const mha_mask* m, const void* 
   p.vec_k = aligned(Kh, 16) && d->d_h % vin == 0;
   p.vec_v = aligned(Vh, 16) && d->d_vh % vin == 0;
   p.vec_z = aligned(dZ, 16) && aligned(Z, 16) && d->d_vh % vz == 0;
+  return MHA_OK;
+}
+
+mha_status attn_core_backward(const mha_dims* d, const mha_mask* m, const void* Qh,
+                              const void* Kh, const void* Vh, const void* Z, const void* dZ,
+                              const float* row_m, const float* row_l, void* dQh, void* dKh,
+                              void* dVh, void* workspace, size_t workspace_bytes, void* stream) {
+  mha::AttnBwdParams p;
+  mha_status s = core_backward_params(d, m, Qh, Kh, Vh, Z, dZ, row_m, row_l, workspace,
+                                      workspace_bytes, p);
+  if (s != MHA_OK) return s;
+  if (!dQh || !dKh || !dVh) return MHA_ERR_NULL;
+  const size_t eo = esize(d->out_dtype);
+  if (!aligned(dQh, eo) || !aligned(dKh, eo) || !aligned(dVh, eo)) return MHA_ERR_ALIGN;
+  p.dQ = dQh;
+  p.dK = dKh;
+  p.dV = dVh;
   const size_t a4 = 4 * eo;   // four-element stores
   p.vec_dq = aligned(dQh, a4) && d->d_h % 4 == 0;
   p.vec_dk = aligned(dKh, a4) && d->d_h % 4 == 0;
   p.vec_dv = aligned(dVh, a4) && d->d_vh % 4 == 0;
   if (mha::launch_attention_backward(p, d->in_dtype, (hipStream_t)stream) != hipSuccess)
     return MHA_ERR_LAUNCH;
+  return MHA_OK;
+}
+
+mha_status attn_bias_backward(const mha_dims* d, const mha_mask* m, const void* Qh,
+                              const void* Kh, const void* Vh, const void* Z, const void* dZ,
+                              const float* row_m, const float* row_l, float* dM,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  mha::AttnBwdParams p;
+  mha_status s = core_backward_params(d, m, Qh, Kh, Vh, Z, dZ, row_m, row_l, workspace,
+                                      workspace_bytes, p);
+  if (s != MHA_OK) return s;
+  if (!m || !(m->flags & MHA_MASK_ADDITIVE)) return MHA_ERR_MASK;
+  if (!dM) return MHA_ERR_NULL;
+  if (!aligned(dM, 4)) return MHA_ERR_ALIGN;
+  const int shared = (m->add_batch_stride == 0) ? 1 : 0;
+  hipStream_t st = (hipStream_t)stream;
+  if (mha::launch_bwd_row_terms(p, st) != hipSuccess) return MHA_ERR_LAUNCH;
+  if (mha::launch_bias_backward(p, dM, shared, st) != hipSuccess) return MHA_ERR_LAUNCH;
   return MHA_OK;
 }
 
@@ -498,7 +528,6 @@ mha_status mha_backward(const mha_dims* d, const mha_mask* m, const void* Q, con
                         void* stream) {
   mha_status s = check_full_dims(d);
   if (s != MHA_OK) return s;
-  if (d->work_dtype == MHA_F32) return MHA_ERR_DTYPE;
   if ((s = check_mask(d, m)) != MHA_OK) return s;
   if (!Q || !K || !V || !W_Q || !W_K || !W_V || !W_O || !dY || !row_m || !row_l ||
       !fwd_workspace)
@@ -554,7 +583,7 @@ mha_status mha_backward(const mha_dims* d, const mha_mask* m, const void* Q, con
   void* dZ = ws + bw.dz;
   const void* dYp = dY;
   int dydt = od;
-  if (od == MHA_F32) {
+  if (od == MHA_F32 && wd != MHA_F32) {
     if (mha::launch_round_f32(static_cast<const float*>(dY), ws + bw.dy, (size_t)Mq * d->d_o, wd,
                               st) != hipSuccess)
       return MHA_ERR_LAUNCH;

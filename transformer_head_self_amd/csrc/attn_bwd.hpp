@@ -102,7 +102,9 @@ __device__ __forceinline__ void bwd_row_terms(const AttnBwdParams& p, int b, int
   p.lse2[idx] = (l > 0.f && m != -INFINITY) ? fmaf(m, kLog2e, __log2f(l)) : INFINITY;
 }
 
+// x rounded to the heads' element type (fp32 heads: unchanged).
 __device__ __forceinline__ float round_as(float x, int elem_dtype) {
+  if (elem_dtype == kF32) return x;
   return elem_dtype == kBF16 ? (float)(bf16)x : (float)(f16)x;
 }
 

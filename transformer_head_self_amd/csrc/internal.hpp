@@ -165,8 +165,22 @@ struct AttnBwdParams {
   int vec_dq, vec_dk, vec_dv;        // 4-element vector stores allowed
 };
 
-// The three launches of the backward pass on `stream` (2-byte elements).
+// The launches of the backward pass on `stream`: the row terms (lse2,
+// dsum), then dK/dV and dQ (matrix cores for 2-byte heads, the vector ALU
+// for fp32 heads).
 hipError_t launch_attention_backward(const AttnBwdParams& p, int elem_dtype, hipStream_t stream);
+
+// The row terms alone (p.lse2, p.dsum from Z, dZ, row_m, row_l).
+hipError_t launch_bwd_row_terms(const AttnBwdParams& p, hipStream_t stream);
+
+// dK/dV and dQ on the vector ALU (any element type; row terms already formed).
+hipError_t launch_attention_backward_scalar(const AttnBwdParams& p, hipStream_t stream);
+
+// dM [Bo, n_q, n_k] (fp32; Bo = 1 when shared_bias, else B): the gradient
+// with respect to the additive bias p.add, summed over heads (and items when
+// shared); row terms already formed.
+hipError_t launch_bias_backward(const AttnBwdParams& p, float* dM, int shared_bias,
+                                hipStream_t stream);
 
 // Largest head widths with an instantiated kernel.
 constexpr int kMaxHeadDim = 128;

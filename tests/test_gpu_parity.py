@@ -290,6 +290,39 @@ BOOL_FAST_CASES = [
 ]
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bool_mask_block_sparse(dt, causal):
+    """A banded boolean mask with sink keys (|i - j| < 96 or j < 16) on the
+    mask-tile path: far from the band a wave's 32 x 64 window of the tile is
+    all forbidden (the wave skips the block), inside the band it is all
+    allowed (no per-score test), at its edges mixed; rows past a 64-key block
+    boundary, a query tail, row statistics checked too."""
+    B, h, n, d = 2, 3, 720, 64
+    _say(f"[bool block-sparse] {dt} causal={causal}")
+    Qh, Kh, Vh = make_heads(B, h, n, n, d, d, "f32" if dt == "f16" else dt, seed=63)
+    dev, host = _heads_dev(Qh, Kh, Vh, dt)
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    G = ((np.abs(i - j) < 96) | (j < 16))[None].repeat(B, axis=0)
+    G[1, :, 16:32] = False                    # the second item: other sinks
+    G[1, :, 700:] = True
+    allow = allowed_set(B, n, n, causal=causal, allowed=G)
+    c = 1.0 / math.sqrt(d)
+    ref = attn_core_ref(*host, c, allow)
+    rm = torch.empty((B, h, n), device=DEV)
+    rl = torch.empty_like(rm)
+    Z = mha.attn_core(*dev, scale=c, causal=causal, allowed=torch.from_numpy(G).to(DEV),
+                      row_m=rm, row_l=rl)
+    torch.cuda.synchronize()
+    err = _rel_err(Z.cpu().numpy(), ref["Z"])
+    bar = SPLIT_TOL[dt] if dt != "f16" else core_bar(*host, c, allow, ref["Z"])
+    _say(f"  Z err {err:.3e} (bar {bar:.2e})")
+    assert err <= bar
+    np.testing.assert_allclose(rm.cpu().numpy(), ref["m"], rtol=1e-3, atol=1e-3)
+    np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-2)
+
+
 @pytest.mark.parametrize("row_stats", [True, False])
 @pytest.mark.parametrize("case", BOOL_FAST_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_bool_mask_direct_load_path(case, row_stats):

@@ -507,32 +507,49 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
     const int k0 = blk * BN;
     // A wave whose rows all precede this block's first key (causal) sees an
     // empty key set here: its summary is the empty state, a no-op merge.
-    const bool active = (qw < p.n_q) && !(p.causal && k0 > qw + 31);
-    if (active) {
-      // General path with aligned mask rows: this block's boolean / additive
-      // mask entries for this lane's keys, four consecutive keys per load
-      // (the keys k0 + 32 kb + 8 a + 4 g + j, j < 4, of score slots
-      // (kb, 4 a + j)), issued before the score products so that their
-      // latency runs under them.  Rows past n_q read nothing (forbidden,
-      // zero bias); groups lie wholly inside or past n_k (n_k % 4 == 0).
-      uint32_t gmv[GEN ? NKB : 1][4];
-      floatx4 amv[GEN ? NKB : 1][4];
-      const bool mvec = GEN && (MLDS || p.mask_vec);
-      if constexpr (MLDS) {
+    bool active = (qw < p.n_q) && !(p.causal && k0 > qw + 31);
+    // General path with aligned mask rows: this block's boolean / additive
+    // mask entries for this lane's keys, four consecutive keys per load
+    // (the keys k0 + 32 kb + 8 a + 4 g + j, j < 4, of score slots
+    // (kb, 4 a + j)), issued before the score products so that their
+    // latency runs under them.  Rows past n_q read nothing (forbidden,
+    // zero bias); groups lie wholly inside or past n_k (n_k % 4 == 0).
+    uint32_t gmv[GEN ? NKB : 1][4];
+    floatx4 amv[GEN ? NKB : 1][4];
+    // MLDS: the wave's 32 x 64 window of the boolean tile decides the block
+    // for the whole wave: no allowed entry -> nothing to add (the empty
+    // summary, as for an inactive wave); every entry allowed -> the mask step
+    // keeps only the causal / padding thresholds (no per-score byte test).
+    bool tile_full = false;
+    if constexpr (MLDS) {
+      if (active) {
         // this lane's row of the block's mask tile: dword (kb, a) holds keys
         // k0 + 32 kb + 8 a + 4 g .. + 3, in chunk 2 kb + a / 2 of the row
         const int mr = wave * 32 + l32, sw = (mr >> 2) & 3;
         unsigned mb = lds_base + (unsigned)(C::DMA_LDS + (blk % C::NS) * MT);
         asm("" : "+s"(mb));
+        uint32_t has_zero = 0u, any_set = 0u;
         #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           #pragma unroll
           for (int a = 0; a < 4; ++a) {
             const int c = 2 * kb + (a >> 1);
-            gmv[kb][a] = lds_load_at<uint32_t>(mb + (unsigned)(mr * 64 + ((c ^ sw) * 16) +
-                                                               8 * (a & 1) + 4 * g));
+            const uint32_t x = lds_load_at<uint32_t>(mb + (unsigned)(mr * 64 + ((c ^ sw) * 16) +
+                                                                     8 * (a & 1) + 4 * g));
+            gmv[kb][a] = x;
             amv[kb][a] = floatx4{0.f, 0.f, 0.f, 0.f};
+            has_zero |= (x - 0x01010101u) & ~x & 0x80808080u;   // nonzero iff a byte is 0
+            any_set |= x;
           }
+        // rows past n_q hold a copy of row n_q - 1 (never stored): harmless
+        // either way
+        if (__all(any_set == 0u)) active = false;
+        tile_full = __all(has_zero == 0u);
+      }
+    }
+    if (active) {
+      const bool mvec = GEN && (MLDS || p.mask_vec);
+      if constexpr (MLDS) {
       } else if constexpr (GEN) {
         if (mvec) {
           #pragma unroll
@@ -603,12 +620,13 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       // the keys j <= lim = min(qi, kvalid - 1): one compare per score.
       // causal / padding thresholds bite only on boundary blocks
       const bool need_cp = (k0 + BN > kvalid) || (p.causal && k0 + BN - 1 > qw);
-      const bool need_mask = need_cp || (GEN && (Gb != nullptr || Ab != nullptr));
+      const bool need_mask =
+          need_cp || (GEN && ((Gb != nullptr && !tile_full) || Ab != nullptr));
       auto apply_mask = [&]() {
         const int lim = p.causal ? min(qi, kvalid - 1) : kvalid - 1;
         const int t = lim - k0 - 4 * g;
         if constexpr (GEN) {
-          if (mvec) {
+          if (mvec && !tile_full) {
             auto grouped = [&](auto cp) {
               constexpr bool CP = decltype(cp)::value;   // threshold compare needed
               #pragma unroll
@@ -637,7 +655,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
           for (int i = 0; i < 16; ++i) {
             const int off = kb * 32 + 8 * (i >> 2) + (i & 3);
             bool ok = off <= t;
-            if (GEN && Gb != nullptr && ok)
+            if (GEN && Gb != nullptr && !tile_full && ok)
               ok = qi < p.n_q && Gb[(size_t)qi * p.n_k + k0 + off + 4 * g] != 0;
             if (GEN && Ab != nullptr) {
               // an allowed key has index <= lim < n_k, and qi < n_q is checked

@@ -54,6 +54,23 @@ def test_model_without_rounding_is_the_definition(causal):
     assert RM.rel_err(Ze, ref) < 1e-12
 
 
+def test_model_without_rounding_masked_rows_start_late():
+    """A boolean mask whose rows 300-339 allow nothing before key 204 (their
+    first blocks empty: the deferred shift stays unset until the redo of the
+    first block with an allowed key) and a band with sink keys: without
+    rounding the deferred-shift model is the definition."""
+    n, d = 720, 64
+    Qh, Kh, Vh = (RM.rnd16(x) for x in make_heads(1, 2, n, n, d, d, "f32", seed=94))
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    G = ((np.abs(i - j) < 96) | (j < 16))[None]
+    G[:, 300:340, :200] = False
+    allow = allowed_set(1, n, n, causal=True, allowed=G)
+    ref = attn_core_ref(Qh, Kh, Vh, 1 / math.sqrt(d), allow)["Z"]
+    Zd = RM.attn_core_f16_model(Qh, Kh, Vh, 1 / math.sqrt(d), allow, exact=True)
+    assert RM.rel_err(Zd, ref) < 1e-12
+
+
 def test_single_allowed_key_is_its_value_rounded_once():
     Qh, Kh, Vh = make_heads(1, 1, 3, 3, 16, 16, "f32", seed=92)
     Qh, Kh, Vh = RM.rnd16(Qh), RM.rnd16(Kh), RM.rnd16(Vh)

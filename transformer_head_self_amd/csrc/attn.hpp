@@ -162,7 +162,9 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   typedef AttnCfg<T, DH, DV, WAVES, BN_> C;
   static_assert(!(SPLIT && LAZY), "a key partition may hold no allowed key for a row");
   static_assert(STATS || (LAZY && C::TR), "the block-sum trigger is for 2-byte elements");
-  static_assert(!(MASKED && (LAZY || !FAST)), "masked fast variant: exact-shift merge");
+  static_assert(!(MASKED && !FAST) && !(MASKED == 1 && LAZY),
+                "masked fast variants: exact-shift merge, or the deferred shift with the "
+                "boolean tile in LDS");
   // GEN: boolean / additive masks are read (the general variant, or the
   // fast variant with masks whose rows hold aligned groups of four keys)
   constexpr bool GEN = !FAST || MASKED != 0;
@@ -284,8 +286,11 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   float l_run = 0.f;        // this half-wave's part of the running normaliser
   float mu = -INFINITY;     // LAZY: reference shift (l_run, o are kept at mu)
   floatx16 negmu;           // LAZY: -mu in every slot, the score MFMA's C input
+  // Masked deferred shift: a row whose blocks so far held no allowed key keeps
+  // mu = -inf (negmu = +inf), so its first allowed score comes out +inf and
+  // sends that block down the exact redo, which sets mu.
   #pragma unroll
-  for (int i = 0; i < 16; ++i) negmu[i] = 0.f;
+  for (int i = 0; i < 16; ++i) negmu[i] = MASKED ? INFINITY : 0.f;
 
   // ---- staging of K/V blocks: global -> registers -> LDS ----------------------
   // Thread chunk t of a block covers tile row krow[t] / vrow[t] (a key) and
@@ -687,15 +692,17 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
 
       if constexpr (LAZY && !STATS) {
         if (!shifted) {
-          // first block: the exact block maximum becomes mu
+          // first block: the exact block maximum becomes mu (masked: -inf
+          // stays -inf, see negmu)
           const float mx = block_max();
-          mu = (mx == -INFINITY) ? 0.f : mx;
+          const float mu_use = (mx == -INFINITY) ? 0.f : mx;
+          mu = MASKED ? mx : mu_use;
           #pragma unroll
           for (int i = 0; i < 16; ++i) negmu[i] = -mu;
           #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
             #pragma unroll
-            for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(s[kb][i] - mu);
+            for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(s[kb][i] - mu_use);
         } else {
           #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
@@ -787,7 +794,10 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
             if (need_mask) apply_mask();
             const float mx = block_max();
             const float mu_new = fmaxf(mu, mx);
-            rescale(__builtin_amdgcn_exp2f(mu - mu_new));
+            // masked rows may still have no allowed key (mu_new = -inf):
+            // nothing to rescale, weights 0
+            const float mu_use = (MASKED && mu_new == -INFINITY) ? 0.f : mu_new;
+            rescale((MASKED && mu_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mu - mu_new));
             mu = mu_new;
             #pragma unroll
             for (int i = 0; i < 16; ++i) negmu[i] = -mu;
@@ -799,7 +809,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
                 floatx8 pf;
                 #pragma unroll
                 for (int t = 0; t < 8; ++t)
-                  pf[t] = __builtin_amdgcn_exp2f(s[kb][8 * st + t] - mu);
+                  pf[t] = __builtin_amdgcn_exp2f(s[kb][8 * st + t] - mu_use);
                 pb[kb][st] = Cvt<T>::eight(pf);
                 bsum = sum8(pb[kb][st], bsum);
               }

@@ -66,13 +66,16 @@ def _ident(x):
 
 
 def attn_core_f16_model(Qh, Kh, Vh, scale, allow, out_dtype="f16", block=64, tau=8.0,
-                        exact=False):
+                        exact=False, add=None):
     """Z [B, n_q, h*d_vh] of the fp16 attention core under the modelled roundings.
 
     Qh, Kh, Vh: head tensors holding fp16 values; allow [B, n_q, n_k].  A row
     with no allowed key in the first block (a boolean mask) keeps mu = -inf
     until its first block with an allowed key, which then takes the redo
     path (mu = that block's exact maximum), as the masked kernel does.
+    `add`: an optional additive score bias M [B or 1, n_q, n_k] (natural-log
+    units, -inf forbids a key), added in fp32 to the base-2 score as
+    M log2(e) (modelled exactly).
     exact=True turns every rounding off (then the model is the plain
     definition in another order of operations, used to pin the model's
     bookkeeping against the oracle).
@@ -88,14 +91,19 @@ def attn_core_f16_model(Qh, Kh, Vh, scale, allow, out_dtype="f16", block=64, tau
         sl = float(np.float32(scale) * np.float32(LOG2E))
     Z = np.empty((B, n_q, h * d_vh))
     nblk = (n_k + block - 1) // block
+    M = None if add is None else np.broadcast_to(np.asarray(add, np.float64), (B, n_q, n_k))
     for b in range(B):
         A = np.asarray(allow[b], bool)
+        if M is not None:
+            A = A & (M[b] > -np.inf)
         for r in range(h):
             if exact:
                 q = Qh[b, r] * sl
             else:
                 q = rnd16((Qh[b, r].astype(np.float32) * np.float32(sl)).astype(np.float64))
             S = q @ Kh[b, r].T                          # base-2 units
+            if M is not None:
+                S = S + np.where(A, M[b], 0.0) * LOG2E
             S = np.where(A, S, -np.inf)
             mu = S[:, :block].max(axis=1)           # -inf: no allowed key yet
             l = np.zeros(n_q)
@@ -187,12 +195,12 @@ def core_bar(Qh, Kh, Vh, scale, allow, ref_Z, elem="f16", out_dtype="f32", floor
              add=None):
     """Twice the larger error (against the oracle's ref_Z) of the forms the
     library may run for these heads: the exact-shift form, and for fp16
-    heads without an additive bias also the deferred shift; never below
-    `floor`."""
+    heads also the deferred shift; never below `floor`."""
     errs = [rel_err(attn_core_exact_shift_model(Qh, Kh, Vh, scale, allow, elem, out_dtype,
                                                 add=add), ref_Z)]
-    if elem == "f16" and scale > 0 and add is None:
-        errs.append(rel_err(attn_core_f16_model(Qh, Kh, Vh, scale, allow, out_dtype), ref_Z))
+    if elem == "f16" and scale > 0:
+        errs.append(rel_err(attn_core_f16_model(Qh, Kh, Vh, scale, allow, out_dtype, add=add),
+                            ref_Z))
     return max(2.0 * max(errs), floor)
 
 

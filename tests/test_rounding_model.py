@@ -71,6 +71,24 @@ def test_model_without_rounding_masked_rows_start_late():
     assert RM.rel_err(Zd, ref) < 1e-12
 
 
+def test_model_without_rounding_additive_bias():
+    """With an additive bias (N(0, 4) entries, a tenth of them -inf, rows
+    300-339 without an allowed key before 200) both models without rounding
+    are the definition."""
+    n, d = 600, 64
+    Qh, Kh, Vh = (RM.rnd16(x) for x in make_heads(1, 2, n, n, d, d, "f32", seed=95))
+    rng = np.random.default_rng(96)
+    M = rng.normal(size=(1, n, n)) * 2.0
+    M[rng.random(M.shape) < 0.1] = -np.inf
+    M[:, 300:340, :200] = -np.inf
+    allow = allowed_set(1, n, n, causal=True)
+    ref = attn_core_ref(Qh, Kh, Vh, 1 / math.sqrt(d), allow, add=M)["Z"]
+    Zd = RM.attn_core_f16_model(Qh, Kh, Vh, 1 / math.sqrt(d), allow, exact=True, add=M)
+    Ze = RM.attn_core_exact_shift_model(Qh, Kh, Vh, 1 / math.sqrt(d), allow, exact=True, add=M)
+    assert RM.rel_err(Zd, ref) < 1e-12
+    assert RM.rel_err(Ze, ref) < 1e-12
+
+
 def test_single_allowed_key_is_its_value_rounded_once():
     Qh, Kh, Vh = make_heads(1, 1, 3, 3, 16, 16, "f32", seed=92)
     Qh, Kh, Vh = RM.rnd16(Qh), RM.rnd16(Kh), RM.rnd16(Vh)

@@ -164,7 +164,12 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   static_assert(STATS || (LAZY && C::TR), "the block-sum trigger is for 2-byte elements");
   static_assert(!(MASKED && !FAST) && !(MASKED == 1 && LAZY),
                 "masked fast variants: exact-shift merge, or the deferred shift with the "
-                "boolean tile in LDS");
+                "boolean tile or the bias tile in LDS");
+  // MASKED == 3: an additive bias and no boolean mask (its tile staged in LDS
+  // as for MASKED == 1): the mask step is one fused multiply-add per score
+  // (a forbidden entry, M = -inf, gives -inf by itself) plus the causal /
+  // padding threshold on boundary blocks.
+  constexpr bool ADDONLY = MASKED == 3;
   // GEN: boolean / additive masks are read (the general variant, or the
   // fast variant with masks whose rows hold aligned groups of four keys)
   constexpr bool GEN = !FAST || MASKED != 0;
@@ -184,7 +189,16 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   constexpr int MT = MLDS ? C::QT * BN : 0;
   constexpr int M_WIN = MT / 1024 / WAVES;
   static_assert(M_WIN * 1024 * WAVES == MT, "whole 1 KB mask windows per wave");
-  constexpr int LDS_BYTES = DMA ? C::DMA_LDS + C::NS * MT : C::REG_LDS;
+  // ALDS (MASKED == 1 on the direct-load path): an additive bias tile (QT
+  // rows x BN fp32 keys, 32 KB at 64 keys) moves by direct loads into one LDS
+  // buffer, each wave its own 32 rows, one block ahead: block blk + 1's rows
+  // are issued at the top of block blk (before the K/V loads of block
+  // blk + 2) into the buffer the wave has just read block blk's rows from.
+  constexpr bool ALDS = (MASKED == 1 || MASKED == 3) && DMA;
+  constexpr int AT = ALDS ? C::QT * BN * 4 : 0;
+  constexpr int A_WIN = AT / 1024 / WAVES;
+  static_assert(!ALDS || A_WIN * 1024 * WAVES == AT, "whole 1 KB bias windows per wave");
+  constexpr int LDS_BYTES = DMA ? C::DMA_LDS + C::NS * MT + AT : C::REG_LDS;
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   T* Ks = reinterpret_cast<T*>(smem);
   T* Vs = Ks + 2 * C::KBUF;
@@ -409,6 +423,43 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       mchk[q] = (unsigned)((slot ^ ((row >> 2) & 3)) * 16);
     }
   }
+  // Bias tile windows (ALDS): window q of wave w holds rows 32 w + 4 q +
+  // lane / 16 of the tile, 256 bytes each; lane i fills 16 bytes (slot
+  // i % 16) from the row's chunk (i % 16) ^ (row % 16) -- 4 fp32 keys -- so
+  // that the reads (16 rows at one chunk per phase) meet distinct bank
+  // groups.  With every row of the tile below n_q and every key of the block
+  // below n_k, window q's byte offset is 4 (row0 + 4 q) n_k + 4 k0 +
+  // 16 (c0 ^ 4 (q % 4)), row0 = q0 + 32 w + lane / 16, c0 = (lane % 16) ^
+  // (lane / 16): four per-lane values (abase), the rest scalar.  Otherwise
+  // rows past n_q read row n_q - 1 and keys past n_k the last four
+  // (n_k % 4 == 0): never used.
+  unsigned abase[ALDS ? 4 : 1];
+  if constexpr (ALDS) {
+    const unsigned row0 = (unsigned)(q0 + wave * 32 + (lane >> 4));
+    const unsigned c0 = (unsigned)((lane & 15) ^ (lane >> 4));
+    #pragma unroll
+    for (int j = 0; j < 4; ++j) abase[j] = 4u * row0 * (unsigned)p.n_k + 16u * (c0 ^ (4u * j));
+  }
+  const unsigned a_lds = lds_base + (unsigned)(C::DMA_LDS + C::NS * MT) + wave * A_WIN * 1024;
+  auto issue_bias = [&](int blk) {
+    if constexpr (ALDS) {
+      const int k0 = blk * BN;
+      if (q0 + C::QT <= p.n_q && k0 + BN <= p.n_k) {
+        #pragma unroll
+        for (int q = 0; q < A_WIN; ++q)
+          lds_dma16(Ab + (size_t)k0 + (size_t)(4 * q) * p.n_k, abase[q & 3], a_lds + q * 1024);
+      } else {
+        #pragma unroll
+        for (int q = 0; q < A_WIN; ++q) {
+          const int row = wave * 32 + 4 * q + (lane >> 4);
+          const int chunk = (lane & 15) ^ (row & 15);
+          const unsigned off = 4u * ((unsigned)min(q0 + row, p.n_q - 1) * (unsigned)p.n_k +
+                                     (unsigned)min(k0 + 4 * chunk, p.n_k - 4));
+          lds_dma16(Ab, off, a_lds + q * 1024);
+        }
+      }
+    }
+  };
   // block blk into stage blk % 3; in the last block, rows past n_k read the
   // last key (masked out, weight 0)
   auto issue_kv = [&](int blk) {
@@ -466,6 +517,9 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   }
 
   if constexpr (DMA) {
+    if constexpr (ALDS) {
+      if (Ab != nullptr && nblk > blk0) issue_bias(blk0);
+    }
     if (nblk > blk0) issue_kv(blk0);
     if (nblk > blk0 + 1) issue_kv(blk0 + 1);
   } else {
@@ -478,13 +532,36 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   }
 
   for (int blk = blk0; blk < nblk; ++blk) {
+    floatx4 amv[GEN ? NKB : 1][4];
     if constexpr (DMA) {
       // block blk has landed once only block blk+1's loads are outstanding;
       // after the barrier no wave reads block blk-1, whose stage is refilled
       if (blk + 1 < nblk) wait_vm_lds<C::K_WIN + C::V_WIN + M_WIN>();
       else wait_vm_lds<0>();
+      compiler_fence();
+      if constexpr (ALDS) {
+        if (Ab != nullptr) {
+          // this block's bias rows of this wave (issued one block ago, older
+          // than the K/V loads of block blk + 1 that may still be in
+          // flight): dword group (kb, a) is chunk 8 kb + 2 a + g of row
+          // 32 w + l32, in slot chunk ^ (row % 16)
+          const unsigned ab = a_lds + (unsigned)(l32 * 256);
+          #pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            #pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const int c = 8 * kb + 2 * a + g;
+              amv[kb][a] = lds_load_at<floatx4>(ab + (unsigned)((c ^ (l32 & 15)) * 16));
+            }
+          // the wave's reads of its rows complete before it refills them
+          asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+        }
+      }
       __builtin_amdgcn_s_barrier();
       compiler_fence();
+      if constexpr (ALDS) {
+        if (Ab != nullptr && blk + 1 < nblk) issue_bias(blk + 1);
+      }
       if (blk + 2 < nblk) issue_kv(blk + 2);
     }
     const int cur = (blk - blk0) & 1;   // register staging: buffer of this block
@@ -519,8 +596,8 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
     // (kb, 4 a + j)), issued before the score products so that their
     // latency runs under them.  Rows past n_q read nothing (forbidden,
     // zero bias); groups lie wholly inside or past n_k (n_k % 4 == 0).
+    // (ALDS: the bias entries were read from LDS at the top of the block.)
     uint32_t gmv[GEN ? NKB : 1][4];
-    floatx4 amv[GEN ? NKB : 1][4];
     // MLDS: the wave's 32 x 64 window of the boolean tile decides the block
     // for the whole wave: no allowed entry -> nothing to add (the empty
     // summary, as for an inactive wave); every entry allowed -> the mask step
@@ -565,9 +642,10 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
               const bool in = qi < p.n_q && key < p.n_k;
               const size_t at = (size_t)qi * p.n_k + key;
               gmv[kb][a] = 0xffffffffu;
-              amv[kb][a] = floatx4{0.f, 0.f, 0.f, 0.f};
+              if (!ALDS) amv[kb][a] = floatx4{0.f, 0.f, 0.f, 0.f};
               if (Gb != nullptr) gmv[kb][a] = in ? *reinterpret_cast<const uint32_t*>(Gb + at) : 0u;
-              if (Ab != nullptr && in) amv[kb][a] = *reinterpret_cast<const floatx4*>(Ab + at);
+              if (!ALDS && Ab != nullptr && in)
+                amv[kb][a] = *reinterpret_cast<const floatx4*>(Ab + at);
             }
         }
       }
@@ -603,7 +681,10 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       // (not in eight-wave workgroups with value rows of 96+ and heads of 128
       // or the exact-shift merge: there the fragments do not fit the
       // registers of two waves per SIMD)
-      constexpr bool VPRE = DMA && !(WAVES >= 8 && C::NDV > 2 && (DH >= 128 || !LAZY));
+      // (nor with a staged bias tile and the exact-shift merge: the bias
+      // entries hold those registers)
+      constexpr bool VPRE = DMA && !(ALDS && !(ADDONLY && LAZY)) &&
+                            !(WAVES >= 8 && C::NDV > 2 && (DH >= 128 || !LAZY));
       vec vpre[VPRE ? NKB : 1][2][VPRE ? C::NDV : 1];
       if constexpr (VPRE) {
         #pragma unroll
@@ -630,6 +711,27 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       auto apply_mask = [&]() {
         const int lim = p.causal ? min(qi, kvalid - 1) : kvalid - 1;
         const int t = lim - k0 - 4 * g;
+        if constexpr (ADDONLY) {
+          // s' = s c' + M log2(e) (prescaled scores: c' = 1); -inf stays -inf
+          auto add_bias = [&](auto cp) {
+            constexpr bool CP = decltype(cp)::value;
+            #pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+              #pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int a = i >> 2, j = i & 3;
+                const int off = kb * 32 + 8 * a + j;
+                const float v = PRESCALE ? fmaf(amv[kb][a][j], kLog2e, s[kb][i])
+                                         : fmaf(s[kb][i], cs0, amv[kb][a][j] * kLog2e);
+                s[kb][i] = (!CP || off <= t) ? v : -INFINITY;
+              }
+          };
+          if (need_cp)
+            add_bias(std::true_type());
+          else
+            add_bias(std::false_type());
+          return;
+        }
         if constexpr (GEN) {
           if (mvec && !tile_full) {
             auto grouped = [&](auto cp) {

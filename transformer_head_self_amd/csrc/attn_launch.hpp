@@ -61,7 +61,15 @@ hipError_t launch_attn_fixed(AttnParams p, hipStream_t stream) {
       constexpr int occm = (DH <= 64 && DV <= 64) ? 2 : 1;
       // a boolean mask alone with 16-byte aligned rows travels into LDS with
       // the K/V tiles; otherwise each lane loads its mask entries
-      if (p.allowed != nullptr && p.add == nullptr && p.mask_g16 && lazy && !stats)
+      // an additive bias alone: the one-FMA mask step, with the deferred
+      // shift when no row statistics are requested
+      if (p.allowed == nullptr && p.add != nullptr && lazy && !stats)
+        hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, true, occm, false, false, 3>),
+                           dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
+      else if (p.allowed == nullptr && p.add != nullptr)
+        hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, false, occm, true, false, 3>),
+                           dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
+      else if (p.allowed != nullptr && p.add == nullptr && p.mask_g16 && lazy && !stats)
         hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, true, occm, false, false, 2>),
                            dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
       else if (p.allowed != nullptr && p.add == nullptr && p.mask_g16)

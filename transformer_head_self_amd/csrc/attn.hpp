@@ -156,6 +156,13 @@ static_assert(kLazyLimit == (float)(1 << (int)kLazyTau), "limit = 2^tau");
 // SPLIT: one key partition per workgroup; partial summaries are written
 // (p.part_m / part_l / part_z) instead of Z.  Uses the exact-shift merge: a
 // partition may hold no allowed key for some rows (empty state).
+// MASKED (direct-load path, p.mask_vec): 1 = boolean mask and / or additive
+// bias read per lane, exact shift; 2 = boolean mask whose tile moves into
+// LDS with the K/V tiles; 3 = additive bias alone, its tile moved into LDS
+// one block ahead.  2 and 3 may run the deferred shift (no row statistics):
+// a row with no allowed key yet keeps mu = -inf, and its first allowed
+// block is redone at an exact shift (the +inf scores trip the block-sum
+// trigger).
 template <typename T, int DH, int DV, int WAVES, int BN_, bool FAST, bool LAZY = false, int OCC = 1,
           bool STATS = true, bool SPLIT = false, int MASKED = 0>
 __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p) {

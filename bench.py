@@ -369,7 +369,7 @@ def backward_bench(args, torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: this benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding plan is design-only)", file=sys.stderr)
         sys.exit(2)
 

@@ -28,7 +28,7 @@ What it computes, and from which passage
   b_K [h*d_h], b_V [h*d_vh], b_O [d_o]) each product X W becomes X W + b,
   the bias broadcast over rows, head r's block in entries r*d .. r*d+d-1.
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
 * masks are allowed sets (additive M in {0, -inf}); combined rules AND;
 * an additive score bias M may also be a general real matrix [B or 1, n_q,
   n_k], added to the scaled scores c q.k (the review page's

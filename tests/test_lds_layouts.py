@@ -189,6 +189,69 @@ def test_forward_mask_tile():
             assert bank_degree(flat, 4) == 8
 
 
+
+def bias_fast_offsets(q0, wave, n_k, k0):
+    """Byte offsets of the bias-tile direct loads on the fast path (every
+    row of the tile below n_q, every key of the block below n_k): window q
+    of lane i is 4 (row0 + 4 q) n_k + 4 k0 + 16 (c0 ^ 4 (q mod 4)),
+    row0 = q0 + 32 wave + i / 16, c0 = (i mod 16) ^ (i / 16)."""
+    out = {}
+    for q in range(8):
+        for lane in range(64):
+            row0 = q0 + 32 * wave + lane // 16
+            c0 = (lane % 16) ^ (lane // 16)
+            out[q, lane] = 4 * (row0 + 4 * q) * n_k + 4 * k0 + 16 * (c0 ^ (4 * (q % 4)))
+    return out
+
+
+@pytest.mark.parametrize("n_k,k0,q0", [(64, 0, 0), (4096, 1984, 3968), (192, 64, 128)])
+def test_forward_bias_tile(n_k, k0, q0):
+    """Additive bias tile: 128 query rows x 64 fp32 keys (256 bytes a row)
+    per block, each wave its own 32 rows in eight 1 KB windows.  Window q of
+    wave w holds rows 32 w + 4 q + i / 16; lane i fills slot i mod 16 of its
+    row from the row's chunk (i mod 16) ^ (row mod 16) (four keys).  The
+    mask step's lane (l32, g) reads row 32 w + l32, chunk 8 kb + 2 a + g at
+    slot chunk ^ (l32 mod 16): keys 32 kb + 8 a + 4 g .. + 3."""
+    rows, rb = 128, 256
+    swz = lambda r: r % 16
+    check_bijection(rb, swz, rows)
+    for wave in range(4):
+        fast = bias_fast_offsets(q0, wave, n_k, k0)
+        # the tile as the windows write it: byte t of window q of this wave
+        # holds global byte fast[q, t / 16] + t mod 16 of the bias matrix
+        lds = np.full(32 * rb, -1, np.int64)
+        for q in range(8):
+            for lane in range(64):
+                row = 32 * wave + 4 * q + lane // 16
+                chunk = (lane % 16) ^ (row % 16)
+                # the direct (clamped-path) form of the same offset
+                direct = 4 * ((q0 + row) * n_k + k0 + 4 * chunk)
+                assert fast[q, lane] == direct
+                t = q * 1024 + 16 * lane
+                assert t // rb == row - 32 * wave and (t % rb) // 16 == lane % 16
+                lds[t:t + 16] = direct + np.arange(16)
+        assert (lds >= 0).all()
+        want_rows = 4 * (q0 + 32 * wave + np.arange(32))[:, None] * n_k + 4 * k0
+        want = (want_rows + np.arange(rb)[None, :]).ravel()
+        assert np.array_equal(np.sort(lds), np.sort(want)), "tile bytes lost or duplicated"
+        for kb, a in itertools.product(range(2), range(4)):
+            addrs = []
+            for lane in range(64):
+                l32, g = lane % 32, lane // 32
+                c = 8 * kb + 2 * a + g
+                addr = l32 * rb + (c ^ (l32 % 16)) * 16
+                key = 32 * kb + 8 * a + 4 * g
+                row = q0 + 32 * wave + l32
+                assert np.array_equal(lds[addr:addr + 16],
+                                      4 * (row * n_k + k0 + key) + np.arange(16))
+                addrs.append(addr)
+            # 16 rows at one chunk per phase: distinct 16-byte bank groups
+            # (unpermuted, all 16 lanes would meet one group)
+            assert bank_degree(addrs, 16) == 1
+            flat = [(lane % 32) * rb + (8 * kb + 2 * a + lane // 32) * 16 for lane in range(64)]
+            assert bank_degree(flat, 16) == 16
+
+
 # ---------------------------------------------------------------------------
 # attention backward (direct-load stages read both row-wise and transposed)
 # ---------------------------------------------------------------------------

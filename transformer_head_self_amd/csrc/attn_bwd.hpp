@@ -323,17 +323,33 @@ void attn_bwd_kv_kernel(AttnBwdParams p) {
       // A and dS; query of slot i: q0 + 32 sb + 8 (i/4) + 4 g + i%4
       const bool need_mask = (p.causal && qs0 < k0w + 31) || (k0w + 31 >= kvalid) ||
                              (qs0 + 31 >= p.n_q) || G != nullptr || M != nullptr;
+      // exponent of each weight; a forbidden score's becomes -inf (weight
+      // exactly 0) without a branch per score
+      if (need_mask) {
+        #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ql = 32 * sb + 8 * (i >> 2) + 4 * g + (i & 3);
+          const int q = q0 + ql;
+          const bool ok = bwd_allowed(p, G, q, key, kvalid);
+          float x;
+          if (M != nullptr) {
+            x = sacc[i] * cs;
+            if (ok) x = fmaf(M[(size_t)q * p.n_k + key], kLog2e, x);
+            x -= Ls[cur][ql];
+          } else {
+            x = fmaf(sacc[i], cs, -Ls[cur][ql]);
+          }
+          sacc[i] = ok ? x : -INFINITY;
+        }
+      } else {
+        #pragma unroll
+        for (int i = 0; i < 16; ++i)
+          sacc[i] = fmaf(sacc[i], cs, -Ls[cur][32 * sb + 8 * (i >> 2) + 4 * g + (i & 3)]);
+      }
       #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int ql = 32 * sb + 8 * (i >> 2) + 4 * g + (i & 3);
-        const int q = q0 + ql;
-        float x = sacc[i] * cs;
-        bool ok = true;
-        if (need_mask) {
-          ok = bwd_allowed(p, G, q, key, kvalid);
-          if (M != nullptr && ok) x = fmaf(M[(size_t)q * p.n_k + key], kLog2e, x);
-        }
-        const float a = ok ? __builtin_amdgcn_exp2f(x - Ls[cur][ql]) : 0.f;
+        const float a = __builtin_amdgcn_exp2f(sacc[i]);
         sacc[i] = a;
         dpacc[i] = a * (dpacc[i] - Ds[cur][ql]);
       }
@@ -459,8 +475,8 @@ void attn_bwd_kv_dma_kernel(AttnBwdParams p) {
   const T* Kb = reinterpret_cast<const T*>(p.K) + (size_t)bh * p.n_k * DH;
   const T* Vb = reinterpret_cast<const T*>(p.V) + (size_t)bh * p.n_k * DV;
   const T* Zb = reinterpret_cast<const T*>(p.dZ) + (size_t)b * p.n_q * p.ldz + (size_t)r * DV;
-  const uint8_t* G = p.allowed ? p.allowed + (size_t)b * p.allowed_batch_stride : nullptr;
-  const float* M = p.add ? p.add + (size_t)b * p.add_batch_stride : nullptr;
+  // causal / key-padding masks only (the host launches this kernel without a
+  // boolean mask or additive bias)
   const float* lse = p.lse2 + (size_t)bh * p.n_q;
   const float* dsm = p.dsum + (size_t)bh * p.n_q;
 
@@ -473,6 +489,13 @@ void attn_bwd_kv_dma_kernel(AttnBwdParams p) {
   for (int c = 0; c < C::VCH; ++c)
     vf[c] = key < p.n_k ? *reinterpret_cast<const vec*>(Vb + (size_t)key * DV + 16 * c + 8 * g)
                         : zero_vec<vec>();
+  // the loop's waits count only the direct loads: the compiler's wait for
+  // these rows is taken here, once, not before every product in the loop
+  // (where a full vmcnt wait would also drain the tiles loaded ahead)
+  #pragma unroll
+  for (int c = 0; c < C::KCH; ++c) asm volatile("" : "+v"(kf[c]));
+  #pragma unroll
+  for (int c = 0; c < C::VCH; ++c) asm volatile("" : "+v"(vf[c]));
 
   floatx16 dk[C::NDH], dv[C::NDV];
   #pragma unroll
@@ -635,17 +658,23 @@ void attn_bwd_kv_dma_kernel(AttnBwdParams p) {
         dq[a] = lds_load_at<floatx4>(a_addr + 1024 + 4 * (8 * a + 32 * sb));
       }
       const bool need_mask = (p.causal && qs0 < k0w + 31) || (k0w + 31 >= kvalid) ||
-                             (qs0 + 31 >= p.n_q) || G != nullptr || M != nullptr;
+                             (qs0 + 31 >= p.n_q);
+      // a forbidden score's exponent becomes -inf (weight exactly 0), without
+      // a branch per score; the test runs on boundary tiles only
+      if (need_mask) {
+        #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = qs0 + 8 * (i >> 2) + 4 * g + (i & 3);
+          const float x = fmaf(sacc[i], cs, -lq[i >> 2][i & 3]);
+          sacc[i] = bwd_allowed(p, nullptr, q, key, kvalid) ? x : -INFINITY;
+        }
+      } else {
+        #pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = fmaf(sacc[i], cs, -lq[i >> 2][i & 3]);
+      }
       #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int q = qs0 + 8 * (i >> 2) + 4 * g + (i & 3);
-        float x = sacc[i] * cs;
-        bool ok = true;
-        if (need_mask) {
-          ok = bwd_allowed(p, G, q, key, kvalid);
-          if (M != nullptr && ok) x = fmaf(M[(size_t)q * p.n_k + key], kLog2e, x);
-        }
-        const float a = ok ? __builtin_amdgcn_exp2f(x - lq[i >> 2][i & 3]) : 0.f;
+        const float a = __builtin_amdgcn_exp2f(sacc[i]);
         sacc[i] = a;
         dpacc[i] = a * (dpacc[i] - dq[i >> 2][i & 3]);
       }
@@ -809,18 +838,30 @@ void attn_bwd_q_kernel(AttnBwdParams p) {
       }
       const bool need_mask = (p.causal && ks0 + 31 > q0w) || (ks0 + 31 >= kvalid) ||
                              (q0w + 31 >= p.n_q) || G != nullptr || M != nullptr;
-      #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = ks0 + 8 * (i >> 2) + 4 * g + (i & 3);
-        float x = sacc[i] * cs;
-        bool ok = true;
-        if (need_mask) {
-          ok = bwd_allowed(p, G, qi, key, kvalid);
-          if (M != nullptr && ok) x = fmaf(M[(size_t)qi * p.n_k + key], kLog2e, x);
+      // forbidden scores: exponent -inf (weight exactly 0), no branch per score
+      if (need_mask) {
+        #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = ks0 + 8 * (i >> 2) + 4 * g + (i & 3);
+          const bool ok = bwd_allowed(p, G, qi, key, kvalid);
+          float x;
+          if (M != nullptr) {
+            x = sacc[i] * cs;
+            if (ok) x = fmaf(M[(size_t)qi * p.n_k + key], kLog2e, x);
+            x -= Lq;
+          } else {
+            x = fmaf(sacc[i], cs, -Lq);
+          }
+          sacc[i] = ok ? x : -INFINITY;
         }
-        const float a = ok ? __builtin_amdgcn_exp2f(x - Lq) : 0.f;
-        sacc[i] = a * (dpacc[i] - Dq);         // dS^T
+      } else {
+        #pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = fmaf(sacc[i], cs, -Lq);
       }
+      #pragma unroll
+      for (int i = 0; i < 16; ++i)
+        sacc[i] = __builtin_amdgcn_exp2f(sacc[i]) * (dpacc[i] - Dq);   // dS^T
+
       // dQ^T += K^T dS^T (slot permutation as in the forward's value product)
       #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -919,8 +960,15 @@ void attn_bwd_q_dma_kernel(AttnBwdParams p) {
   for (int c = 0; c < C::VCH; ++c)
     zf[c] = qi < p.n_q ? load8_as<T>(p.dZ, p.z_dtype, zrow, 16 * c + 8 * g, DV, p.vec_z)
                        : zero_vec<vec>();
-  const float Lq = qi < p.n_q ? p.lse2[(size_t)bh * p.n_q + qi] : INFINITY;
-  const float Dq = qi < p.n_q ? p.dsum[(size_t)bh * p.n_q + qi] : 0.f;
+  const float Lq0 = qi < p.n_q ? p.lse2[(size_t)bh * p.n_q + qi] : INFINITY;
+  const float Dq0 = qi < p.n_q ? p.dsum[(size_t)bh * p.n_q + qi] : 0.f;
+  // waited for here, once (see the dK/dV kernel)
+  #pragma unroll
+  for (int c = 0; c < C::KCH; ++c) asm volatile("" : "+v"(qf[c]));
+  #pragma unroll
+  for (int c = 0; c < C::VCH; ++c) asm volatile("" : "+v"(zf[c]));
+  float Lq = Lq0, Dq = Dq0;
+  asm volatile("" : "+v"(Lq), "+v"(Dq));
 
   floatx16 dq[C::NDH];
   #pragma unroll
@@ -1032,14 +1080,22 @@ void attn_bwd_q_dma_kernel(AttnBwdParams p) {
         mfma_chunk(dpacc, lds_load_at<vec>(va_addr[c] + 32 * sb * D::VRB), zf[c]);
       const bool need_mask = (p.causal && ks0 + 31 > q0w) || (ks0 + 31 >= kvalid) ||
                              (q0w + 31 >= p.n_q);
-      #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = ks0 + 8 * (i >> 2) + 4 * g + (i & 3);
-        const float x = sacc[i] * cs;
-        const bool ok = !need_mask || bwd_allowed(p, nullptr, qi, key, kvalid);
-        const float a = ok ? __builtin_amdgcn_exp2f(x - Lq) : 0.f;
-        sacc[i] = a * (dpacc[i] - Dq);         // dS^T
+      // forbidden scores: exponent -inf (weight exactly 0), boundary tiles only
+      if (need_mask) {
+        #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = ks0 + 8 * (i >> 2) + 4 * g + (i & 3);
+          const float x = fmaf(sacc[i], cs, -Lq);
+          sacc[i] = bwd_allowed(p, nullptr, qi, key, kvalid) ? x : -INFINITY;
+        }
+      } else {
+        #pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = fmaf(sacc[i], cs, -Lq);
       }
+      #pragma unroll
+      for (int i = 0; i < 16; ++i)
+        sacc[i] = __builtin_amdgcn_exp2f(sacc[i]) * (dpacc[i] - Dq);   // dS^T
+
       #pragma unroll
       for (int st = 0; st < 2; ++st) {
         floatx8 sf;

@@ -644,12 +644,19 @@ void attn_bwd_kv_dma_kernel(AttnBwdParams p) {
         sacc[i] = 0.f;
         dpacc[i] = 0.f;
       }
+      // every operand of the two products read first (their LDS latencies
+      // overlap), then the products
+      vec qop[C::KCH], zop[C::VCH];
       #pragma unroll
-      for (int c = 0; c < C::KCH; ++c)
-        mfma_chunk(sacc, lds_load_at<vec>(qa_addr[c] + 32 * sb * D::QRB), kf[c]);
+      for (int c = 0; c < C::KCH; ++c) qop[c] = lds_load_at<vec>(qa_addr[c] + 32 * sb * D::QRB);
       #pragma unroll
-      for (int c = 0; c < C::VCH; ++c)
-        mfma_chunk(dpacc, lds_load_at<vec>(za_addr[c] + 32 * sb * D::ZRB), vf[c]);
+      for (int c = 0; c < C::VCH; ++c) zop[c] = lds_load_at<vec>(za_addr[c] + 32 * sb * D::ZRB);
+      #pragma unroll
+      for (int c = 0; c < C::KCH; ++c) mfma_chunk(sacc, qop[c], kf[c]);
+      #pragma unroll
+      for (int c = 0; c < C::VCH; ++c) mfma_chunk(dpacc, zop[c], vf[c]);
+      __builtin_amdgcn_sched_group_barrier(0x100, C::KCH + C::VCH, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, C::KCH + C::VCH, 0);
       // L and D of slot i's query 32 sb + 8 (i/4) + 4 g + i%4
       floatx4 lq[4], dq[4];
       #pragma unroll
@@ -1072,12 +1079,18 @@ void attn_bwd_q_dma_kernel(AttnBwdParams p) {
         sacc[i] = 0.f;
         dpacc[i] = 0.f;
       }
+      // operands read first, then the products (as in the dK/dV pass)
+      vec kop[C::KCH], vop[C::VCH];
       #pragma unroll
-      for (int c = 0; c < C::KCH; ++c)
-        mfma_chunk(sacc, lds_load_at<vec>(ka_addr[c] + 32 * sb * D::KRB), qf[c]);
+      for (int c = 0; c < C::KCH; ++c) kop[c] = lds_load_at<vec>(ka_addr[c] + 32 * sb * D::KRB);
       #pragma unroll
-      for (int c = 0; c < C::VCH; ++c)
-        mfma_chunk(dpacc, lds_load_at<vec>(va_addr[c] + 32 * sb * D::VRB), zf[c]);
+      for (int c = 0; c < C::VCH; ++c) vop[c] = lds_load_at<vec>(va_addr[c] + 32 * sb * D::VRB);
+      #pragma unroll
+      for (int c = 0; c < C::KCH; ++c) mfma_chunk(sacc, kop[c], qf[c]);
+      #pragma unroll
+      for (int c = 0; c < C::VCH; ++c) mfma_chunk(dpacc, vop[c], zf[c]);
+      __builtin_amdgcn_sched_group_barrier(0x100, C::KCH + C::VCH, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, C::KCH + C::VCH, 0);
       const bool need_mask = (p.causal && ks0 + 31 > q0w) || (ks0 + 31 >= kvalid) ||
                              (q0w + 31 >= p.n_q);
       // forbidden scores: exponent -inf (weight exactly 0), boundary tiles only

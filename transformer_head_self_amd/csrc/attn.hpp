@@ -225,7 +225,13 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   const int sp = SPLIT ? (int)(blockIdx.x % (unsigned)p.splits) : 0;   // key partition
   const int id = SPLIT ? (int)(blockIdx.x / (unsigned)p.splits) : (int)blockIdx.x;
   const int qt_rank = id / BH;
-  const int bh = id - qt_rank * BH;
+  int bh = id - qt_rank * BH;
+  // With a boolean mask or an additive bias ([B or 1, n_q, n_k], read by
+  // every head of an item): the BH / 8 heads an XCD receives are consecutive
+  // (b, r) pairs, so an item's heads share its mask rows in that XCD's L2
+  // (a bijection of [0, BH) when BH % 8 == 0).
+  if (!SPLIT && (p.allowed != nullptr || p.add != nullptr) && BH % 8 == 0)
+    bh = (bh % 8) * (BH / 8) + bh / 8;
   const int qt = p.causal ? (p.num_q_tiles - 1 - qt_rank) : qt_rank;
   const int b = bh / p.h;
   const int r = bh - b * p.h;

@@ -44,11 +44,23 @@ static bool wide_gemm_applies(const GemmBatch& b) {
 }
 
 
+// With fewer 256 x 128 tiles than CUs, the 128 x 128 tile of the same kernel
+// (four waves of 64 x 64) doubles the workgroups, and up to three share a CU
+// (48 KB of LDS each) instead of one wave per SIMD working alone.
+static constexpr long long kCUs = 256;   // MI355X
+static bool half_gemm_applies(const GemmBatch& b) {
+  long long tiles = 0;
+  for (int i = 0; i < b.count; ++i)
+    tiles += (long long)((b.p[i].M + 255) / 256) * ((b.p[i].N + 127) / 128);
+  return tiles < kCUs;
+}
+
 hipError_t launch_gemm(const GemmBatch& in, int compute_dtype, int w_dtype, hipStream_t stream) {
   GemmBatch b = in;
   const bool big = dma_gemm_applies(b, compute_dtype, w_dtype);
   const bool wide = big && wide_gemm_applies(b);
-  const int BM = big ? 256 : 128, BN = wide ? 256 : 128;
+  const bool half = big && !wide && half_gemm_applies(b);
+  const int BM = big && !half ? 256 : 128, BN = wide ? 256 : 128;
   int total = 0;
   for (int i = 0; i < b.count; ++i) {
     GemmProblem& p = b.p[i];
@@ -72,13 +84,24 @@ hipError_t launch_gemm(const GemmBatch& in, int compute_dtype, int w_dtype, hipS
       return hipErrorInvalidValue;
     return hipGetLastError();
   }
+  if (big && half) {
+    if (compute_dtype == kBF16 && w_dtype == kBF16)
+      hipLaunchKernelGGL((gemm_dma_kernel<bf16, bf16, 2>), dim3(total), dim3(256), 0, stream, b);
+    else if (compute_dtype == kF16 && w_dtype == kF16)
+      hipLaunchKernelGGL((gemm_dma_kernel<f16, f16, 2>), dim3(total), dim3(256), 0, stream, b);
+    else if (compute_dtype == kF16 && w_dtype == kBF16)
+      hipLaunchKernelGGL((gemm_dma_kernel<f16, bf16, 2>), dim3(total), dim3(256), 0, stream, b);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (big) {
     if (compute_dtype == kBF16 && w_dtype == kBF16)
-      hipLaunchKernelGGL((gemm_dma_kernel<bf16, bf16>), dim3(total), dim3(256), 0, stream, b);
+      hipLaunchKernelGGL((gemm_dma_kernel<bf16, bf16, 4>), dim3(total), dim3(256), 0, stream, b);
     else if (compute_dtype == kF16 && w_dtype == kF16)
-      hipLaunchKernelGGL((gemm_dma_kernel<f16, f16>), dim3(total), dim3(256), 0, stream, b);
+      hipLaunchKernelGGL((gemm_dma_kernel<f16, f16, 4>), dim3(total), dim3(256), 0, stream, b);
     else if (compute_dtype == kF16 && w_dtype == kBF16)
-      hipLaunchKernelGGL((gemm_dma_kernel<f16, bf16>), dim3(total), dim3(256), 0, stream, b);
+      hipLaunchKernelGGL((gemm_dma_kernel<f16, bf16, 4>), dim3(total), dim3(256), 0, stream, b);
     else
       return hipErrorInvalidValue;
     return hipGetLastError();

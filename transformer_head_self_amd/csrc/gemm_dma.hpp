@@ -9,7 +9,9 @@
 // re-rounded (nearest even) after it is read from LDS.
 //
 // Design (ours): a 256 x 128 workgroup tile, four waves of 128 x 64, k
-// stages of 32.  Tiles move from global memory into LDS with
+// stages of 32 (MI = 4); or, for grids that would leave CUs idle, a 128 x
+// 128 tile of four waves of 64 x 64 (MI = 2: twice the workgroups, 48 KB of
+// LDS, three workgroups per CU).  Tiles move from global memory into LDS with
 // global_load_lds_dwordx4 (no staging registers): each wave instruction
 // fills 1 KB of LDS, lane i writing bytes 16i..16i+15 of it from an address
 // of its own choice (a fixed 32-bit lane offset from a scalar base that
@@ -31,25 +33,29 @@
 
 namespace mha {
 
+template <int MI>   // 32-row blocks of C per wave
 struct GemmDmaCfg {
-  static constexpr int BM = 256, BN = 128, BK = 32, NS = 3;
+  static constexpr int BM = 64 * MI, BN = 128, BK = 32, NS = 3;
   static constexpr int NT = 256;
-  static constexpr int XBYTES = BM * BK * 2;           // 16 KB per stage
+  static constexpr int XBYTES = BM * BK * 2;           // 16 KB per stage (MI = 4)
   static constexpr int WBYTES = BK * BN * 2;           // 8 KB per stage
-  static constexpr int X_INSTR = XBYTES / 1024 / 4;    // per wave per stage: 4
+  static constexpr int X_INSTR = XBYTES / 1024 / 4;    // per wave per stage: MI
   static constexpr int W_INSTR = WBYTES / 1024 / 4;    // per wave per stage: 2
   static constexpr int LOADS = X_INSTR + W_INSTR;      // vector-memory ops per wave per stage
   static constexpr int X_AT = 0;                       // X stages at 0, 16K, 32K
   static constexpr int W_AT = NS * XBYTES;             // W stages at 48K, 56K, 64K
-  static constexpr int LDS = NS * (XBYTES + WBYTES);   // 72 KB: two workgroups per CU
+  static constexpr int LDS = NS * (XBYTES + WBYTES);   // 72 KB (MI = 4): two workgroups per CU
+  static constexpr int STAGE_OUT = 32 * MI * 144;      // staged stores per wave
+  static_assert(LDS >= 4 * STAGE_OUT, "staging space for four waves");
 };
 
 // T: element type of A and of the MFMA operands; TW: storage type of W.
-template <typename T, typename TW>
+template <typename T, typename TW, int MI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_dma_kernel(GemmBatch batch) {
   static_assert(sizeof(T) == 2 && sizeof(TW) == 2, "2-byte elements only");
-  typedef GemmDmaCfg C;
+  static_assert(MI == 4 || MI == 2, "128 or 64 rows per wave");
+  typedef GemmDmaCfg<MI> C;
   typedef typename Elem<T>::vec vec;
   typedef typename Elem<TW>::vec wvec;
   typedef typename Elem<TW>::vec4 wvec4;
@@ -79,11 +85,11 @@ void gemm_dma_kernel(GemmBatch batch) {
   const char* W = reinterpret_cast<const char*>(P.W);
   const unsigned lds_base = (unsigned)(size_t)(__attribute__((address_space(3))) char*)smem;
 
-  floatx16 acc[2][4];
+  floatx16 acc[2][MI];
   #pragma unroll
   for (int j = 0; j < 2; ++j)
     #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
       #pragma unroll
       for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.f;
 
@@ -122,13 +128,13 @@ void gemm_dma_kernel(GemmBatch batch) {
   };
 
   // ---- per-lane LDS read bases (bytes); the rest is immediate ------------
-  // A operand (B of the MFMA): row r = wm*128 + 32 i + l32, chunk 2 kc + g;
+  // A operand (B of the MFMA): row r = wm*32*MI + 32 i + l32, chunk 2 kc + g;
   // the slot permutation depends on r only through (r >> 2) & 3, which 32 i
   // does not change, so i is an immediate and kc selects one of two bases.
   int xr[2];
   #pragma unroll
   for (int kc = 0; kc < 2; ++kc) {
-    const int r = wm * 128 + l32;
+    const int r = wm * 32 * MI + l32;
     xr[kc] = r * 64 + (((2 * kc + g) ^ ((r >> 2) & 3)) * 16);
   }
   // W^T operand (A of the MFMA), transposing read: this lane addresses k row
@@ -150,7 +156,7 @@ void gemm_dma_kernel(GemmBatch batch) {
     const char* ws = smem + C::W_AT + B * C::WBYTES;
     #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      vec wf[2], xf[4];
+      vec wf[2], xf[MI];
       #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const char* p = ws + wr[j] + kc * 16 * 256;
@@ -159,12 +165,12 @@ void gemm_dma_kernel(GemmBatch batch) {
         wf[j] = convert_chunk<T, TW>(wvec{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       }
       #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
         xf[i] = *reinterpret_cast<const vec*>(xs + xr[kc] + i * 32 * 64);
       #pragma unroll
       for (int j = 0; j < 2; ++j)
         #pragma unroll
-        for (int i = 0; i < 4; ++i) mfma_chunk(acc[j][i], wf[j], xf[i]);
+        for (int i = 0; i < MI; ++i) mfma_chunk(acc[j][i], wf[j], xf[i]);
     }
   };
 
@@ -201,15 +207,14 @@ void gemm_dma_kernel(GemmBatch batch) {
   // The epilogue's index arithmetic starts here: opaque copies of its inputs
   // keep the compiler from computing it before the loop, where it would hold
   // registers across the whole k loop.
-  int m0w = m0 + wm * 128, n0w = n0 + wn * 64, lane_e = lane;
+  int m0w = m0 + wm * 32 * MI, n0w = n0 + wn * 64, lane_e = lane;
   asm volatile("" : "+s"(m0w), "+s"(n0w), "+v"(lane_e));
   add_column_bias<TW>(P, acc, n0w, lane_e >> 5);
   // every wave has finished reading the stage buffers before they are reused
-  // for the staged stores (18 KB per wave of the 72 KB)
+  // for the staged stores (18 KB per wave of the 72 KB at MI = 4)
   __syncthreads();
-  static_assert(C::LDS >= 4 * 128 * 144, "staging space for four waves");
   store_wave_block_any_lds(P, acc, m0w, n0w, lane_e >> 5, lane_e & 31,
-                           smem + wave * (128 * 144));
+                           smem + wave * C::STAGE_OUT);
 }
 
 }  // namespace mha

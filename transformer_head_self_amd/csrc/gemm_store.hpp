@@ -1,6 +1,7 @@
-// Epilogue shared by the 2-byte projection GEMMs: one wave's 128 x 64 block
-// of C, held as acc[j][i] = rows m0w + 32 i + (lane % 32), columns
-// n0w + 32 j + 8 a + 4 g + (0..3) in register 4a..4a+3 (g = lane / 32).
+// Epilogue shared by the 2-byte projection GEMMs: one wave's (32 NI) x 64
+// block of C (NI = 4 or 2), held as acc[j][i] = rows m0w + 32 i + (lane %
+// 32), columns n0w + 32 j + 8 a + 4 g + (0..3) in register 4a..4a+3
+// (g = lane / 32).
 //
 // kHeads: C is the head-major array (B, heads, ntok, dh) of page "Multi-head
 // attention and self-attention", Definition (the per-head projections),
@@ -42,8 +43,8 @@ __device__ __forceinline__ void add_column_bias(const GemmProblem& P, floatx16 (
       }
 }
 
-template <int DT, bool HEADS>
-__device__ __forceinline__ void store_wave_block(const GemmProblem& P, const floatx16 (&acc)[2][4],
+template <int DT, bool HEADS, int NI>
+__device__ __forceinline__ void store_wave_block(const GemmProblem& P, const floatx16 (&acc)[2][NI],
                                                  int m0w, int n0w, int g, int l32) {
   const int M = P.M, N = P.N;
   // column part of the destination offset, per (j, a)
@@ -63,7 +64,7 @@ __device__ __forceinline__ void store_wave_block(const GemmProblem& P, const flo
     }
   const bool vec_ok = HEADS ? true : (P.vec_c && (N % 4) == 0);
   #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const int m = m0w + 32 * i + l32;
     if (m >= M) continue;
     size_t roff;
@@ -91,27 +92,28 @@ __device__ __forceinline__ void store_wave_block(const GemmProblem& P, const flo
 // (rows padded by 16 bytes: the 8-byte writes of 32 rows and the 16-byte
 // row reads both spread evenly over the banks), then reads back 16
 // consecutive bytes per lane and stores them: 8 rows x 128 bytes per
-// instruction for 2-byte outputs, 4 rows x 256 bytes for fp32 (two passes
-// of 64 rows).  With a head width of 64 a wave's block is one contiguous
-// 16 KB run of the head-major array.  `lds` is this wave's region of at
-// least 128 x 144 bytes (18 KB), free for the wave's exclusive use; LDS
+// instruction for 2-byte outputs (one pass of 32 NI rows), 4 rows x 256
+// bytes for fp32 (two passes of 16 NI rows).  With a head width of 64 a
+// wave's block is one contiguous run of the head-major array.  `lds` is this
+// wave's region of at least 32 NI x 144 bytes (18 KB for NI = 4), free for
+// the wave's exclusive use; LDS
 // operations of one wave complete in order, so no barrier is needed between
 // the writes and the reads.  Conditions (checked by lds_store_ok): 2-byte
 // head-major outputs need a head width that is a multiple of 8; row-major
 // outputs need 16-byte aligned rows.
-template <int DT, bool HEADS>
+template <int DT, bool HEADS, int NI>
 __device__ __forceinline__ void store_wave_block_lds(const GemmProblem& P,
-                                                     const floatx16 (&acc)[2][4], int m0w,
+                                                     const floatx16 (&acc)[2][NI], int m0w,
                                                      int n0w, int g, int l32, char* lds) {
   constexpr int ES = DT == kF32 ? 4 : 2;
   constexpr int ROWB = 64 * ES + 16;          // padded LDS row
-  constexpr int ROWS = DT == kF32 ? 64 : 128; // rows per pass
+  constexpr int ROWS = (DT == kF32 ? 16 : 32) * NI;  // rows per pass: at most 144 * 32 NI bytes
   constexpr int LPR = 64 * ES / 16;           // lanes per row in the read-back
   constexpr int RPI = 64 / LPR;               // rows per store instruction
   const int lane = g * 32 + l32;
   const int M = P.M, N = P.N;
   #pragma unroll
-  for (int pass = 0; pass < 128 / ROWS; ++pass) {
+  for (int pass = 0; pass < 32 * NI / ROWS; ++pass) {
     // registers -> LDS: row (32 i + l32) - pass*ROWS, columns 32 j + 8 a + 4 g
     #pragma unroll
     for (int ii = 0; ii < ROWS / 32; ++ii) {
@@ -171,8 +173,9 @@ __device__ __forceinline__ bool lds_store_ok(const GemmProblem& P) {
 
 // Dispatch on the problem's output layout and element type once, outside
 // the unrolled stores, so the accumulators stay in registers.
+template <int NI>
 __device__ __forceinline__ void store_wave_block_any(const GemmProblem& P,
-                                                     const floatx16 (&acc)[2][4], int m0w,
+                                                     const floatx16 (&acc)[2][NI], int m0w,
                                                      int n0w, int g, int l32) {
   if (P.epilogue == kHeads) {
     if (P.out_dtype == kF32) store_wave_block<kF32, true>(P, acc, m0w, n0w, g, l32);
@@ -190,8 +193,9 @@ __device__ __forceinline__ void store_wave_block_any(const GemmProblem& P,
 namespace mha {
 
 // As store_wave_block_any, staged through `lds` when lds_store_ok(P).
+template <int NI>
 __device__ __forceinline__ void store_wave_block_any_lds(const GemmProblem& P,
-                                                         const floatx16 (&acc)[2][4], int m0w,
+                                                         const floatx16 (&acc)[2][NI], int m0w,
                                                          int n0w, int g, int l32, char* lds) {
   if (!lds_store_ok(P)) {
     store_wave_block_any(P, acc, m0w, n0w, g, l32);

@@ -163,6 +163,56 @@ static_assert(kLazyLimit == (float)(1 << (int)kLazyTau), "limit = 2^tau");
 // a row with no allowed key yet keeps mu = -inf, and its first allowed
 // block is redone at an exact shift (the +inf scores trip the block-sum
 // trigger).
+// Key padding without the causal rule: the item of rank k when the items
+// are ordered by decreasing key count (ties by index), for B <= 64 (lane i
+// holds item i's count; every lane of the wave takes part; the result is
+// uniform).
+__device__ __forceinline__ int item_of_rank(const AttnParams& p, int k) {
+  const int lane = threadIdx.x & 63;
+  const int mine = lane < p.B ? max(0, min(p.key_len[lane], p.n_k)) : -1;
+  int rank = 0;
+  for (int j = 0; j < p.B; ++j) {
+    const int other = __builtin_amdgcn_readlane(mine, j);
+    rank += (other > mine || (other == mine && j < lane)) ? 1 : 0;
+  }
+  const unsigned long long hit = __ballot(lane < p.B && rank == k);   // one lane
+  return hit ? __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit)) : 0;
+}
+
+struct TileId {
+  int qt, bh;
+};
+
+// Workgroup id -> (query tile, batch*head) of the attention kernels.
+// * Default: query tiles outer, heads inner; with round-robin dispatch over
+//   the 8 XCDs every tile of one head lands on the same XCD when B*h is a
+//   multiple of 8, so its K/V stay in that XCD's L2.  Causal: longest tiles
+//   (most keys) first.
+// * Key padding without the causal rule (B <= 64), on grids of more than
+//   512 workgroups (two per CU; a smaller grid is resident at once and only
+//   pays for the ordering): items in decreasing key count, so the longest
+//   rows start first and the short ones fill the slots that free up (a
+//   longest-first schedule; every tile of an item has the same length).
+// * A boolean mask or an additive bias ([B or 1, n_q, n_k], read by every
+//   head of an item): the BH / 8 heads an XCD receives are consecutive
+//   (b, r) pairs, so an item's heads share its mask rows in that XCD's L2 (a
+//   bijection of [0, BH) when BH % 8 == 0).
+__device__ __forceinline__ TileId tile_of_workgroup(const AttnParams& p, int id, bool split) {
+  const int BH = p.B * p.h;
+  if (!split && !p.causal && p.key_len != nullptr && p.B > 1 && p.B <= 64 &&
+      p.num_q_tiles * BH > 512) {
+    const int per_item = p.num_q_tiles * p.h;
+    const int k = id / per_item, within = id - k * per_item;
+    const int qt = within / p.h, r = within - qt * p.h;
+    return TileId{qt, item_of_rank(p, k) * p.h + r};
+  }
+  const int qt_rank = id / BH;
+  int bh = id - qt_rank * BH;
+  if (!split && (p.allowed != nullptr || p.add != nullptr) && BH % 8 == 0)
+    bh = (bh % 8) * (BH / 8) + bh / 8;
+  return TileId{p.causal ? (p.num_q_tiles - 1 - qt_rank) : qt_rank, bh};
+}
+
 template <typename T, int DH, int DV, int WAVES, int BN_, bool FAST, bool LAZY = false, int OCC = 1,
           bool STATS = true, bool SPLIT = false, int MASKED = 0>
 __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p) {
@@ -217,22 +267,12 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   const int g = lane >> 5;      // lane half
   const int l32 = lane & 31;
 
-  // Workgroup -> (query tile, batch*head).  Query tiles outer, heads inner:
-  // with round-robin dispatch over the 8 XCDs, every tile of one head lands
-  // on the same XCD when B*h is a multiple of 8, so its K/V stay in that
-  // XCD's L2.  Causal: longest tiles (most keys) first.
+  // Workgroup -> (query tile, batch*head): tile_of_workgroup.
   const int BH = p.B * p.h;
   const int sp = SPLIT ? (int)(blockIdx.x % (unsigned)p.splits) : 0;   // key partition
   const int id = SPLIT ? (int)(blockIdx.x / (unsigned)p.splits) : (int)blockIdx.x;
-  const int qt_rank = id / BH;
-  int bh = id - qt_rank * BH;
-  // With a boolean mask or an additive bias ([B or 1, n_q, n_k], read by
-  // every head of an item): the BH / 8 heads an XCD receives are consecutive
-  // (b, r) pairs, so an item's heads share its mask rows in that XCD's L2
-  // (a bijection of [0, BH) when BH % 8 == 0).
-  if (!SPLIT && (p.allowed != nullptr || p.add != nullptr) && BH % 8 == 0)
-    bh = (bh % 8) * (BH / 8) + bh / 8;
-  const int qt = p.causal ? (p.num_q_tiles - 1 - qt_rank) : qt_rank;
+  const TileId tile = tile_of_workgroup(p, id, SPLIT);
+  const int qt = tile.qt, bh = tile.bh;
   const int b = bh / p.h;
   const int r = bh - b * p.h;
   const int q0 = qt * C::QT;

@@ -58,11 +58,8 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_pipe_kernel(AttnParams p
   const int l32 = lane & 31;
 
   // Workgroup -> (query tile, batch*head) as in attn_fwd_kernel.
-  const int BH = p.B * p.h;
-  const int id = blockIdx.x;
-  const int qt_rank = id / BH;
-  const int bh = id - qt_rank * BH;
-  const int qt = p.causal ? (p.num_q_tiles - 1 - qt_rank) : qt_rank;
+  const TileId tile = tile_of_workgroup(p, (int)blockIdx.x, false);
+  const int qt = tile.qt, bh = tile.bh;
   const int b = bh / p.h;
   const int r = bh - b * p.h;
   const int q0 = qt * C::QT;

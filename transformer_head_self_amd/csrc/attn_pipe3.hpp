@@ -101,13 +101,9 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd3_kernel(AttnParams p) {
   const int g = lane >> 5;
   const int l32 = lane & 31;
 
-  // Workgroup -> (query tile, batch*head) as in attn_fwd_kernel: heads
-  // inner, so the tiles of one head share an XCD; causal: longest first.
-  const int BH = p.B * p.h;
-  const int id = blockIdx.x;
-  const int qt_rank = id / BH;
-  const int bh = id - qt_rank * BH;
-  const int qt = p.causal ? (p.num_q_tiles - 1 - qt_rank) : qt_rank;
+  // Workgroup -> (query tile, batch*head) as in attn_fwd_kernel.
+  const TileId tile = tile_of_workgroup(p, (int)blockIdx.x, false);
+  const int qt = tile.qt, bh = tile.bh;
   const int b = bh / p.h;
   const int r = bh - b * p.h;
   const int q0 = qt * C::QT;

@@ -246,7 +246,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   constexpr int MT = MLDS ? C::QT * BN : 0;
   constexpr int M_WIN = MT / 1024 / WAVES;
   static_assert(M_WIN * 1024 * WAVES == MT, "whole 1 KB mask windows per wave");
-  // ALDS (MASKED == 1 on the direct-load path): an additive bias tile (QT
+  // ALDS (MASKED == 1 or 3, direct-load path): an additive bias tile (QT
   // rows x BN fp32 keys, 32 KB at 64 keys) moves by direct loads into one LDS
   // buffer, each wave its own 32 rows, one block ahead: block blk + 1's rows
   // are issued at the top of block blk (before the K/V loads of block

@@ -51,9 +51,12 @@ hipError_t launch_attn_fixed(AttnParams p, hipStream_t stream) {
   // skips the running maximum (block-sum trigger).
   const bool stats = p.row_m != nullptr || p.row_l != nullptr;
   // Boolean masks and additive biases on exact-width 2-byte heads with
-  // aligned mask rows: the direct-load kernel with the exact-shift merge
-  // (a row's first key block may hold no allowed key, which the deferred
-  // shift's start assumes).
+  // aligned mask rows: the direct-load kernel; the boolean tile (16-byte
+  // aligned rows) and the bias alone have variants of their own, which run
+  // the deferred shift when no row statistics are requested (a row whose
+  // first key blocks allow nothing keeps its shift unset until its first
+  // allowed block, which goes down the exact redo); every other combination
+  // runs the exact-shift merge.
   if constexpr (sizeof(T) == 2) {
     const bool fast_masked = p.d_h == DH && p.d_vh == DV && p.vec_q && p.vec_k && p.vec_v &&
                              (p.allowed != nullptr || p.add != nullptr) && p.mask_vec;

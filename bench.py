@@ -17,8 +17,9 @@ Printed JSON line (rank 0):
   output's rows of that item with the oracle's (``parity``);
 * ms_median / ms_min: per-step times from events around every timed step;
 * settled: the same forward timed again after about 0.2 s of back-to-back
-  steps (the GPU clock rises over the first milliseconds of sustained load;
-  ``value`` keeps the requested warm-up and steps).
+  steps, then the attention kernel alone (the GPU clock rises over the
+  first milliseconds of sustained load; ``value`` and ``roofline`` keep the
+  requested warm-up and steps).
 """
 
 from __future__ import annotations
@@ -462,8 +463,12 @@ def main():
             torch.cuda.synchronize()
             n_settle += 20
         ms_settled, per_settled = timed_steps(step, args.steps, stream, torch)
+        # the attention kernel alone right after, still under sustained load
+        ms_core_settled, per_core_settled = timed_steps(core, args.steps, stream, torch)
         settled = {"settle_steps": n_settle, "ms_per_step": round(ms_settled, 5),
-                   "ms_median": round(per_settled[len(per_settled) // 2], 5)}
+                   "ms_median": round(per_settled[len(per_settled) // 2], 5),
+                   "attn_core_ms": round(ms_core_settled, 5),
+                   "attn_core_ms_median": round(per_core_settled[len(per_core_settled) // 2], 5)}
 
     core_flops = w.core_flops_effective(x["key_len"])
     total_flops = core_flops + w.proj_flops()
@@ -485,6 +490,8 @@ def main():
     nominal = w.core_flops() + w.proj_flops()
     if settled is not None:
         settled["value"] = round(total_flops / (settled["ms_per_step"] * 1e-3) / 1e12, 3)
+        settled["attn_core_frac_of_peak"] = round(
+            core_flops / (settled["attn_core_ms"] * 1e-3) / 1e12 / peak, 4)
     out = {
         "metric": METRIC,
         "value": round(value, 3),

@@ -326,6 +326,35 @@ def test_bool_mask_block_sparse(dt, causal, row_stats):
         np.testing.assert_allclose(rl.cpu().numpy(), ref["l"], rtol=1e-2)
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_bool_mask_bytes_other_than_one(dt):
+    """A uint8 mask whose allowed entries are any nonzero byte (2, 128, 255,
+    ...; mha.h: allowed[b][i][j] != 0), on the mask-tile path, causal.  A
+    wave's window counts as wholly allowed only when bit 0 is set in every
+    byte, so windows of even nonzero bytes take the per-score test; windows
+    of odd bytes and of ones skip it.  Rows 0-255 use even bytes only, rows
+    256-511 odd ones, the rest a mix with zeros (forbidden)."""
+    B, h, n, d = 2, 2, 640, 64
+    _say(f"[bool bytes] {dt}")
+    Qh, Kh, Vh = make_heads(B, h, n, n, d, d, "f32" if dt == "f16" else dt, seed=64)
+    dev, host = _heads_dev(Qh, Kh, Vh, dt)
+    rng = np.random.default_rng(65)
+    G = np.empty((B, n, n), dtype=np.uint8)
+    G[:, :256] = 2 * rng.integers(1, 128, size=(B, 256, n))          # even, nonzero
+    G[:, 256:512] = 2 * rng.integers(0, 128, size=(B, 256, n)) + 1   # odd
+    G[:, 512:] = rng.integers(0, 256, size=(B, n - 512, n)) * (rng.random((B, n - 512, n)) < 0.5)
+    G[:, 512:, 0] = 3                                                # every row keeps key 0
+    allow = allowed_set(B, n, n, causal=True, allowed=G != 0)
+    c = 1.0 / math.sqrt(d)
+    ref = attn_core_ref(*host, c, allow)
+    Z = mha.attn_core(*dev, scale=c, causal=True, allowed=torch.from_numpy(G).to(DEV))
+    torch.cuda.synchronize()
+    err = _rel_err(Z.cpu().numpy(), ref["Z"])
+    bar = SPLIT_TOL[dt] if dt != "f16" else core_bar(*host, c, allow, ref["Z"])
+    _say(f"  Z err {err:.3e} (bar {bar:.2e})")
+    assert err <= bar
+
+
 @pytest.mark.parametrize("row_stats", [True, False])
 @pytest.mark.parametrize("case", BOOL_FAST_CASES, ids=lambda c: "-".join(map(str, c)))
 def test_bool_mask_direct_load_path(case, row_stats):

@@ -189,6 +189,51 @@ def test_forward_mask_tile():
             assert bank_degree(flat, 4) == 8
 
 
+def test_forward_mask_window_reads_and_tests():
+    """The mask step reads dwords (kb, a) in pairs: chunk c = 2 kb + h at base
+    row * 64 + 16 (c ^ ((row / 4) mod 4)) + 4 g, dword a = 2 h + e at + 8 e
+    (one two-dword LDS read per chunk), the addresses of the per-dword form
+    above.  Its window tests: no allowed entry iff the OR of the dwords is 0;
+    every entry allowed (skip the per-score test) only if bit 0 is set in
+    every byte of the AND: exact for 0 / 1 bytes, and for other bytes never
+    true unless every byte is nonzero (so a false answer only costs the
+    per-score test)."""
+    for wv, lane, kb, h, e in itertools.product(range(4), range(64), range(2), range(2),
+                                                range(2)):
+        l32, g = lane % 32, lane // 32
+        mr = 32 * wv + l32
+        c, a = 2 * kb + h, 2 * h + e
+        base = mr * 64 + (c ^ ((mr >> 2) & 3)) * 16 + 4 * g
+        direct = mr * 64 + ((2 * kb + a // 2) ^ ((mr >> 2) & 3)) * 16 + 8 * (a & 1) + 4 * g
+        assert base + 8 * e == direct
+    rng = np.random.default_rng(7)
+
+    def tests(words):
+        all_and = np.bitwise_and.reduce(words)
+        any_set = np.bitwise_or.reduce(words)
+        return any_set == 0, (all_and & 0x01010101) == 0x01010101
+
+    def as_words(b):
+        return b.reshape(-1, 4).astype(np.uint32) @ np.array([1, 1 << 8, 1 << 16, 1 << 24],
+                                                               dtype=np.uint32)
+    for trial in range(4000):
+        kind = trial % 4
+        if kind == 0:
+            b = (rng.random(32) < 0.97).astype(np.uint8)              # 0 / 1
+        elif kind == 1:
+            b = np.ones(32, np.uint8)
+        elif kind == 2:
+            b = np.zeros(32, np.uint8)
+            b[rng.integers(32)] = rng.integers(0, 2) * rng.integers(1, 256)
+        else:
+            b = rng.integers(0, 256, 32).astype(np.uint8) * (rng.random(32) < 0.95)
+        none_allowed, full = tests(as_words(b))
+        assert none_allowed == (not b.any())
+        if full:
+            assert b.all()
+        if kind <= 1:
+            assert full == bool(b.all())
+
 
 def bias_fast_offsets(q0, wave, n_k, k0):
     """Byte offsets of the bias-tile direct loads on the fast path (every

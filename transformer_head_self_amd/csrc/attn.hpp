@@ -663,23 +663,30 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
         const int mr = wave * 32 + l32, sw = (mr >> 2) & 3;
         unsigned mb = lds_base + (unsigned)(C::DMA_LDS + (blk % C::NS) * MT);
         asm("" : "+s"(mb));
-        uint32_t has_zero = 0u, any_set = 0u;
+        uint32_t all_and = 0xffffffffu, any_set = 0u;
         #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           #pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const int c = 2 * kb + (a >> 1);
-            const uint32_t x = lds_load_at<uint32_t>(mb + (unsigned)(mr * 64 + ((c ^ sw) * 16) +
-                                                                     8 * (a & 1) + 4 * g));
-            gmv[kb][a] = x;
-            amv[kb][a] = floatx4{0.f, 0.f, 0.f, 0.f};
-            has_zero |= (x - 0x01010101u) & ~x & 0x80808080u;   // nonzero iff a byte is 0
-            any_set |= x;
+          for (int h = 0; h < 2; ++h) {
+            // dwords a = 2 h and 2 h + 1: bytes 4 g and 8 + 4 g of chunk c
+            const int c = 2 * kb + h;
+            const unsigned ca = mb + (unsigned)(mr * 64 + ((c ^ sw) * 16) + 4 * g);
+            #pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const uint32_t x = lds_load_at<uint32_t>(ca + 8u * (unsigned)e);
+              gmv[kb][2 * h + e] = x;
+              amv[kb][2 * h + e] = floatx4{0.f, 0.f, 0.f, 0.f};
+              all_and &= x;
+              any_set |= x;
+            }
           }
         // rows past n_q hold a copy of row n_q - 1 (never stored): harmless
         // either way
         if (__all(any_set == 0u)) active = false;
-        tile_full = __all(has_zero == 0u);
+        // every entry allowed if bit 0 is set in every byte: exact for 0 / 1
+        // entries; other nonzero bytes may fail it and only take the
+        // per-score test below
+        tile_full = __all((all_and & 0x01010101u) == 0x01010101u);
       }
     }
     if (active) {

@@ -246,6 +246,12 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   constexpr int MT = MLDS ? C::QT * BN : 0;
   constexpr int M_WIN = MT / 1024 / WAVES;
   static_assert(M_WIN * 1024 * WAVES == MT, "whole 1 KB mask windows per wave");
+  // Stages in flight: three, or two for the boolean tile at three workgroups
+  // per CU (at d = 64: 48 KB of LDS instead of 72 KB).  With two, block
+  // blk + 1 is issued once every wave is past block blk - 1, so its loads
+  // have one block of compute to land instead of two.
+  constexpr int NS = (MLDS && OCC >= 3) ? 2 : C::NS;
+  constexpr int DMA_LDS = NS * C::STAGE;
   // ALDS (MASKED == 1 or 3, direct-load path): an additive bias tile (QT
   // rows x BN fp32 keys, 32 KB at 64 keys) moves by direct loads into one LDS
   // buffer, each wave its own 32 rows, one block ahead: block blk + 1's rows
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   constexpr int AT = ALDS ? C::QT * BN * 4 : 0;
   constexpr int A_WIN = AT / 1024 / WAVES;
   static_assert(!ALDS || A_WIN * 1024 * WAVES == AT, "whole 1 KB bias windows per wave");
-  constexpr int LDS_BYTES = DMA ? C::DMA_LDS + C::NS * MT + AT : C::REG_LDS;
+  constexpr int LDS_BYTES = DMA ? DMA_LDS + NS * MT + AT : C::REG_LDS;
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   T* Ks = reinterpret_cast<T*>(smem);
   T* Vs = Ks + 2 * C::KBUF;
@@ -493,7 +499,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
     #pragma unroll
     for (int j = 0; j < 4; ++j) abase[j] = 4u * row0 * (unsigned)p.n_k + 16u * (c0 ^ (4u * j));
   }
-  const unsigned a_lds = lds_base + (unsigned)(C::DMA_LDS + C::NS * MT) + wave * A_WIN * 1024;
+  const unsigned a_lds = lds_base + (unsigned)(DMA_LDS + NS * MT) + wave * A_WIN * 1024;
   auto issue_bias = [&](int blk) {
     if constexpr (ALDS) {
       const int k0 = blk * BN;
@@ -513,13 +519,13 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       }
     }
   };
-  // block blk into stage blk % 3; in the last block, rows past n_k read the
+  // block blk into stage blk % NS; in the last block, rows past n_k read the
   // last key (masked out, weight 0)
   auto issue_kv = [&](int blk) {
     const int k0 = blk * BN;
-    const unsigned st = lds_base + (unsigned)((blk % C::NS) * C::STAGE);
+    const unsigned st = lds_base + (unsigned)((blk % NS) * C::STAGE);
     if constexpr (MLDS) {
-      const unsigned mst = lds_base + (unsigned)(C::DMA_LDS + (blk % C::NS) * MT);
+      const unsigned mst = lds_base + (unsigned)(DMA_LDS + (blk % NS) * MT);
       #pragma unroll
       for (int q = 0; q < M_WIN; ++q)
         lds_dma16(Gb, mrow[q] + min((unsigned)k0 + mchk[q], (unsigned)(p.n_k - 16)),
@@ -574,7 +580,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       if (Ab != nullptr && nblk > blk0) issue_bias(blk0);
     }
     if (nblk > blk0) issue_kv(blk0);
-    if (nblk > blk0 + 1) issue_kv(blk0 + 1);
+    if (NS == 3 && nblk > blk0 + 1) issue_kv(blk0 + 1);
   } else {
     if (nblk > blk0) {
       load_kv(blk0);
@@ -587,9 +593,12 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   for (int blk = blk0; blk < nblk; ++blk) {
     floatx4 amv[GEN ? NKB : 1][4];
     if constexpr (DMA) {
-      // block blk has landed once only block blk+1's loads are outstanding;
-      // after the barrier no wave reads block blk-1, whose stage is refilled
-      if (blk + 1 < nblk) wait_vm_lds<C::K_WIN + C::V_WIN + M_WIN>();
+      // three stages: block blk has landed once only block blk+1's loads are
+      // outstanding; after the barrier no wave reads block blk-1, whose
+      // stage is refilled with block blk+2.  Two stages: block blk's loads
+      // are the only ones outstanding; after the barrier block blk-1's stage
+      // is refilled with block blk+1.
+      if (NS == 3 && blk + 1 < nblk) wait_vm_lds<C::K_WIN + C::V_WIN + M_WIN>();
       else wait_vm_lds<0>();
       compiler_fence();
       if constexpr (ALDS) {
@@ -615,7 +624,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       if constexpr (ALDS) {
         if (Ab != nullptr && blk + 1 < nblk) issue_bias(blk + 1);
       }
-      if (blk + 2 < nblk) issue_kv(blk + 2);
+      if (blk + NS - 1 < nblk) issue_kv(blk + NS - 1);
     }
     const int cur = (blk - blk0) & 1;   // register staging: buffer of this block
     const T* ks = Ks + cur * C::KBUF;
@@ -626,7 +635,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
     // it kept a separate strength-reduced address per read).
     unsigned kaddr[DMA ? C::KCH : 1], vaddr[DMA ? C::NDV : 1];
     if constexpr (DMA) {
-      unsigned st_addr = lds_base + (unsigned)((blk % C::NS) * C::STAGE);
+      unsigned st_addr = lds_base + (unsigned)((blk % NS) * C::STAGE);
       asm("" : "+s"(st_addr));
       #pragma unroll
       for (int c = 0; c < C::KCH; ++c) {
@@ -661,7 +670,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
         // this lane's row of the block's mask tile: dword (kb, a) holds keys
         // k0 + 32 kb + 8 a + 4 g .. + 3, in chunk 2 kb + a / 2 of the row
         const int mr = wave * 32 + l32, sw = (mr >> 2) & 3;
-        unsigned mb = lds_base + (unsigned)(C::DMA_LDS + (blk % C::NS) * MT);
+        unsigned mb = lds_base + (unsigned)(DMA_LDS + (blk % NS) * MT);
         asm("" : "+s"(mb));
         uint32_t all_and = 0xffffffffu, any_set = 0u;
         #pragma unroll
@@ -742,8 +751,9 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
       // or the exact-shift merge: there the fragments do not fit the
       // registers of two waves per SIMD)
       // (nor with a staged bias tile and the exact-shift merge: the bias
-      // entries hold those registers)
-      constexpr bool VPRE = DMA && !(ALDS && !(ADDONLY && LAZY)) &&
+      // entries hold those registers; nor with the boolean tile at three
+      // workgroups per CU, which must fit 168 registers)
+      constexpr bool VPRE = DMA && !(ALDS && !(ADDONLY && LAZY)) && !(MLDS && OCC >= 3) &&
                             !(WAVES >= 8 && C::NDV > 2 && (DH >= 128 || !LAZY));
       vec vpre[VPRE ? NKB : 1][2][VPRE ? C::NDV : 1];
       if constexpr (VPRE) {

@@ -62,6 +62,11 @@ hipError_t launch_attn_fixed(AttnParams p, hipStream_t stream) {
                              (p.allowed != nullptr || p.add != nullptr) && p.mask_vec;
     if (fast_masked) {
       constexpr int occm = (DH <= 64 && DV <= 64) ? 2 : 1;
+      // the boolean tile with the deferred shift at d = 64: three workgroups
+      // per CU on two LDS stages (48 KB) and 168 registers, measured against
+      // two workgroups on three stages (72 KB) in one process: 176.7-178.1
+      // against 190.7-191.5 us at B = 4, T = 4096, h = 16, causal
+      constexpr int occb = (DH == 64 && DV == 64) ? 3 : occm;
       // a boolean mask alone with 16-byte aligned rows travels into LDS with
       // the K/V tiles; otherwise each lane loads its mask entries
       // an additive bias alone: the one-FMA mask step, with the deferred
@@ -73,7 +78,7 @@ hipError_t launch_attn_fixed(AttnParams p, hipStream_t stream) {
         hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, false, occm, true, false, 3>),
                            dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
       else if (p.allowed != nullptr && p.add == nullptr && p.mask_g16 && lazy && !stats)
-        hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, true, occm, false, false, 2>),
+        hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, true, occb, false, false, 2>),
                            dim3((unsigned)grid), dim3(C::NT), 0, stream, p);
       else if (p.allowed != nullptr && p.add == nullptr && p.mask_g16)
         hipLaunchKernelGGL((attn_fwd_kernel<T, DH, DV, WAVES, BN, true, false, occm, true, false, 2>),

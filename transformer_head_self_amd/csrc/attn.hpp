@@ -62,8 +62,8 @@ struct AttnCfg {
   static constexpr int V_PER_T = (V_CHUNKS + NT - 1) / NT;
   static constexpr int REG_LDS = 2 * (KBUF + VBUF) * (int)sizeof(T);   // register staging
   // Direct-to-LDS staging (2-byte fast path): unpadded rows of KRB / VRB
-  // bytes, three stages of one K tile and one V tile, K_WIN / V_WIN 1 KB
-  // load instructions per wave per tile.
+  // bytes, three stages of one K tile and one V tile (a kernel may run two),
+  // K_WIN / V_WIN 1 KB load instructions per wave per tile.
   static constexpr int KRB = DH * (int)sizeof(T), VRB = DV * (int)sizeof(T);
   static constexpr int KTILE = BN * KRB, VTILE = BN * VRB;
   static constexpr int STAGE = KTILE + VTILE, NS = 3;
@@ -236,8 +236,8 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void attn_fwd_kernel(AttnParams p)
   constexpr int VEC = C::VEC;
   constexpr int BN = C::BN;
 
-  // DMA: K/V tiles move from global memory straight into LDS (three stages in
-  // flight); otherwise they are staged through registers (two buffers).
+  // DMA: K/V tiles move from global memory straight into LDS (NS stages in
+  // flight, below); otherwise they are staged through registers (two buffers).
   constexpr bool DMA = C::TR && FAST && BN_ == 64;
   // MASKED == 2: the boolean mask's tile (QT rows x 64 key bytes) is loaded
   // straight into LDS with each block's K/V tiles, after the stages

@@ -287,6 +287,11 @@ BOOL_FAST_CASES = [
     ("f16", 2, 2, 400, 400, 64, 64, True, None, False),
     ("bf16", 2, 2, 336, 336, 64, 64, True, (336, 200), True),
     ("f16", 1, 3, 272, 272, 128, 128, True, None, True),
+    # one and two key blocks (the two-stage ring of the d = 64 deferred-shift
+    # kernel: a prologue of one block, a last block right after it)
+    ("f16", 1, 2, 64, 64, 64, 64, False, None, False),
+    ("bf16", 2, 2, 130, 128, 64, 64, False, (128, 70), False),
+    ("f16", 2, 1, 96, 96, 64, 64, True, None, True),
 ]
 
 
